@@ -1,0 +1,255 @@
+"""Checks that pin the CPU oracle to something other than itself.
+
+Each function returns an error figure; tests/test_oracle_pins.py asserts it
+is small for the oracle as written, and tests/test_oracle_mutants.py plants
+plausible mistakes in the oracle (on the CPU) and asserts that at least one
+of these figures then becomes large.
+"""
+import itertools
+import math
+
+import numpy as np
+
+from tests import brute
+
+# A layer small enough for pure-Python loops: h = 8, 2 heads of d = 4,
+# FFN 32, batch 2, and up to 6 positions.
+TINY = dict(hidden=8, heads=2, head_dim=4, ffn=32, tp=1, batch=2, seq=6, eps=1e-5)
+PARAM_SHAPES = [("ln1_g", "h"), ("ln1_b", "h"), ("w_q", "hh"), ("b_q", "h"), ("w_k", "hh"),
+                ("b_k", "h"), ("w_v", "hh"), ("b_v", "h"), ("w_o", "hh"), ("b_o", "h"),
+                ("ln2_g", "h"), ("ln2_b", "h"), ("w1", "fh"), ("b1", "f"), ("w2", "hf"), ("b2", "h")]
+
+
+def tiny_params(cfg, seed, wstd=0.5):
+    """Random parameters with every term switched on (non-zero biases, gamma
+    away from 1, beta away from 0) and weights large enough that the softmax
+    is far from uniform."""
+    rng = np.random.default_rng(seed)
+    h, f = cfg["hidden"], cfg["ffn"]
+    dims = {"h": (h,), "hh": (h, h), "fh": (f, h), "hf": (h, f), "f": (f,)}
+    p = {}
+    for name, kind in PARAM_SHAPES:
+        if name.endswith("_g"):
+            p[name] = 1.0 + 0.3 * rng.standard_normal(dims[kind])
+        elif name.startswith("w"):
+            p[name] = wstd * rng.standard_normal(dims[kind])
+        else:
+            p[name] = 0.2 * rng.standard_normal(dims[kind])
+    return p
+
+
+def tiny_inputs(cfg, seed):
+    rng = np.random.default_rng(seed + 17)
+    shape = (cfg["seq"], cfg["batch"], cfg["hidden"])
+    return rng.standard_normal(shape), rng.standard_normal(shape)
+
+
+def brute_error(orc, seed=0, cfg=TINY):
+    """max |oracle y - brute-force y| on a tiny layer."""
+    p = tiny_params(cfg, seed)
+    x, _ = tiny_inputs(cfg, seed)
+    y = orc.layer_forward(x, p, cfg)["y"]
+    pl = {k: v.tolist() for k, v in p.items()}
+    yb = np.array(brute.layer_forward(x.tolist(), pl, cfg["heads"], cfg["eps"]))
+    return float(np.abs(y - yb).max())
+
+
+def fd_error(orc, seed=1, cfg=None, eps=1e-6):
+    """Largest relative gap between the oracle's backward and central
+    differences of L = sum(y * dy), over every parameter entry and every
+    input entry."""
+    cfg = dict(TINY, seq=4) if cfg is None else cfg
+    p = tiny_params(cfg, seed)
+    x, dy = tiny_inputs(cfg, seed)
+    fw = orc.layer_forward(x, p, cfg)
+    gr = orc.layer_backward(dy, p, cfg, fw)
+
+    def loss(pp, xx):
+        return float((orc.layer_forward(xx, pp, cfg)["y"] * dy).sum())
+
+    worst = 0.0
+    targets = [(name, p[name]) for name, _ in PARAM_SHAPES] + [("x", x)]
+    for name, arr in targets:
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = loss(p, x)
+            arr[idx] = old - eps
+            lm = loss(p, x)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        scale = max(1.0, float(np.abs(num).max()))
+        worst = max(worst, float(np.abs(num - gr[name]).max()) / scale)
+    return worst
+
+
+def compositions(n):
+    """Every composition of n (ordered partitions into positive parts)."""
+    for cuts in itertools.product([0, 1], repeat=n - 1):
+        parts, run = [], 1
+        for c in cuts:
+            if c:
+                parts.append(run)
+                run = 1
+            else:
+                run += 1
+        parts.append(run)
+        yield parts
+
+
+def bounds_of(parts):
+    b = [0]
+    for n in parts:
+        b.append(b[-1] + n)
+    return b
+
+
+def tp_layer(orc, x, dy, p, cfg, bounds):
+    """The whole layer computed the tensor-parallel + token-slice way: t
+    shards, each run slice by slice through the shard functions, with the
+    all-reduces simulated by sums over ranks.  Returns (y, dx, full grads
+    re-assembled from the shards)."""
+    t, s = cfg["tp"], cfg["seq"]
+    h, f = cfg["hidden"], cfg["ffn"]
+    ht, ft = h // t, f // t
+    sps = [orc.shard_params(p, r, cfg) for r in range(t)]
+    kvs = [orc.new_kv_cache(cfg) for _ in range(t)]
+    kvgs = [orc.new_kv_grad(cfg) for _ in range(t)]
+    y = np.zeros_like(x)
+    dx = np.zeros_like(x)
+    saved = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        outs = [orc.shard_attn_forward(x, sps[r], cfg, kvs[r], a, b) for r in range(t)]
+        h_mid = orc.residual_combine(x[a:b], sum(o[0] for o in outs), p["b_o"])
+        mouts = [orc.shard_mlp_forward(h_mid, sps[r], cfg) for r in range(t)]
+        y[a:b] = orc.residual_combine(h_mid, sum(o[0] for o in mouts), p["b2"])
+        saved.append(([o[1] for o in outs], [o[1] for o in mouts], a, b))
+    grads = [dict() for _ in range(t)]
+
+    def acc(r, gr):
+        for k, v in gr.items():
+            grads[r][k] = grads[r].get(k, 0.0) + v
+
+    for sa, sm, a, b in reversed(saved):
+        res = [orc.shard_mlp_backward(dy[a:b], sps[r], sm[r]) for r in range(t)]
+        for r in range(t):
+            acc(r, res[r][1])
+        du2 = sum(rr[0] for rr in res)
+        res = [orc.shard_attn_backward(dy[a:b], du2, sps[r], sm[r], sa[r], kvs[r], kvgs[r])
+               for r in range(t)]
+        for r in range(t):
+            acc(r, res[r][2])
+        du1 = sum(rr[1] for rr in res)
+        res1 = [orc.ln1_backward(res[r][0], du1, sps[r], sa[r]) for r in range(t)]
+        for r in range(t):
+            acc(r, res1[r][1])
+        dx[a:b] = res1[0][0]
+    full = {}
+    for name in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "b_o", "b2"):
+        full[name] = grads[0][name]
+    full["w_q"] = np.concatenate([g["w_qkv"][:ht] for g in grads])
+    full["w_k"] = np.concatenate([g["w_qkv"][ht:2 * ht] for g in grads])
+    full["w_v"] = np.concatenate([g["w_qkv"][2 * ht:] for g in grads])
+    full["b_q"] = np.concatenate([g["b_qkv"][:ht] for g in grads])
+    full["b_k"] = np.concatenate([g["b_qkv"][ht:2 * ht] for g in grads])
+    full["b_v"] = np.concatenate([g["b_qkv"][2 * ht:] for g in grads])
+    full["w_o"] = np.concatenate([g["w_o"] for g in grads], axis=1)
+    full["w1"] = np.concatenate([g["w1"] for g in grads])
+    full["b1"] = np.concatenate([g["b1"] for g in grads])
+    full["w2"] = np.concatenate([g["w2"] for g in grads], axis=1)
+    # replicated parameters must get the same gradient on every rank
+    rep_gap = max(float(np.abs(grads[r][k] - grads[0][k]).max())
+                  for r in range(t) for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "b_o", "b2"))
+    return y, dx, full, rep_gap
+
+
+def tp_error(orc, t, parts, seed=2, cfg=None):
+    """max gap between the tensor-parallel, token-sliced computation and the
+    unsharded layer, over y, dx and every parameter gradient."""
+    cfg = dict(TINY, tp=t, heads=max(2, t)) if cfg is None else cfg
+    cfg = dict(cfg, seq=sum(parts))
+    p = tiny_params(cfg, seed)
+    x, dy = tiny_inputs(cfg, seed)
+    fw = orc.layer_forward(x, p, cfg)
+    gr = orc.layer_backward(dy, p, cfg, fw)
+    y, dx, full, rep_gap = tp_layer(orc, x, dy, p, cfg, bounds_of(parts))
+    err = max(float(np.abs(y - fw["y"]).max()), float(np.abs(dx - gr["x"]).max()), rep_gap)
+    for k, v in full.items():
+        err = max(err, float(np.abs(v - gr[k]).max()))
+    return err
+
+
+def closed_form_errors(orc):
+    """Closed forms and special cases of the layer, returned as a dict of
+    error figures (each should be ~0)."""
+    cfg = dict(TINY)
+    out = {}
+    rng = np.random.default_rng(5)
+    # attention: the first position sees only itself, so o_0 = v_0
+    q, k, v = (rng.standard_normal((2, 3, 5, 4)) for _ in range(3))
+    o, prob, lse = orc.causal_attention(q, k, v, 0)
+    out["o0_is_v0"] = float(np.abs(o[:, :, 0] - v[:, :, 0]).max())
+    # softmax rows sum to 1 and put no weight on later positions
+    out["rows_sum_1"] = float(np.abs(prob.sum(-1) - 1).max())
+    out["no_future"] = float(np.abs(np.triu(prob, 1)).max())
+    # lse is the log of the softmax denominator: P_pj = exp(s_pj - lse_p)
+    sc = np.einsum("bnpd,bnjd->bnpj", q, k) / 2.0
+    keep = np.tril(np.ones((5, 5), dtype=bool))
+    out["lse_relation"] = float(np.abs(np.where(keep, np.exp(sc - lse[..., None]), 0) - prob).max())
+    # zero queries and keys: uniform weights, o_p = mean_{j<=p} v_j
+    o, _, lse = orc.causal_attention(np.zeros_like(q), np.zeros_like(k), v, 0)
+    mean_v = np.cumsum(v, axis=2) / np.arange(1, 6)[None, None, :, None]
+    out["uniform_mean"] = float(np.abs(o - mean_v).max())
+    out["uniform_lse"] = float(np.abs(lse - np.log(np.arange(1, 6))[None, None, :]).max())
+    # a slice that starts at position 2 sees keys 0..2+i
+    o2, _, _ = orc.causal_attention(np.zeros((2, 3, 2, 4)), np.zeros((2, 3, 4, 4)), v[:, :, :4], 2)
+    out["offset_mean"] = float(np.abs(o2 - mean_v[:, :, 2:4]).max())
+    # all weights and biases zero: both blocks add nothing, y = x
+    p = tiny_params(cfg, 3)
+    for name in p:
+        if name.startswith("w") or name.startswith("b"):
+            p[name] = np.zeros_like(p[name])
+    x, _ = tiny_inputs(cfg, 3)
+    out["zero_layer_identity"] = float(np.abs(orc.layer_forward(x, p, cfg)["y"] - x).max())
+    # LayerNorm with gamma 1, beta 0: mean 0 and biased variance var/(var+eps)
+    xr = rng.standard_normal((7, 16)) * 3 + 1
+    u, mean, rstd = orc.layer_norm(xr, np.ones(16), np.zeros(16), 1e-5)
+    var = xr.var(axis=-1)
+    out["ln_mean"] = float(np.abs(u.mean(-1)).max())
+    out["ln_var"] = float(np.abs(u.var(-1) - var / (var + 1e-5)).max())
+    out["ln_stats"] = float(max(np.abs(mean - xr.mean(-1)).max(),
+                                np.abs(rstd - 1 / np.sqrt(var + 1e-5)).max()))
+    # LayerNorm is invariant to shifting and scaling its input row
+    u2, _, _ = orc.layer_norm(xr * 2.5 + 4.0, np.ones(16), np.zeros(16), 0.0)
+    u3, _, _ = orc.layer_norm(xr, np.ones(16), np.zeros(16), 0.0)
+    out["ln_affine_invariance"] = float(np.abs(u2 - u3).max())
+    return out
+
+
+def gelu_table_errors(orc, table):
+    """Gap to standard-normal table values: GELU(z) = z Phi(z) and
+    GELU'(z) = Phi(z) + z phi(z) at the tabulated points."""
+    z = np.array([r["z"] for r in table])
+    phi = np.array([r["Phi"] for r in table])
+    dens = np.array([r["phi"] for r in table])
+    return dict(gelu=float(np.abs(orc.gelu(z) - z * phi).max()),
+                gelu_grad=float(np.abs(orc.gelu_grad(z) - (phi + z * dens)).max()))
+
+
+def cube_error(orc, seed=4):
+    """Oracle cube block vs the brute force, and the block identity
+    C_ij = sum_l A_il B_lj over a 2-way split of the FFN width."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((3, 6))
+    w1 = 0.5 * rng.standard_normal((10, 6))
+    b1 = 0.2 * rng.standard_normal(10)
+    w2 = 0.5 * rng.standard_normal((6, 10))
+    c = orc.cube_ffn_block(x, w1, b1, w2)
+    cb = np.array(brute.cube_ffn_block(x.tolist(), w1.tolist(), b1.tolist(), w2.tolist()))
+    halves = sum(orc.cube_ffn_block(x, w1[i:i + 5], b1[i:i + 5], w2[:, i:i + 5]) for i in (0, 5))
+    return max(float(np.abs(c - cb).max()), float(np.abs(c - halves).max()))
+
+
+def math_erf_ok():
+    return abs(math.erf(1.0) - 0.8427007929497149) < 1e-15

@@ -1,0 +1,91 @@
+"""CPU pins of the oracle: brute force, finite differences, the
+tensor-parallel shard-sum identity, token-slice invariance, closed forms and
+normal-table values.  No GPU is involved."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_brute_force_forward():
+    for seed in range(3):
+        assert pins.brute_error(oracle, seed) < 1e-12
+
+
+def test_finite_differences_backward():
+    assert pins.fd_error(oracle) < 1e-6
+
+
+@pytest.mark.parametrize("t", [1, 2])
+def test_shard_sum_whole_sequence(t):
+    # one slice covering the sequence: the Megatron split alone
+    assert pins.tp_error(oracle, t, [6]) < 1e-12
+
+
+def test_shard_sum_four_ranks():
+    cfg = dict(pins.TINY, hidden=16, heads=4, head_dim=4, ffn=32, tp=4)
+    assert pins.tp_error(oracle, 4, [2, 3, 1], cfg=cfg) < 1e-12
+
+
+def test_every_slice_partition():
+    # all 2^(s-1) partitions of s = 6 positions, on two ranks
+    worst = max(pins.tp_error(oracle, 2, parts) for parts in pins.compositions(6))
+    assert worst < 1e-12
+
+
+def test_token_by_token_single_rank():
+    assert pins.tp_error(oracle, 1, [1] * 6) < 1e-12
+
+
+def test_closed_forms():
+    errs = pins.closed_form_errors(oracle)
+    bad = {k: v for k, v in errs.items() if not v < 1e-12}
+    assert not bad, bad
+
+
+def test_gelu_normal_table():
+    with open(os.path.join(GOLDEN, "normal_table.json")) as fh:
+        table = json.load(fh)["rows"]
+    errs = pins.gelu_table_errors(oracle, table)
+    assert errs["gelu"] < 1e-14 and errs["gelu_grad"] < 1e-14, errs
+
+
+def test_cube_block():
+    assert pins.cube_error(oracle) < 1e-12
+
+
+def test_slice_order_is_enforced():
+    cfg = dict(pins.TINY, seq=4)
+    p = pins.tiny_params(cfg, 0)
+    x, _ = pins.tiny_inputs(cfg, 0)
+    sp = oracle.shard_params(p, 0, cfg)
+    kv = oracle.new_kv_cache(cfg)
+    with pytest.raises(ValueError):
+        oracle.shard_attn_forward(x, sp, cfg, kv, 2, 4)
+
+
+def test_shard_layer_step_single_rank():
+    """shard_layer_step (one device, reduced inputs handed in) equals the
+    unsharded layer at t = 1 once its own partial sums are fed back."""
+    cfg = dict(pins.TINY, seq=6)
+    p = pins.tiny_params(cfg, 7)
+    x, dy = pins.tiny_inputs(cfg, 7)
+    fw = oracle.layer_forward(x, p, cfg)
+    gr = oracle.layer_backward(dy, p, cfg, fw)
+    sp = oracle.shard_params(p, 0, cfg)
+    bounds = [0, 2, 3, 6]
+    z = np.zeros_like(x)
+    r1 = oracle.shard_layer_step(x, fw["h_mid"], dy, z, z, sp, cfg, bounds)
+    r2 = oracle.shard_layer_step(x, fw["h_mid"], dy, r1["p_du2"], z, sp, cfg, bounds)
+    r3 = oracle.shard_layer_step(x, fw["h_mid"], dy, r1["p_du2"], r2["p_du1"], sp, cfg, bounds)
+    assert np.abs(x + r3["p_attn"] + p["b_o"] - fw["h_mid"]).max() < 1e-12
+    assert np.abs(fw["h_mid"] + r3["p_mlp"] + p["b2"] - fw["y"]).max() < 1e-12
+    assert np.abs(r3["dx"] - gr["x"]).max() < 1e-12
+    for k in ("ln1_g", "ln2_g", "b_o", "b2", "w1", "w2"):
+        assert np.abs(r3["grads"][k] - gr[k]).max() < 1e-12
