@@ -1,0 +1,238 @@
+/*
+ * tpshard.h - one tensor-parallel device's share of a pre-LayerNorm GPT
+ * decoder layer, run over token slices, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Rank r of t holds a column-split QKV projection (its
+ * group of n/t heads) and a column-split FC1 with GELU, and a row-split
+ * output projection and FC2 whose products are partial sums that an
+ * all-reduce over the t ranks would add ("Transformer Training 11: model
+ * parallelism", tensor-parallelism slide).  LayerNorm is replicated on every
+ * rank (same deck, sequence-parallelism slide).  The layer runs slice by
+ * slice along the token dimension, each slice attending to the cached K/V of
+ * the slices before it ("TeraPipe: Token-Level Pipeline Parallelism for
+ * Training Large-Scale Language Models", section 3).  The backward uses the
+ * product-gradient forms of "Maximizing Parallelism in Distributed Training
+ * for Huge Neural Networks", section 3.1.2, and the bias/scale backward of
+ * its section 3.1.3.
+ *
+ * Forward of one layer (x: layer input, y: layer output; sums run over the
+ * t ranks and are the caller's all-reduce):
+ *   TP_FWD_ATTN  : P_attn,r = Attn_r(LN1(x)) W_o,r^T           (fp32 partial)
+ *   caller       : h_mid = x + sum_r P_attn,r + b_o             (tp_residual_combine)
+ *   TP_FWD_MLP   : P_mlp,r = GELU(LN2(h_mid) W1,r^T + b1,r) W2,r^T
+ *   caller       : y = h_mid + sum_r P_mlp,r + b2
+ * Backward, given dY:
+ *   TP_BWD_MLP   : dU2,r (fp32 partial), dW1,r, db1,r, dW2,r, db2
+ *   caller       : dU2 = sum_r dU2,r
+ *   TP_BWD_ATTN  : dH = dY + LN2^T(dU2); dU1,r (fp32 partial), dW_o,r, db_o,
+ *                  dW_qkv,r, db_qkv,r, dgamma2, dbeta2
+ *   caller       : dU1 = sum_r dU1,r
+ *   TP_BWD_LN1   : dX = dH + LN1^T(dU1), dgamma1, dbeta1
+ *
+ * Readings where the pages are silent: LayerNorm with the biased variance;
+ * exact erf GELU; attention scale 1/sqrt(d); the causal mask keeps the
+ * diagonal; no dropout; the row-split biases b_o and b2 are not in the
+ * partial sums (the caller adds them once, after the reduction).
+ *
+ * Layouts (row-major, element type = cfg->dtype unless marked fp32):
+ *   activations       [s, b, h]   sequence-major: token row m = p*b + bi, so a
+ *                                 slice is a contiguous block of rows
+ *   w_qkv             [3 h_t, h]  rows [0,h_t) W_q, [h_t,2h_t) W_k, [2h_t,3h_t)
+ *                                 W_v of this rank's heads (head i of the rank
+ *                                 owns rows [i d, (i+1) d) of each)
+ *   b_qkv             [3 h_t]
+ *   w_o               [h, h_t]    columns of the full W_o for this rank's heads
+ *   w1 [f_t, h], b1 [f_t], w2 [h, f_t]
+ *   ln*_g, ln*_b      [h]         replicated
+ *   K/V cache         [b, n_t, s, d] each
+ *   dK/dV accumulators[b, n_t, s, d] fp32 each
+ *   gradients         fp32, same shapes as the weights; ACCUMULATED (+=)
+ * with n_t = heads/t, h_t = hidden/t, f_t = ffn/t.
+ *
+ * Ownership.  The caller allocates every buffer (device memory for tensors,
+ * host memory for the structs and the partition) and keeps it alive until
+ * the stream has run the work; the library allocates nothing and frees
+ * nothing.  Structs are read (and, for the cache protocol fields, written)
+ * only during the call.
+ *
+ * Asynchrony.  Every call enqueues kernels on the given HIP stream
+ * (hipStream_t passed as void*; NULL is the default stream) and returns.
+ *
+ * Errors.  Argument checks run on the host before anything is enqueued; a
+ * failed check returns a non-zero tp_status, enqueues nothing and leaves
+ * every buffer and struct untouched.  TP_EHIP means a kernel launch failed;
+ * work already enqueued by that call may have run.  tp_last_error() gives a
+ * message for the calling thread's last failure.  No C++ exception crosses
+ * this interface.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_EINVAL = 1,       /* null pointer, bad enum, bad slice range */
+    TP_ESHAPE = 2,       /* configuration or partition inconsistent or unsupported size */
+    TP_EALIGN = 3,       /* a device pointer is not 16-byte aligned */
+    TP_EORDER = 4,       /* token-slice order violated (cache protocol) */
+    TP_EUNSUPPORTED = 5, /* valid but not implemented (e.g. head_dim not 64/128) */
+    TP_EHIP = 6          /* HIP runtime error while enqueueing */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Shape of the whole layer and of this rank's share.  hidden = heads *
+ * head_dim; heads and ffn divisible by tp_size; head_dim 64 or 128; ffn/t a
+ * multiple of 8; hidden <= 16384.  dtype is the storage type of activations,
+ * weights, the K/V cache and saved activations; all products accumulate in
+ * fp32 and all partial sums and gradients are fp32.  ln_eps is LayerNorm's
+ * epsilon (1e-5 in this repository's workloads). */
+typedef struct {
+    int32_t hidden;
+    int32_t heads;
+    int32_t head_dim;
+    int32_t ffn;
+    int32_t tp_size;
+    int32_t batch;
+    int32_t seq_len;
+    int32_t dtype; /* tp_dtype */
+    float ln_eps;
+} tp_shard_cfg;
+
+/* This rank's parameters, device pointers of element type cfg->dtype.
+ * b_o and b2 are not here: they are added by the caller after the
+ * reduction (tp_residual_combine). */
+typedef struct {
+    const void *ln1_g, *ln1_b;
+    const void *w_qkv, *b_qkv;
+    const void *w_o;
+    const void *ln2_g, *ln2_b;
+    const void *w1, *b1;
+    const void *w2;
+} tp_shard_weights;
+
+/* fp32 device gradient buffers, accumulated (+=); the caller zeroes them
+ * before the first backward call of a step.  b_o and b2 are the replicated
+ * row-split biases: every rank computes the same value. */
+typedef struct {
+    float *ln1_g, *ln1_b;
+    float *w_qkv, *b_qkv;
+    float *w_o, *b_o;
+    float *ln2_g, *ln2_b;
+    float *w1, *b1;
+    float *w2, *b2;
+} tp_shard_grads;
+
+/* Token-slice partition l_1..l_M of the sequence (host memory): every
+ * length >= 1 and the lengths sum to seq_len ("TeraPipe", section 3).  Slice
+ * j covers positions [o_j, o_j + l_j) with o_j = l_1 + ... + l_{j-1}, i.e.
+ * token rows [o_j b, (o_j + l_j) b) of every [s, b, ...] activation. */
+typedef struct {
+    int32_t num_slices;
+    const int32_t *len;
+} tp_partition;
+
+/* Prefix K/V cache (device memory, [b, n_t, s, d] each, element type
+ * cfg->dtype) and the number of positions already filled.  A forward
+ * attention call over slices [j0, j1) requires filled == o_{j0} (else
+ * TP_EORDER) and sets filled = o_{j1} when it returns TP_OK. */
+typedef struct {
+    void *k, *v;
+    int32_t filled;
+} tp_kv_cache;
+
+/* dK/dV accumulators of the backward over slices (device memory, fp32,
+ * [b, n_t, s, d] each).  Backward attention calls run the slices in reverse:
+ * a call over [j0, j1) requires done_from == o_{j1} (else TP_EORDER) and sets
+ * done_from = o_{j0}.  Start a step with done_from = seq_len; the first call
+ * does not read the accumulators, so they need no zeroing. */
+typedef struct {
+    float *dk, *dv;
+    int32_t done_from;
+} tp_kv_grad;
+
+typedef enum { TP_FWD_ATTN = 0, TP_FWD_MLP = 1 } tp_fwd_phase;
+typedef enum { TP_BWD_MLP = 0, TP_BWD_ATTN = 1, TP_BWD_LN1 = 2 } tp_bwd_phase;
+
+/* Bytes of the opaque "saved" buffer: activations the forward keeps for the
+ * backward, for the whole sequence (u1, LN statistics, Q, O, log-sum-exp,
+ * u2, Z, GELU(Z)).  0 if cfg is invalid. */
+size_t tp_shard_saved_bytes(const tp_shard_cfg *cfg);
+
+/* Bytes of the per-call "scratch" buffer (any call, any slice range); its
+ * contents do not survive a call.  0 if cfg is invalid. */
+size_t tp_shard_scratch_bytes(const tp_shard_cfg *cfg);
+
+/* Forward of one phase over slices [slice_begin, slice_end) of part.
+ *   in           TP_FWD_ATTN: x [s, b, h]; TP_FWD_MLP: h_mid [s, b, h]
+ *                (the combined residual stream).  Only the call's rows are read.
+ *   partial_out  fp32 [s, b, h]: this rank's partial sum for the call's rows
+ *                (P_attn,r or P_mlp,r), overwritten.
+ *   kv           TP_FWD_ATTN: the cache, written at the call's positions;
+ *                TP_FWD_MLP: ignored (may be NULL).
+ *   saved        tp_shard_saved_bytes(cfg) bytes, written at the call's rows.
+ *   scratch      tp_shard_scratch_bytes(cfg) bytes.
+ * All device pointers 16-byte aligned. */
+tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
+                             const tp_partition *part, int32_t slice_begin, int32_t slice_end,
+                             int32_t phase, const void *in, float *partial_out,
+                             tp_kv_cache *kv, void *saved, void *scratch, void *stream);
+
+/* Backward of one phase over slices [slice_begin, slice_end).  Phases of one
+ * slice range run in the order MLP, ATTN, LN1; slice ranges run in reverse.
+ *   dy           TP_BWD_MLP, TP_BWD_ATTN: gradient of the layer output y
+ *                [s, b, h]; TP_BWD_LN1: unused.
+ *   ln_in        TP_BWD_ATTN: h_mid (the input of LN2); TP_BWD_LN1: x (the
+ *                input of LN1); TP_BWD_MLP: unused.
+ *   reduced_in   fp32 [s, b, h]: TP_BWD_ATTN: sum_r dU2,r; TP_BWD_LN1:
+ *                sum_r dU1,r; TP_BWD_MLP: unused.
+ *   partial_out  fp32 [s, b, h], overwritten at the call's rows:
+ *                TP_BWD_MLP: dU2,r; TP_BWD_ATTN: dU1,r; TP_BWD_LN1: unused.
+ *   dh           [s, b, h]: written by TP_BWD_ATTN, read by TP_BWD_LN1.
+ *   dx           [s, b, h]: written by TP_BWD_LN1.
+ *   g            gradients, accumulated (+=).
+ *   kv, kvg      TP_BWD_ATTN only: the cache the forward filled and the
+ *                dK/dV accumulators (protocol above).
+ *   saved        the buffer the forward filled for these rows. */
+tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
+                             const tp_partition *part, int32_t slice_begin, int32_t slice_end,
+                             int32_t phase, const void *dy, const void *ln_in,
+                             const float *reduced_in, float *partial_out, void *dh, void *dx,
+                             const tp_shard_grads *g, const tp_kv_cache *kv, tp_kv_grad *kvg,
+                             const void *saved, void *scratch, void *stream);
+
+/* The caller's step after an all-reduce ("Transformer Training 11",
+ * tensor-parallelism slide: one all-reduce adds the partial sums):
+ * out[m][c] = resid[m][c] + reduced[m][c] + bias[c] for rows m < rows.
+ * resid, bias, out: element type cfg->dtype ([rows, hidden], [hidden]);
+ * reduced fp32 [rows, hidden]. */
+tp_status tp_residual_combine(const tp_shard_cfg *cfg, int64_t rows, const void *resid,
+                              const float *reduced, const void *bias, void *out, void *stream);
+
+/* One device's block of a 2x2x2 cube-partitioned FFN ("Maximizing
+ * Parallelism ...", section 3.1.2: each processor multiplies (M/p, N/p) by
+ * (N/p, K/p) sub-matrices; section 2.3: C_ij = sum_l A_il B_lj), bf16 with
+ * fp32 accumulation:
+ *   hbuf = GELU(x w1^T + b1)  (bf16 [rows, ffn], caller-provided)
+ *   out  = hbuf w2^T          (fp32 [rows, hidden]: the block's partial sum;
+ *                              the reduction across the cube is not taken)
+ * x [rows, hidden], w1 [ffn, hidden], b1 [ffn], w2 [hidden, ffn], all bf16.
+ * hidden and ffn multiples of 8. */
+tp_status tp_cube_ffn_block(int32_t rows, int32_t hidden, int32_t ffn, const void *x,
+                            const void *w1, const void *b1, const void *w2, void *hbuf,
+                            float *out, void *stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *tp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

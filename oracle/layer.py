@@ -191,9 +191,17 @@ def causal_attention_backward(do, q, k, v, p, o):
 # The unsharded layer ([MP] section 3.2; [TT11] tensor-parallel slide)
 # ----------------------------------------------------------------------------
 
+def _mm(a, m):
+    """a @ m over the last axis of a, as one 2-D product of the flattened
+    rows (numpy would otherwise loop over the leading axes)."""
+    a = np.asarray(a, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    return (a.reshape(-1, a.shape[-1]) @ m).reshape(a.shape[:-1] + (m.shape[-1],))
+
+
 def _linear(a, w, b=None):
     """y = a W^T (+ b) with W stored [out, in]."""
-    y = a @ w.T
+    y = _mm(a, np.asarray(w).T)
     return y if b is None else y + b
 
 
@@ -238,18 +246,18 @@ def layer_backward(dy, p, cfg, fw):
     # MLP block
     gr["b2"] = _rows(dy).sum(axis=0)
     gr["w2"] = _rows(dy).T @ _rows(fw["g"])
-    dg = dy @ p["w2"]
+    dg = _mm(dy, p["w2"])
     dz = dg * gelu_grad(fw["z"])
     gr["b1"] = _rows(dz).sum(axis=0)
     gr["w1"] = _rows(dz).T @ _rows(fw["u2"])
-    du2 = dz @ p["w1"]
+    du2 = _mm(dz, p["w1"])
     dln2, gr["ln2_g"], gr["ln2_b"] = layer_norm_backward(
         du2, fw["h_mid"], p["ln2_g"], fw["mu2"], fw["rstd2"])
     dh = dy + dln2
     # attention block
     gr["b_o"] = _rows(dh).sum(axis=0)
     gr["w_o"] = _rows(dh).T @ _rows(fw["om"])
-    dom = dh @ p["w_o"]
+    dom = _mm(dh, p["w_o"])
     dq, dk, dv = causal_attention_backward(
         heads_split(dom, n), fw["q"], fw["k"], fw["v"], fw["prob"], fw["o"])
     du1 = np.zeros_like(fw["u1"])
@@ -257,7 +265,7 @@ def layer_backward(dy, p, cfg, fw):
         dm = heads_merge(dt)
         gr["b_" + name] = _rows(dm).sum(axis=0)
         gr["w_" + name] = _rows(dm).T @ _rows(fw["u1"])
-        du1 += dm @ p["w_" + name]
+        du1 += _mm(dm, p["w_" + name])
     dln1, gr["ln1_g"], gr["ln1_b"] = layer_norm_backward(
         du1, fw["x"], p["ln1_g"], fw["mu1"], fw["rstd1"])
     gr["x"] = dh + dln1
@@ -367,11 +375,11 @@ def shard_mlp_backward(dy_rows, sp, saved_mlp):
     dW2,r = dY^T G, dW1,r = dZ^T u2 ([MP] 3.1.2), db1,r = sum dZ and the
     replicated db2 = sum dY ([MP] 3.1.3).  Returns (dU2_partial, grads)."""
     dy = np.asarray(dy_rows, dtype=np.float64)
-    dg = dy @ sp["w2"]
+    dg = _mm(dy, sp["w2"])
     dz = dg * gelu_grad(saved_mlp["z"])
     gr = dict(w2=_rows(dy).T @ _rows(saved_mlp["g"]), b2=_rows(dy).sum(axis=0),
               w1=_rows(dz).T @ _rows(saved_mlp["u2"]), b1=_rows(dz).sum(axis=0))
-    return dz @ sp["w1"], gr
+    return _mm(dz, sp["w1"]), gr
 
 
 def shard_attn_backward(dy_rows, du2_sum_rows, sp, saved_mlp, saved_attn, kv, kvg):
@@ -397,7 +405,7 @@ def shard_attn_backward(dy_rows, du2_sum_rows, sp, saved_mlp, saved_attn, kv, kv
     dh = dy + dln2
     gr = dict(ln2_g=dg2, ln2_b=db2, b_o=_rows(dh).sum(axis=0),
               w_o=_rows(dh).T @ _rows(saved_attn["om"]))
-    dom = dh @ sp["w_o"]
+    dom = _mm(dh, sp["w_o"])
     dq, dk, dv = causal_attention_backward(
         heads_split(dom, nt), saved_attn["q"], kv["k"][:, :, :stop],
         kv["v"][:, :, :stop], saved_attn["prob"], saved_attn["o"])
@@ -409,7 +417,7 @@ def shard_attn_backward(dy_rows, du2_sum_rows, sp, saved_mlp, saved_attn, kv, kv
                            heads_merge(kvg["dv"][:, :, start:stop])], axis=-1)
     gr["w_qkv"] = _rows(dqkv).T @ _rows(saved_attn["u1"])
     gr["b_qkv"] = _rows(dqkv).sum(axis=0)
-    return dh, dqkv @ sp["w_qkv"], gr
+    return dh, _mm(dqkv, sp["w_qkv"]), gr
 
 
 def ln1_backward(dh_rows, du1_sum_rows, sp, saved_attn):

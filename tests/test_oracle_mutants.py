@@ -41,7 +41,7 @@ MUTANTS = [
     ("shard_attn_forward", 'partial = _linear(om, sp["w_o"])', 'partial = _linear(om, sp["w_o"], sp["b_o"])'),
     ("shard_attn_backward", 'kvg["dk"][:, :, :stop] += dk', 'kvg["dk"][:, :, :stop] = dk'),
     ("shard_attn_backward", 'heads_merge(kvg["dv"][:, :, start:stop])', 'heads_merge(kvg["dk"][:, :, start:stop])'),
-    ("shard_mlp_backward", 'return dz @ sp["w1"], gr', 'return dg @ sp["w1"], gr'),
+    ("shard_mlp_backward", 'return _mm(dz, sp["w1"]), gr', 'return _mm(dg, sp["w1"]), gr'),
     ("ln1_backward", 'return np.asarray(dh_rows, dtype=np.float64) + dln1', 'return dln1'),
     ("cube_ffn_block", "return gelu(x @", "return (x @"),
 ]

@@ -1,0 +1,137 @@
+"""ctypes binding of the C-ABI in include/tpshard.h.
+
+Argument marshalling only: the functions below take integers (device
+addresses, sizes, a HIP stream handle) and host structs, call the library,
+and raise TPError on a non-zero status.  All arithmetic runs in the HIP
+kernels of libtpshard.so; loading fails loudly if the library is missing.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpshard.so")
+
+TP_OK, TP_EINVAL, TP_ESHAPE, TP_EALIGN, TP_EORDER, TP_EUNSUPPORTED, TP_EHIP = range(7)
+STATUS_NAMES = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_ESHAPE", 3: "TP_EALIGN", 4: "TP_EORDER",
+                5: "TP_EUNSUPPORTED", 6: "TP_EHIP"}
+TP_F32, TP_BF16 = 0, 1
+TP_FWD_ATTN, TP_FWD_MLP = 0, 1
+TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1 = 0, 1, 2
+
+EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
+            "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_last_error"]
+
+
+class TPError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), msg))
+        self.status = status
+
+
+class tp_shard_cfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("tp_size", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+WEIGHT_FIELDS = ["ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "ln2_g", "ln2_b", "w1", "b1", "w2"]
+GRAD_FIELDS = ["ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2"]
+
+
+class tp_shard_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class tp_shard_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
+
+
+class tp_partition(ctypes.Structure):
+    _fields_ = [("num_slices", ctypes.c_int32), ("len", ctypes.POINTER(ctypes.c_int32))]
+
+
+class tp_kv_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("filled", ctypes.c_int32)]
+
+
+class tp_kv_grad(ctypes.Structure):
+    _fields_ = [("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("done_from", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtpshard.so is not built (run python -m token_transformer_layer_amd.build); "
+                           "there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.tp_shard_saved_bytes.argtypes = [P(tp_shard_cfg)]
+    L.tp_shard_saved_bytes.restype = ctypes.c_size_t
+    L.tp_shard_scratch_bytes.argtypes = [P(tp_shard_cfg)]
+    L.tp_shard_scratch_bytes.restype = ctypes.c_size_t
+    L.tp_shard_layer_fwd.argtypes = [P(tp_shard_cfg), P(tp_shard_weights), P(tp_partition), i32, i32, i32,
+                                     vp, vp, P(tp_kv_cache), vp, vp, vp]
+    L.tp_shard_layer_fwd.restype = ctypes.c_int
+    L.tp_shard_layer_bwd.argtypes = [P(tp_shard_cfg), P(tp_shard_weights), P(tp_partition), i32, i32, i32,
+                                     vp, vp, vp, vp, vp, vp, P(tp_shard_grads), P(tp_kv_cache), P(tp_kv_grad),
+                                     vp, vp, vp]
+    L.tp_shard_layer_bwd.restype = ctypes.c_int
+    L.tp_residual_combine.argtypes = [P(tp_shard_cfg), i64, vp, vp, vp, vp, vp]
+    L.tp_residual_combine.restype = ctypes.c_int
+    L.tp_cube_ffn_block.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.tp_cube_ffn_block.restype = ctypes.c_int
+    L.tp_last_error.argtypes = []
+    L.tp_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != TP_OK:
+        raise TPError(status, lib().tp_last_error().decode())
+
+
+def make_partition(lengths):
+    """Host partition struct; the returned object keeps its array alive."""
+    arr = (ctypes.c_int32 * len(lengths))(*[int(n) for n in lengths])
+    part = tp_partition(len(lengths), ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    part._keep = arr
+    return part
+
+
+def tp_shard_saved_bytes(cfg):
+    return lib().tp_shard_saved_bytes(ctypes.byref(cfg))
+
+
+def tp_shard_scratch_bytes(cfg):
+    return lib().tp_shard_scratch_bytes(ctypes.byref(cfg))
+
+
+def tp_shard_layer_fwd(cfg, w, part, slice_begin, slice_end, phase, in_ptr, partial_out, kv, saved, scratch,
+                       stream):
+    _check(lib().tp_shard_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(part), slice_begin,
+                                    slice_end, phase, in_ptr, partial_out,
+                                    ctypes.byref(kv) if kv is not None else None, saved, scratch, stream))
+
+
+def tp_shard_layer_bwd(cfg, w, part, slice_begin, slice_end, phase, dy, ln_in, reduced_in, partial_out, dh, dx,
+                       g, kv, kvg, saved, scratch, stream):
+    _check(lib().tp_shard_layer_bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(part), slice_begin,
+                                    slice_end, phase, dy, ln_in, reduced_in, partial_out, dh, dx,
+                                    ctypes.byref(g), ctypes.byref(kv) if kv is not None else None,
+                                    ctypes.byref(kvg) if kvg is not None else None, saved, scratch, stream))
+
+
+def tp_residual_combine(cfg, rows, resid, reduced, bias, out, stream):
+    _check(lib().tp_residual_combine(ctypes.byref(cfg), rows, resid, reduced, bias, out, stream))
+
+
+def tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream):
+    _check(lib().tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream))

@@ -1,0 +1,455 @@
+// C-ABI of the layer-shard library: argument checks, buffer layouts of the
+// saved/scratch regions, and the kernel sequence of each phase.
+//
+// The phase split follows the two all-reduces per layer and direction of
+// "Transformer Training 11: model parallelism" (tensor-parallelism slide):
+// every call ends where a partial sum must be reduced across ranks, and the
+// next phase starts from the reduced tensor.  Calls run over a range of token
+// slices ("TeraPipe", section 3): position-wise steps (LayerNorm, the
+// products, GELU) batch the rows of all slices in the range, and attention
+// covers the range's queries against the cache prefix [0, end of range).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "tpshard.h"
+
+using namespace tpk;
+
+namespace {
+
+thread_local std::string g_err;
+
+tp_status fail(tp_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+constexpr int64_t kMaxBuffer = (int64_t)1 << 31;  // buffer loads address < 2^31 bytes
+
+struct Dims {
+    int64_t h, n, d, f, t, b, s, nt, ht, ft, T;
+    int es;
+    DType dt;
+};
+
+tp_status check_cfg(const tp_shard_cfg *c, Dims *o) {
+    if (!c) return fail(TP_EINVAL, "cfg is NULL");
+    if (c->dtype != TP_F32 && c->dtype != TP_BF16) return fail(TP_EINVAL, "dtype %d is not TP_F32 or TP_BF16", c->dtype);
+    if (c->hidden <= 0 || c->heads <= 0 || c->head_dim <= 0 || c->ffn <= 0 || c->tp_size <= 0 || c->batch <= 0 ||
+        c->seq_len <= 0)
+        return fail(TP_ESHAPE, "every size in cfg must be positive");
+    if ((int64_t)c->heads * c->head_dim != c->hidden)
+        return fail(TP_ESHAPE, "hidden (%d) != heads (%d) * head_dim (%d)", c->hidden, c->heads, c->head_dim);
+    if (c->heads % c->tp_size) return fail(TP_ESHAPE, "heads (%d) not divisible by tp_size (%d)", c->heads, c->tp_size);
+    if (c->ffn % c->tp_size) return fail(TP_ESHAPE, "ffn (%d) not divisible by tp_size (%d)", c->ffn, c->tp_size);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(TP_EUNSUPPORTED, "head_dim %d: only 64 and 128 are implemented", c->head_dim);
+    if ((c->ffn / c->tp_size) % 8) return fail(TP_ESHAPE, "ffn/tp_size (%d) must be a multiple of 8", c->ffn / c->tp_size);
+    if (c->hidden > 16384) return fail(TP_EUNSUPPORTED, "hidden %d > 16384", c->hidden);
+    if (!(c->ln_eps > 0.f) || !std::isfinite(c->ln_eps)) return fail(TP_EINVAL, "ln_eps must be positive and finite");
+    Dims d;
+    d.h = c->hidden; d.n = c->heads; d.d = c->head_dim; d.f = c->ffn; d.t = c->tp_size; d.b = c->batch; d.s = c->seq_len;
+    d.nt = d.n / d.t; d.ht = d.h / d.t; d.ft = d.f / d.t; d.T = d.b * d.s;
+    d.es = c->dtype == TP_BF16 ? 2 : 4;
+    d.dt = c->dtype == TP_BF16 ? DType::BF16 : DType::F32;
+    // every tensor the kernels address with 32-bit buffer offsets
+    int64_t widest = d.h > 3 * d.ht ? d.h : 3 * d.ht;
+    if (d.ft > widest) widest = d.ft;
+    if (d.T * widest * 4 >= kMaxBuffer || d.ft * d.h * 4 >= kMaxBuffer || 3 * d.ht * d.h * 4 >= kMaxBuffer)
+        return fail(TP_ESHAPE, "a tensor of this configuration exceeds 2 GiB");
+    if (o) *o = d;
+    return TP_OK;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// Regions of the saved buffer (full sequence, T = s*b token rows).
+struct Saved {
+    int64_t u1, mu1, rs1, q, o, lse, u2, mu2, rs2, z, g, total;
+};
+Saved saved_layout(const Dims &d) {
+    Saved L;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) { int64_t r = off; off += align256(bytes); return r; };
+    L.u1 = take(d.T * d.h * d.es);
+    L.mu1 = take(d.T * 4);
+    L.rs1 = take(d.T * 4);
+    L.q = take(d.b * d.nt * d.s * d.d * d.es);
+    L.o = take(d.T * d.ht * d.es);
+    L.lse = take(d.b * d.nt * d.s * 4);
+    L.u2 = take(d.T * d.h * d.es);
+    L.mu2 = take(d.T * 4);
+    L.rs2 = take(d.T * 4);
+    L.z = take(d.T * d.ft * d.es);
+    L.g = take(d.T * d.ft * d.es);
+    L.total = off;
+    return L;
+}
+
+struct Scratch {
+    int64_t dz, dO, delta, dqkv, red, total;
+};
+Scratch scratch_layout(const Dims &d) {
+    Scratch L;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) { int64_t r = off; off += align256(bytes); return r; };
+    L.dz = take(d.T * d.ft * d.es);
+    L.dO = take(d.T * d.ht * d.es);
+    L.delta = take(d.b * d.nt * d.s * 4);
+    L.dqkv = take(d.T * 3 * d.ht * d.es);
+    int64_t red = (int64_t)layernorm_bwd_partials_floats((int)d.T, (int)d.h);
+    int64_t widest = d.h;
+    if (d.ft > widest) widest = d.ft;
+    if (3 * d.ht > widest) widest = 3 * d.ht;
+    int64_t cs = (int64_t)colsum_partials_floats((int)d.T, (int)widest);
+    L.red = take((red > cs ? red : cs) * 4);
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+#define NEED(ptr, name)                                                                   \
+    do {                                                                                  \
+        if (!(ptr)) return fail(TP_EINVAL, "%s is NULL", name);                          \
+        if (!aligned16(ptr)) return fail(TP_EALIGN, "%s is not 16-byte aligned", name); \
+    } while (0)
+
+tp_status check_range(const Dims &d, const tp_partition *part, int32_t j0, int32_t j1, int64_t *o0, int64_t *o1) {
+    if (!part || !part->len) return fail(TP_EINVAL, "partition is NULL");
+    if (part->num_slices <= 0) return fail(TP_ESHAPE, "partition has no slices");
+    int64_t sum = 0;
+    for (int i = 0; i < part->num_slices; ++i) {
+        if (part->len[i] <= 0) return fail(TP_ESHAPE, "slice %d has length %d (must be >= 1)", i, part->len[i]);
+        sum += part->len[i];
+    }
+    if (sum != d.s) return fail(TP_ESHAPE, "slice lengths sum to %lld, seq_len is %lld", (long long)sum, (long long)d.s);
+    if (j0 < 0 || j1 > part->num_slices || j0 >= j1)
+        return fail(TP_EINVAL, "slice range [%d, %d) is not inside [0, %d)", j0, j1, part->num_slices);
+    int64_t a = 0;
+    for (int i = 0; i < j0; ++i) a += part->len[i];
+    int64_t b = a;
+    for (int i = j0; i < j1; ++i) b += part->len[i];
+    *o0 = a;
+    *o1 = b;
+    return TP_OK;
+}
+
+tp_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return TP_OK;
+    return fail(TP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCALL(expr, what)                          \
+    do {                                             \
+        tp_status _s = hip_status((expr), (what));   \
+        if (_s != TP_OK) return _s;                  \
+    } while (0)
+
+template <typename P>
+P at(const void *base, int64_t byte_off) {
+    return (P)((const char *)base + byte_off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tp_shard_saved_bytes(const tp_shard_cfg *cfg) {
+    Dims d;
+    if (check_cfg(cfg, &d) != TP_OK) return 0;
+    return (size_t)saved_layout(d).total;
+}
+
+size_t tp_shard_scratch_bytes(const tp_shard_cfg *cfg) {
+    Dims d;
+    if (check_cfg(cfg, &d) != TP_OK) return 0;
+    return (size_t)scratch_layout(d).total;
+}
+
+const char *tp_last_error(void) { return g_err.c_str(); }
+
+tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part,
+                             int32_t slice_begin, int32_t slice_end, int32_t phase, const void *in,
+                             float *partial_out, tp_kv_cache *kv, void *saved, void *scratch, void *stream) {
+    Dims d;
+    tp_status s = check_cfg(cfg, &d);
+    if (s != TP_OK) return s;
+    if (!w) return fail(TP_EINVAL, "weights is NULL");
+    int64_t o0, o1;
+    if ((s = check_range(d, part, slice_begin, slice_end, &o0, &o1)) != TP_OK) return s;
+    if (phase != TP_FWD_ATTN && phase != TP_FWD_MLP) return fail(TP_EINVAL, "forward phase %d is not valid", phase);
+    NEED(in, "in");
+    NEED(partial_out, "partial_out");
+    NEED(saved, "saved");
+    (void)scratch;
+    const Saved L = saved_layout(d);
+    const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
+    hipStream_t st = (hipStream_t)stream;
+    const int es = d.es;
+    EpiArgs e;
+    if (phase == TP_FWD_ATTN) {
+        NEED(w->ln1_g, "w.ln1_g");
+        NEED(w->ln1_b, "w.ln1_b");
+        NEED(w->w_qkv, "w.w_qkv");
+        NEED(w->b_qkv, "w.b_qkv");
+        NEED(w->w_o, "w.w_o");
+        if (!kv) return fail(TP_EINVAL, "kv is NULL");
+        NEED(kv->k, "kv.k");
+        NEED(kv->v, "kv.v");
+        if (kv->filled != o0)
+            return fail(TP_EORDER, "slices must run in order: cache holds %d positions, call starts at %lld", kv->filled,
+                        (long long)o0);
+        void *u1 = at<char *>(saved, L.u1 + r0 * d.h * es);
+        HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln1_g,
+                              w->ln1_b, u1, at<float *>(saved, L.mu1 + r0 * 4), at<float *>(saved, L.rs1 + r0 * 4), st),
+                "layernorm forward (LN1)");
+        e = EpiArgs{};
+        e.bias = w->b_qkv;
+        e.q = at<char *>(saved, L.q);
+        e.k = kv->k;
+        e.v = kv->v;
+        e.batch = (int)d.b; e.seq = (int)d.s; e.nt = (int)d.nt; e.d = (int)d.d; e.ht = (int)d.ht; e.row0 = (int)r0;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)(3 * d.ht), (int)d.h, Mat{u1, d.h, true}, Mat{w->w_qkv, d.h, true}, Epi::Qkv,
+                     e, st),
+                "QKV product");
+        AttnArgs a{};
+        a.batch = (int)d.b; a.nt = (int)d.nt; a.seq = (int)d.s; a.d = (int)d.d; a.q0 = (int)o0; a.q1 = (int)o1;
+        a.scale = 1.0f / std::sqrt((float)d.d);
+        a.q = at<char *>(saved, L.q); a.k = kv->k; a.v = kv->v;
+        a.o = at<char *>(saved, L.o); a.lse = at<float *>(saved, L.lse);
+        HIPCALL(attn_fwd(d.dt, a, st), "attention forward");
+        e = EpiArgs{};
+        e.c = partial_out + r0 * d.h;
+        e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ht, Mat{at<char *>(saved, L.o + r0 * d.ht * es), d.ht, true},
+                     Mat{w->w_o, d.ht, true}, Epi::StoreF32, e, st),
+                "out-projection product");
+        kv->filled = (int32_t)o1;
+        return TP_OK;
+    }
+    NEED(w->ln2_g, "w.ln2_g");
+    NEED(w->ln2_b, "w.ln2_b");
+    NEED(w->w1, "w.w1");
+    NEED(w->b1, "w.b1");
+    NEED(w->w2, "w.w2");
+    void *u2 = at<char *>(saved, L.u2 + r0 * d.h * es);
+    HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln2_g,
+                          w->ln2_b, u2, at<float *>(saved, L.mu2 + r0 * 4), at<float *>(saved, L.rs2 + r0 * 4), st),
+            "layernorm forward (LN2)");
+    void *z = at<char *>(saved, L.z + r0 * d.ft * es);
+    void *gg = at<char *>(saved, L.g + r0 * d.ft * es);
+    e = EpiArgs{};
+    e.c = z; e.ldc = d.ft; e.c2 = gg; e.ldc2 = d.ft; e.bias = w->b1;
+    HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{u2, d.h, true}, Mat{w->w1, d.h, true}, Epi::BiasGelu, e, st),
+            "FC1 product");
+    e = EpiArgs{};
+    e.c = partial_out + r0 * d.h;
+    e.ldc = d.h;
+    HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ft, Mat{gg, d.ft, true}, Mat{w->w2, d.ft, true}, Epi::StoreF32, e,
+                 st),
+            "FC2 product");
+    return TP_OK;
+}
+
+tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part,
+                             int32_t slice_begin, int32_t slice_end, int32_t phase, const void *dy, const void *ln_in,
+                             const float *reduced_in, float *partial_out, void *dh, void *dx, const tp_shard_grads *g,
+                             const tp_kv_cache *kv, tp_kv_grad *kvg, const void *saved, void *scratch, void *stream) {
+    Dims d;
+    tp_status s = check_cfg(cfg, &d);
+    if (s != TP_OK) return s;
+    if (!w) return fail(TP_EINVAL, "weights is NULL");
+    if (!g) return fail(TP_EINVAL, "grads is NULL");
+    int64_t o0, o1;
+    if ((s = check_range(d, part, slice_begin, slice_end, &o0, &o1)) != TP_OK) return s;
+    if (phase != TP_BWD_MLP && phase != TP_BWD_ATTN && phase != TP_BWD_LN1)
+        return fail(TP_EINVAL, "backward phase %d is not valid", phase);
+    NEED(saved, "saved");
+    NEED(scratch, "scratch");
+    const Saved L = saved_layout(d);
+    const Scratch S = scratch_layout(d);
+    const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
+    hipStream_t st = (hipStream_t)stream;
+    const int es = d.es;
+    float *red = at<float *>(scratch, S.red);
+    EpiArgs e;
+
+    if (phase == TP_BWD_MLP) {
+        NEED(dy, "dy");
+        NEED(partial_out, "partial_out");
+        NEED(w->w1, "w.w1");
+        NEED(w->w2, "w.w2");
+        NEED(g->w1, "g.w1");
+        NEED(g->b1, "g.b1");
+        NEED(g->w2, "g.w2");
+        NEED(g->b2, "g.b2");
+        const void *dyr = at<const char *>(dy, r0 * d.h * es);
+        void *dz = at<char *>(scratch, S.dz + r0 * d.ft * es);
+        const void *z = at<const char *>(saved, L.z + r0 * d.ft * es);
+        const void *gg = at<const char *>(saved, L.g + r0 * d.ft * es);
+        const void *u2 = at<const char *>(saved, L.u2 + r0 * d.h * es);
+        e = EpiArgs{};
+        e.c = dz; e.ldc = d.ft; e.aux = z; e.ldaux = d.ft;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{dyr, d.h, true}, Mat{w->w2, d.ft, false}, Epi::GeluGrad,
+                     e, st),
+                "FC2 input-gradient product");
+        e = EpiArgs{};
+        e.c = partial_out + r0 * d.h; e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ft, Mat{dz, d.ft, true}, Mat{w->w1, d.h, false}, Epi::StoreF32,
+                     e, st),
+                "FC1 input-gradient product");
+        e = EpiArgs{};
+        e.c = g->w2; e.ldc = d.ft;
+        HIPCALL(gemm(d.dt, (int)d.h, (int)d.ft, (int)nrows, Mat{dyr, d.h, false}, Mat{gg, d.ft, false}, Epi::AccumF32, e,
+                     st),
+                "FC2 weight-gradient product");
+        e = EpiArgs{};
+        e.c = g->w1; e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)d.ft, (int)d.h, (int)nrows, Mat{dz, d.ft, false}, Mat{u2, d.h, false}, Epi::AccumF32, e,
+                     st),
+                "FC1 weight-gradient product");
+        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)d.ft, dz, d.ft, g->b1, red, st), "b1 gradient");
+        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)d.h, dyr, d.h, g->b2, red, st), "b2 gradient");
+        return TP_OK;
+    }
+
+    if (phase == TP_BWD_ATTN) {
+        NEED(dy, "dy");
+        NEED(ln_in, "ln_in");
+        NEED(reduced_in, "reduced_in");
+        NEED(partial_out, "partial_out");
+        NEED(dh, "dh");
+        NEED(w->ln2_g, "w.ln2_g");
+        NEED(w->w_qkv, "w.w_qkv");
+        NEED(w->w_o, "w.w_o");
+        NEED(g->ln2_g, "g.ln2_g");
+        NEED(g->ln2_b, "g.ln2_b");
+        NEED(g->w_o, "g.w_o");
+        NEED(g->b_o, "g.b_o");
+        NEED(g->w_qkv, "g.w_qkv");
+        NEED(g->b_qkv, "g.b_qkv");
+        if (!kv || !kvg) return fail(TP_EINVAL, "kv and kvg are required for TP_BWD_ATTN");
+        NEED(kv->k, "kv.k");
+        NEED(kv->v, "kv.v");
+        NEED(kvg->dk, "kvg.dk");
+        NEED(kvg->dv, "kvg.dv");
+        if (kv->filled < o1)
+            return fail(TP_EORDER, "the cache holds %d positions; this call needs %lld", kv->filled, (long long)o1);
+        if (kvg->done_from != o1)
+            return fail(TP_EORDER, "backward slices must run in reverse: done_from is %d, call ends at %lld",
+                        kvg->done_from, (long long)o1);
+        void *dhr = at<char *>(dh, r0 * d.h * es);
+        HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, at<const char *>(dy, r0 * d.h * es),
+                              at<const char *>(ln_in, r0 * d.h * es), w->ln2_g, at<const float *>(saved, L.mu2 + r0 * 4),
+                              at<const float *>(saved, L.rs2 + r0 * 4), dhr, g->ln2_g, g->ln2_b, red, st),
+                "layernorm backward (LN2)");
+        void *dO = at<char *>(scratch, S.dO + r0 * d.ht * es);
+        const void *o = at<const char *>(saved, L.o + r0 * d.ht * es);
+        e = EpiArgs{};
+        e.c = dO; e.ldc = d.ht;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.ht, (int)d.h, Mat{dhr, d.h, true}, Mat{w->w_o, d.ht, false}, Epi::Store, e,
+                     st),
+                "out-projection input-gradient product");
+        e = EpiArgs{};
+        e.c = g->w_o; e.ldc = d.ht;
+        HIPCALL(gemm(d.dt, (int)d.h, (int)d.ht, (int)nrows, Mat{dhr, d.h, false}, Mat{o, d.ht, false}, Epi::AccumF32, e,
+                     st),
+                "out-projection weight-gradient product");
+        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)d.h, dhr, d.h, g->b_o, red, st), "b_o gradient");
+        AttnArgs a{};
+        a.batch = (int)d.b; a.nt = (int)d.nt; a.seq = (int)d.s; a.d = (int)d.d; a.q0 = (int)o0; a.q1 = (int)o1;
+        a.scale = 1.0f / std::sqrt((float)d.d);
+        a.q = at<const char *>(saved, L.q); a.k = kv->k; a.v = kv->v;
+        a.o = const_cast<char *>(at<const char *>(saved, L.o));
+        a.lse = at<float *>(saved, L.lse);
+        a.dout = at<const char *>(scratch, S.dO);
+        a.delta = at<float *>(scratch, S.delta);
+        a.dqkv = at<char *>(scratch, S.dqkv);
+        a.dk_acc = kvg->dk; a.dv_acc = kvg->dv;
+        a.k_final0 = (int)o0;
+        a.acc_in = kvg->done_from != d.s;
+        HIPCALL(attn_bwd(d.dt, a, st), "attention backward");
+        const void *dqkv = at<const char *>(scratch, S.dqkv + r0 * 3 * d.ht * es);
+        const void *u1 = at<const char *>(saved, L.u1 + r0 * d.h * es);
+        e = EpiArgs{};
+        e.c = partial_out + r0 * d.h; e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)(3 * d.ht), Mat{dqkv, 3 * d.ht, true}, Mat{w->w_qkv, d.h, false},
+                     Epi::StoreF32, e, st),
+                "QKV input-gradient product");
+        e = EpiArgs{};
+        e.c = g->w_qkv; e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)(3 * d.ht), (int)d.h, (int)nrows, Mat{dqkv, 3 * d.ht, false}, Mat{u1, d.h, false},
+                     Epi::AccumF32, e, st),
+                "QKV weight-gradient product");
+        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)(3 * d.ht), dqkv, 3 * d.ht, g->b_qkv, red, st), "b_qkv gradient");
+        kvg->done_from = (int32_t)o0;
+        return TP_OK;
+    }
+
+    // TP_BWD_LN1
+    NEED(ln_in, "ln_in");
+    NEED(reduced_in, "reduced_in");
+    NEED(dh, "dh");
+    NEED(dx, "dx");
+    NEED(w->ln1_g, "w.ln1_g");
+    NEED(g->ln1_g, "g.ln1_g");
+    NEED(g->ln1_b, "g.ln1_b");
+    HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, at<const char *>(dh, r0 * d.h * es),
+                          at<const char *>(ln_in, r0 * d.h * es), w->ln1_g, at<const float *>(saved, L.mu1 + r0 * 4),
+                          at<const float *>(saved, L.rs1 + r0 * 4), at<char *>(dx, r0 * d.h * es), g->ln1_g, g->ln1_b,
+                          red, st),
+            "layernorm backward (LN1)");
+    return TP_OK;
+}
+
+tp_status tp_residual_combine(const tp_shard_cfg *cfg, int64_t rows, const void *resid, const float *reduced,
+                              const void *bias, void *out, void *stream) {
+    Dims d;
+    tp_status s = check_cfg(cfg, &d);
+    if (s != TP_OK) return s;
+    if (rows < 0 || rows > d.T) return fail(TP_ESHAPE, "rows %lld outside [0, batch*seq_len]", (long long)rows);
+    NEED(resid, "resid");
+    NEED(reduced, "reduced");
+    NEED(bias, "bias");
+    NEED(out, "out");
+    return hip_status(residual_combine(d.dt, rows, (int)d.h, resid, reduced, bias, out, (hipStream_t)stream),
+                      "residual combine");
+}
+
+tp_status tp_cube_ffn_block(int32_t rows, int32_t hidden, int32_t ffn, const void *x, const void *w1, const void *b1,
+                            const void *w2, void *hbuf, float *out, void *stream) {
+    if (rows <= 0 || hidden <= 0 || ffn <= 0) return fail(TP_ESHAPE, "rows, hidden and ffn must be positive");
+    if (hidden % 8 || ffn % 8) return fail(TP_ESHAPE, "hidden and ffn must be multiples of 8");
+    if ((int64_t)rows * ffn * 2 >= kMaxBuffer || (int64_t)rows * hidden * 4 >= kMaxBuffer ||
+        (int64_t)ffn * hidden * 2 >= kMaxBuffer)
+        return fail(TP_ESHAPE, "a tensor of this block exceeds 2 GiB");
+    NEED(x, "x");
+    NEED(w1, "w1");
+    NEED(b1, "b1");
+    NEED(w2, "w2");
+    NEED(hbuf, "hbuf");
+    NEED(out, "out");
+    hipStream_t st = (hipStream_t)stream;
+    EpiArgs e;
+    e.c = nullptr; e.c2 = hbuf; e.ldc2 = ffn; e.bias = b1;
+    HIPCALL(gemm(DType::BF16, rows, ffn, hidden, Mat{x, hidden, true}, Mat{w1, hidden, true}, Epi::BiasGelu, e, st),
+            "cube FC1 product");
+    e = EpiArgs{};
+    e.c = out; e.ldc = hidden;
+    HIPCALL(gemm(DType::BF16, rows, hidden, ffn, Mat{hbuf, ffn, true}, Mat{w2, ffn, true}, Epi::StoreF32, e, st),
+            "cube FC2 product");
+    return TP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,734 @@
+// Causal attention of one slice of queries over the prefix K/V cache, and
+// its backward, on gfx950.
+//
+// A slice's queries at positions [q0, q1) attend to cache positions
+// [0, q1): a token needs only the keys and values of earlier positions and
+// its own ("TeraPipe: Token-Level Pipeline Parallelism for Training
+// Large-Scale Language Models", section 3), and the heads of a rank are
+// independent ("Transformer Training 11: model parallelism",
+// tensor-parallelism slide).  Scores are q.k / sqrt(d), masked for keys after
+// the query; the softmax is taken online (running maximum and sum per query)
+// so K and V stream once per query tile from HBM through LDS.
+//
+// bf16 kernels use v_mfma_f32_16x16x32_bf16.  In the forward each wave owns
+// 16 queries and computes S^T = K Q^T, so one lane holds one query's scores
+// for 16 keys; those registers are, without any data movement, the B operand
+// of O^T += V^T P^T (the 32 keys of one MFMA step are taken as keys
+// 4g..4g+3 and 16+4g..16+4g+3 of lane group g, and V^T is read from LDS in
+// the same order).  The backward recomputes P from the saved log-sum-exp and
+// uses two kernels so that no floating-point atomics are needed and results
+// are deterministic: one per key tile (dK, dV, looping over the queries that
+// see those keys) and one per query tile (dQ, looping over the keys the
+// queries see).  dK and dV of keys before the call's first query are
+// accumulated in fp32 across calls, because the backward runs the slices in
+// reverse and later slices' queries also see earlier keys.
+//
+// fp32 kernels are plain one-wave-per-row loops (used for the fp32 storage
+// configuration only).
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS tile [64 rows][D] bf16 with 16-byte chunks swizzled by row.
+template <int D>
+__device__ __forceinline__ int rowtile_off(int row, int ch) {
+    constexpr int CH = D / 8;
+    return row * (D * 2) + ((ch ^ (row & (CH - 1))) << 4);
+}
+// LDS tile [D rows][64 keys] bf16 (transposed), 8-byte units swizzled by row.
+__device__ __forceinline__ int coltile_off(int row, int unit) { return row * 128 + ((unit ^ (row & 15)) << 3); }
+
+// Copies a 64 x D bf16 tile whose rows are `ld` elements apart, rows
+// [r0, r0+64) of which only rows < rend exist, into registers (16 bytes per
+// lane per vector, zeros past rend).
+template <int D>
+struct RowTile {
+    static constexpr int VEC = 64 * D / 8 / 256;
+    u32x4 r[VEC];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t base, int r0, int rend, int tid) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            int v = tid + i * 256;
+            int row = v / (D / 8), ch = v % (D / 8);
+            uint32_t off = (r0 + row < rend) ? (uint32_t)((base + (int64_t)(r0 + row) * D + ch * 8) * 2) : kOOB;
+            r[i] = buf_load16(rs, off);
+        }
+    }
+    // natural layout [row][D]
+    __device__ __forceinline__ void store_rows(char *lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            int v = tid + i * 256;
+            int row = v / (D / 8), ch = v % (D / 8);
+            *(u32x4 *)(lds + rowtile_off<D>(row, ch)) = r[i];
+        }
+    }
+};
+
+// Same tile, loaded so that each lane holds 4 consecutive rows of one
+// 8-column chunk, and stored transposed as [D][64].
+template <int D>
+struct ColTile {
+    static constexpr int NB = 16 * (D / 8);  // (4-row group, chunk) pairs
+    u32x4 r[4];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t base, int r0, int rend, int tid) {
+        if (tid < NB) {
+            int ch = tid % (D / 8), kg = tid / (D / 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int row = r0 + kg * 4 + i;
+                uint32_t off = row < rend ? (uint32_t)((base + (int64_t)row * D + ch * 8) * 2) : kOOB;
+                r[i] = buf_load16(rs, off);
+            }
+        }
+    }
+    __device__ __forceinline__ void store_cols(char *lds, int tid) const {
+        if (tid < NB) {
+            int ch = tid % (D / 8), kg = tid / (D / 8);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                uint32_t lo0 = r[0][c >> 1], lo1 = r[1][c >> 1], lo2 = r[2][c >> 1], lo3 = r[3][c >> 1];
+                uint32_t w0, w1;
+                if (c & 1) {
+                    w0 = (lo0 >> 16) | (lo1 & 0xffff0000u);
+                    w1 = (lo2 >> 16) | (lo3 & 0xffff0000u);
+                } else {
+                    w0 = (lo0 & 0xffffu) | (lo1 << 16);
+                    w1 = (lo2 & 0xffffu) | (lo3 << 16);
+                }
+                *(u32x2 *)(lds + coltile_off(ch * 8 + c, kg)) = u32x2{w0, w1};
+            }
+        }
+    }
+};
+
+// A operand of an MFMA step over 32 keys (or queries) from a transposed tile:
+// row `row`, units (step*8 + g) and (step*8 + 4 + g).
+__device__ __forceinline__ bf16x8 read_cols(const char *lds, int row, int step, int g) {
+    u32x2 a = *(const u32x2 *)(lds + coltile_off(row, step * 8 + g));
+    u32x2 b = *(const u32x2 *)(lds + coltile_off(row, step * 8 + 4 + g));
+    u32x4 w{a[0], a[1], b[0], b[1]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4 &lo, const f32x4 &hi) {
+    u32x4 w{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ float group_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float group_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+struct AttnP {
+    int batch, nt, seq, q0, q1, k_final0, acc_in;
+    float scale;
+    const bf16 *q, *k, *v, *o, *dout;
+    bf16 *out;  // forward: O; backward: dQKV
+    float *lse, *delta, *dk_acc, *dv_acc;
+    uint32_t kv_bytes, q_bytes;
+};
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_bf16(AttnP a) {
+    constexpr int KS = D / 32;  // MFMA steps over d
+    constexpr int DB = D / 16;  // 16-row blocks of d
+    __shared__ __attribute__((aligned(16))) char ks_lds[64 * D * 2];
+    __shared__ __attribute__((aligned(16))) char vt_lds[64 * D * 2];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int qt0 = a.q0 + blockIdx.x * 64;
+    const int qw0 = qt0 + w * 16;
+    const int my_q = qw0 + li;
+    const int q_eff = min(my_q, a.q1 - 1);  // padding lanes act as the last query
+    const int kend = min(a.q1, qt0 + 64);
+    const int64_t slab = (int64_t)bh * a.seq * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+
+    bf16x8 qreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        uint32_t off = my_q < a.q1 ? (uint32_t)((slab + (int64_t)my_q * D + s * 32 + g * 8) * 2) : kOOB;
+        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    }
+
+    f32x4 acc_o[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc_o[i] = f32x4{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    RowTile<D> kt_r;
+    ColTile<D> vt_r;
+    const int nkt = (kend + 63) / 64;
+    kt_r.load(rk, slab, 0, kend, tid);
+    vt_r.load(rv, slab, 0, kend, tid);
+    for (int kt = 0; kt < nkt; ++kt) {
+        kt_r.store_rows(ks_lds, tid);
+        vt_r.store_cols(vt_lds, tid);
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            kt_r.load(rk, slab, (kt + 1) * 64, kend, tid);
+            vt_r.load(rv, slab, (kt + 1) * 64, kend, tid);
+        }
+        const int key0 = kt * 64;
+        if (key0 <= qw0 + 15) {  // some key of the tile is visible to this wave
+            f32x4 s[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                s[kb] = f32x4{};
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                    bf16x8 ka = *(const bf16x8 *)(ks_lds + rowtile_off<D>(kb * 16 + li, st * 4 + g));
+                    s[kb] = mfma16(ka, qreg[st], s[kb]);
+                }
+            }
+            // S^T[key = key0 + kb*16 + 4g + v][query = my_q]
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    int key = key0 + kb * 16 + 4 * g + v;
+                    float x = key <= q_eff ? s[kb][v] * sl2 : -INFINITY;
+                    s[kb][v] = x;
+                    mt = fmaxf(mt, x);
+                }
+            mt = group_max(mt);
+            const float m_new = fmaxf(m_run, mt);  // finite: key 0 is always visible
+            const float alpha = exp2f(m_run - m_new);
+            m_run = m_new;
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float p = exp2f(s[kb][v] - m_new);
+                    s[kb][v] = p;
+                    ls += p;
+                }
+            l_run = l_run * alpha + ls;
+#pragma unroll
+            for (int i = 0; i < DB; ++i) acc_o[i] *= alpha;
+            bf16x8 pb[2] = {pack8(s[0], s[1]), pack8(s[2], s[3])};
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    acc_o[db] = mfma16(read_cols(vt_lds, db * 16 + li, st, g), pb[st], acc_o[db]);
+        }
+        __syncthreads();
+    }
+    const float l_tot = group_sum(l_run);
+    if (my_q < a.q1) {
+        const float inv = 1.0f / l_tot;
+        const int ht = a.nt * D;
+        bf16 *orow = const_cast<bf16 *>(a.out) + ((int64_t)my_q * a.batch + bi) * ht + head * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            u32x2 w2{pack_bf2(acc_o[db][0] * inv, acc_o[db][1] * inv), pack_bf2(acc_o[db][2] * inv, acc_o[db][3] * inv)};
+            *(u32x2 *)(orow + db * 16 + 4 * g) = w2;
+        }
+        if (g == 0) a.lse[(int64_t)bh * a.seq + my_q] = (m_run + log2f(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward
+// ---------------------------------------------------------------------------
+
+// delta[bh][p] = sum_j dO[p][j] O[p][j] for the queries [q0, q1).
+template <typename T>
+__global__ __launch_bounds__(256) void attn_delta_kernel(int batch, int nt, int seq, int d, int q0, int q1,
+                                                         const T *__restrict__ o, const T *__restrict__ dout,
+                                                         float *__restrict__ delta) {
+    const int64_t n = (int64_t)(q1 - q0) * batch * nt;
+    const int64_t i = blockIdx.x * 256LL + threadIdx.x;
+    if (i >= n) return;
+    const int head = (int)(i % nt);
+    const int64_t r = i / nt;  // call-local token row
+    const int bi = (int)(r % batch);
+    const int p = q0 + (int)(r / batch);
+    const int64_t base = ((int64_t)p * batch + bi) * nt * d + (int64_t)head * d;
+    float s = 0.f;
+    for (int j = 0; j < d; ++j) s += to_f32(o[base + j]) * to_f32(dout[base + j]);
+    delta[((int64_t)bi * nt + head) * seq + p] = s;
+}
+
+// dK, dV for the keys of tile blockIdx.x (keys [0, q1)), over the call's
+// queries [q0, q1).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(AttnP a) {
+    constexpr int KS = D / 32, DB = D / 16;
+    __shared__ __attribute__((aligned(16))) char q_lds[64 * D * 2];
+    __shared__ __attribute__((aligned(16))) char qt_lds[64 * D * 2];
+    __shared__ __attribute__((aligned(16))) char do_lds[64 * D * 2];
+    __shared__ __attribute__((aligned(16))) char dot_lds[64 * D * 2];
+    __shared__ float lse_lds[64], del_lds[64];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int kt0 = blockIdx.x * 64;
+    const int kw0 = kt0 + w * 16;
+    const int my_k = kw0 + li;
+    const int ht = a.nt * D;
+    const int64_t slab = (int64_t)bh * a.seq * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+    // dO lives token-major [s, b, ht]: rows of one (bi, head) are batch*ht apart
+    const uint32_t do_bytes = (uint32_t)(((int64_t)a.seq * a.batch * ht) * 2);
+    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, do_bytes);
+
+    bf16x8 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        uint32_t off = my_k < a.q1 ? (uint32_t)((slab + (int64_t)my_k * D + s * 32 + g * 8) * 2) : kOOB;
+        kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+        vreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    }
+    f32x4 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x4{}; acc_dv[i] = f32x4{}; }
+
+    const int qstart = max(a.q0, kt0);
+    const int nqt = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
+    RowTile<D> qr, dor;
+    ColTile<D> qc, doc;
+    // dO rows for (bi, head): element (p, j) at (p*batch + bi)*ht + head*D + j.
+    // The tile loaders take rows `D` apart from `base`, so dO goes through a
+    // per-row address instead (below).
+    auto load_tile = [&](int p0) {
+        qr.load(rq, slab, p0, a.q1, tid);
+        qc.load(rq, slab, p0, a.q1, tid);
+#pragma unroll
+        for (int i = 0; i < RowTile<D>::VEC; ++i) {
+            int v = tid + i * 256;
+            int row = v / (D / 8), ch = v % (D / 8);
+            int p = p0 + row;
+            uint32_t off = p < a.q1 ? (uint32_t)((((int64_t)p * a.batch + bi) * ht + head * D + ch * 8) * 2) : kOOB;
+            dor.r[i] = buf_load16(rdo, off);
+        }
+        if (tid < ColTile<D>::NB) {
+            int ch = tid % (D / 8), kg = tid / (D / 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int p = p0 + kg * 4 + i;
+                uint32_t off = p < a.q1 ? (uint32_t)((((int64_t)p * a.batch + bi) * ht + head * D + ch * 8) * 2) : kOOB;
+                doc.r[i] = buf_load16(rdo, off);
+            }
+        }
+    };
+    if (nqt > 0) load_tile(qstart);
+    for (int qt = 0; qt < nqt; ++qt) {
+        const int p0 = qstart + qt * 64;
+        qr.store_rows(q_lds, tid);
+        qc.store_cols(qt_lds, tid);
+        dor.store_rows(do_lds, tid);
+        doc.store_cols(dot_lds, tid);
+        if (tid < 64) {
+            int p = p0 + tid;
+            bool ok = p < a.q1;
+            lse_lds[tid] = ok ? a.lse[(int64_t)bh * a.seq + p] * kLog2e : INFINITY;
+            del_lds[tid] = ok ? a.delta[(int64_t)bh * a.seq + p] : 0.f;
+        }
+        __syncthreads();
+        if (qt + 1 < nqt) load_tile(p0 + 64);
+        if (p0 + 63 >= kw0) {  // some query of the tile sees some key of this wave
+            f32x4 sp[4], dp[4];
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                sp[qb] = f32x4{};
+                dp[qb] = f32x4{};
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                    bf16x8 qa = *(const bf16x8 *)(q_lds + rowtile_off<D>(qb * 16 + li, st * 4 + g));
+                    bf16x8 da = *(const bf16x8 *)(do_lds + rowtile_off<D>(qb * 16 + li, st * 4 + g));
+                    sp[qb] = mfma16(qa, kreg[st], sp[qb]);
+                    dp[qb] = mfma16(da, vreg[st], dp[qb]);
+                }
+            }
+            // sp[qb][v]: S[query = p0 + qb*16 + 4g + v][key = my_k]
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    int qi = qb * 16 + 4 * g + v;
+                    int p = p0 + qi;
+                    float pr = (my_k <= p) ? exp2f(sp[qb][v] * sl2 - lse_lds[qi]) : 0.f;
+                    sp[qb][v] = pr;
+                    dp[qb][v] = pr * (dp[qb][v] - del_lds[qi]);
+                }
+            bf16x8 pb[2] = {pack8(sp[0], sp[1]), pack8(sp[2], sp[3])};
+            bf16x8 sb[2] = {pack8(dp[0], dp[1]), pack8(dp[2], dp[3])};
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    acc_dv[db] = mfma16(read_cols(dot_lds, db * 16 + li, st, g), pb[st], acc_dv[db]);
+                    acc_dk[db] = mfma16(read_cols(qt_lds, db * 16 + li, st, g), sb[st], acc_dk[db]);
+                }
+        }
+        __syncthreads();
+    }
+    if (my_k >= a.q1) return;
+    // acc_dk[db][v] = dK[key = my_k][d = db*16 + 4g + v] / scale (same for dV, unscaled)
+    const int64_t arow = slab + (int64_t)my_k * D;
+    const bool final_key = my_k >= a.k_final0;
+    bf16 *dst = a.out + ((int64_t)my_k * a.batch + bi) * (3 * ht) + head * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int j = db * 16 + 4 * g;
+        f32x4 dk = acc_dk[db] * a.scale, dv = acc_dv[db];
+        if (a.acc_in) {
+            dk += *(const f32x4 *)(a.dk_acc + arow + j);
+            dv += *(const f32x4 *)(a.dv_acc + arow + j);
+        }
+        if (final_key) {
+            *(u32x2 *)(dst + ht + j) = u32x2{pack_bf2(dk[0], dk[1]), pack_bf2(dk[2], dk[3])};
+            *(u32x2 *)(dst + 2 * ht + j) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
+        } else {
+            *(f32x4 *)(a.dk_acc + arow + j) = dk;
+            *(f32x4 *)(a.dv_acc + arow + j) = dv;
+        }
+    }
+}
+
+// dQ for the query tile blockIdx.x of [q0, q1), over keys [0, q1).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_bf16(AttnP a) {
+    constexpr int KS = D / 32, DB = D / 16;
+    __shared__ __attribute__((aligned(16))) char k_lds[64 * D * 2];
+    __shared__ __attribute__((aligned(16))) char kt_lds[64 * D * 2];
+    __shared__ __attribute__((aligned(16))) char v_lds[64 * D * 2];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int qt0 = a.q0 + blockIdx.x * 64;
+    const int qw0 = qt0 + w * 16;
+    const int my_q = qw0 + li;
+    const int q_eff = min(my_q, a.q1 - 1);
+    const int kend = min(a.q1, qt0 + 64);
+    const int ht = a.nt * D;
+    const int64_t slab = (int64_t)bh * a.seq * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+    const uint32_t do_bytes = (uint32_t)(((int64_t)a.seq * a.batch * ht) * 2);
+    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, do_bytes);
+
+    bf16x8 qreg[KS], doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        bool ok = my_q < a.q1;
+        uint32_t off = ok ? (uint32_t)((slab + (int64_t)my_q * D + s * 32 + g * 8) * 2) : kOOB;
+        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+        uint32_t offd = ok ? (uint32_t)((((int64_t)my_q * a.batch + bi) * ht + head * D + s * 32 + g * 8) * 2) : kOOB;
+        doreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, offd));
+    }
+    const float lse2 = my_q < a.q1 ? a.lse[(int64_t)bh * a.seq + my_q] * kLog2e : INFINITY;
+    const float del = my_q < a.q1 ? a.delta[(int64_t)bh * a.seq + my_q] : 0.f;
+
+    f32x4 acc_dq[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc_dq[i] = f32x4{};
+
+    RowTile<D> kr, vr;
+    ColTile<D> kc;
+    const int nkt = (kend + 63) / 64;
+    kr.load(rk, slab, 0, kend, tid);
+    kc.load(rk, slab, 0, kend, tid);
+    vr.load(rv, slab, 0, kend, tid);
+    for (int kt = 0; kt < nkt; ++kt) {
+        kr.store_rows(k_lds, tid);
+        kc.store_cols(kt_lds, tid);
+        vr.store_rows(v_lds, tid);
+        __syncthreads();
+        if (kt + 1 < nkt) {
+            kr.load(rk, slab, (kt + 1) * 64, kend, tid);
+            kc.load(rk, slab, (kt + 1) * 64, kend, tid);
+            vr.load(rv, slab, (kt + 1) * 64, kend, tid);
+        }
+        const int key0 = kt * 64;
+        if (key0 <= qw0 + 15) {
+            f32x4 sp[4], dp[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sp[kb] = f32x4{};
+                dp[kb] = f32x4{};
+#pragma unroll
+                for (int st = 0; st < KS; ++st) {
+                    bf16x8 ka = *(const bf16x8 *)(k_lds + rowtile_off<D>(kb * 16 + li, st * 4 + g));
+                    bf16x8 va = *(const bf16x8 *)(v_lds + rowtile_off<D>(kb * 16 + li, st * 4 + g));
+                    sp[kb] = mfma16(ka, qreg[st], sp[kb]);
+                    dp[kb] = mfma16(va, doreg[st], dp[kb]);
+                }
+            }
+            // sp[kb][v]: S^T[key = key0 + kb*16 + 4g + v][query = my_q]
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    int key = key0 + kb * 16 + 4 * g + v;
+                    float pr = key <= q_eff ? exp2f(sp[kb][v] * sl2 - lse2) : 0.f;
+                    dp[kb][v] = pr * (dp[kb][v] - del);
+                }
+            bf16x8 sb[2] = {pack8(dp[0], dp[1]), pack8(dp[2], dp[3])};
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    acc_dq[db] = mfma16(read_cols(kt_lds, db * 16 + li, st, g), sb[st], acc_dq[db]);
+        }
+        __syncthreads();
+    }
+    if (my_q >= a.q1) return;
+    bf16 *dst = a.out + ((int64_t)my_q * a.batch + bi) * (3 * ht) + head * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        f32x4 dq = acc_dq[db] * a.scale;
+        *(u32x2 *)(dst + db * 16 + 4 * g) = u32x2{pack_bf2(dq[0], dq[1]), pack_bf2(dq[2], dq[3])};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernels: one wavefront per query (forward, dQ) or per key (dK, dV)
+// ---------------------------------------------------------------------------
+
+struct AttnF {
+    int batch, nt, seq, d, q0, q1, k_final0, acc_in;
+    float scale;
+    const float *q, *k, *v, *o, *dout;
+    float *out, *lse, *delta, *dk_acc, *dv_acc;
+};
+
+__global__ __launch_bounds__(64) void attn_fwd_f32(AttnF a) {
+    __shared__ float qs[128], ps[64];
+    const int lane = threadIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int p = a.q0 + blockIdx.x, d = a.d;
+    const int64_t slab = (int64_t)bh * a.seq * d;
+    for (int j = lane; j < d; j += 64) qs[j] = a.q[slab + (int64_t)p * d + j];
+    __syncthreads();
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int c0 = 0; c0 <= p; c0 += 64) {
+        int key = c0 + lane;
+        float s = -INFINITY;
+        if (key <= p) {
+            float acc = 0.f;
+            for (int j = 0; j < d; ++j) acc = fmaf(qs[j], a.k[slab + (int64_t)key * d + j], acc);
+            s = acc * a.scale;
+        }
+        float mn = fmaxf(m, wave_max(s));
+        float alpha = expf(m - mn);
+        float pr = key <= p ? expf(s - mn) : 0.f;
+        l = l * alpha + wave_sum(pr);
+        o0 *= alpha;
+        o1 *= alpha;
+        m = mn;
+        ps[lane] = pr;
+        __syncthreads();
+        int cnt = min(64, p + 1 - c0);
+        for (int t = 0; t < cnt; ++t) {
+            const float *vr = a.v + slab + (int64_t)(c0 + t) * d;
+            o0 = fmaf(ps[t], vr[lane], o0);
+            if (lane + 64 < d) o1 = fmaf(ps[t], vr[lane + 64], o1);
+        }
+        __syncthreads();
+    }
+    float *orow = a.out + ((int64_t)p * a.batch + bi) * (a.nt * d) + head * d;
+    if (lane < d) orow[lane] = o0 / l;
+    if (lane + 64 < d) orow[lane + 64] = o1 / l;
+    if (lane == 0) a.lse[(int64_t)bh * a.seq + p] = m + logf(l);
+}
+
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32(AttnF a) {
+    __shared__ float qs[128], dos[128], dss[64];
+    const int lane = threadIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int p = a.q0 + blockIdx.x, d = a.d, ht = a.nt * d;
+    const int64_t slab = (int64_t)bh * a.seq * d;
+    const float *dor = a.dout + ((int64_t)p * a.batch + bi) * ht + head * d;
+    for (int j = lane; j < d; j += 64) {
+        qs[j] = a.q[slab + (int64_t)p * d + j];
+        dos[j] = dor[j];
+    }
+    __syncthreads();
+    const float lse = a.lse[(int64_t)bh * a.seq + p], del = a.delta[(int64_t)bh * a.seq + p];
+    float dq0 = 0.f, dq1 = 0.f;
+    for (int c0 = 0; c0 <= p; c0 += 64) {
+        int key = c0 + lane;
+        float ds = 0.f;
+        if (key <= p) {
+            float s = 0.f, dp = 0.f;
+            for (int j = 0; j < d; ++j) {
+                s = fmaf(qs[j], a.k[slab + (int64_t)key * d + j], s);
+                dp = fmaf(dos[j], a.v[slab + (int64_t)key * d + j], dp);
+            }
+            float pr = expf(s * a.scale - lse);
+            ds = pr * (dp - del);
+        }
+        dss[lane] = ds;
+        __syncthreads();
+        int cnt = min(64, p + 1 - c0);
+        for (int t = 0; t < cnt; ++t) {
+            const float *kr = a.k + slab + (int64_t)(c0 + t) * d;
+            dq0 = fmaf(dss[t], kr[lane], dq0);
+            if (lane + 64 < d) dq1 = fmaf(dss[t], kr[lane + 64], dq1);
+        }
+        __syncthreads();
+    }
+    float *dst = a.out + ((int64_t)p * a.batch + bi) * (3 * ht) + head * d;
+    if (lane < d) dst[lane] = dq0 * a.scale;
+    if (lane + 64 < d) dst[lane + 64] = dq1 * a.scale;
+}
+
+__global__ __launch_bounds__(64) void attn_bwd_dkdv_f32(AttnF a) {
+    __shared__ float ks[128], vs[128], pss[64], dss[64];
+    const int lane = threadIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int key = blockIdx.x, d = a.d, ht = a.nt * d;
+    const int64_t slab = (int64_t)bh * a.seq * d;
+    for (int j = lane; j < d; j += 64) {
+        ks[j] = a.k[slab + (int64_t)key * d + j];
+        vs[j] = a.v[slab + (int64_t)key * d + j];
+    }
+    __syncthreads();
+    float dk0 = 0.f, dk1 = 0.f, dv0 = 0.f, dv1 = 0.f;
+    const int pstart = max(a.q0, key);
+    for (int c0 = pstart; c0 < a.q1; c0 += 64) {
+        int p = c0 + lane;
+        float pr = 0.f, ds = 0.f;
+        if (p < a.q1) {
+            const float *dor = a.dout + ((int64_t)p * a.batch + bi) * ht + head * d;
+            float s = 0.f, dp = 0.f;
+            for (int j = 0; j < d; ++j) {
+                s = fmaf(a.q[slab + (int64_t)p * d + j], ks[j], s);
+                dp = fmaf(dor[j], vs[j], dp);
+            }
+            pr = expf(s * a.scale - a.lse[(int64_t)bh * a.seq + p]);
+            ds = pr * (dp - a.delta[(int64_t)bh * a.seq + p]);
+        }
+        pss[lane] = pr;
+        dss[lane] = ds;
+        __syncthreads();
+        int cnt = min(64, a.q1 - c0);
+        for (int t = 0; t < cnt; ++t) {
+            int pp = c0 + t;
+            const float *dor = a.dout + ((int64_t)pp * a.batch + bi) * ht + head * d;
+            const float *qr = a.q + slab + (int64_t)pp * d;
+            dv0 = fmaf(pss[t], dor[lane], dv0);
+            dk0 = fmaf(dss[t], qr[lane], dk0);
+            if (lane + 64 < d) {
+                dv1 = fmaf(pss[t], dor[lane + 64], dv1);
+                dk1 = fmaf(dss[t], qr[lane + 64], dk1);
+            }
+        }
+        __syncthreads();
+    }
+    dk0 *= a.scale;
+    dk1 *= a.scale;
+    const int64_t arow = slab + (int64_t)key * d;
+    if (a.acc_in) {
+        if (lane < d) { dk0 += a.dk_acc[arow + lane]; dv0 += a.dv_acc[arow + lane]; }
+        if (lane + 64 < d) { dk1 += a.dk_acc[arow + lane + 64]; dv1 += a.dv_acc[arow + lane + 64]; }
+    }
+    if (key >= a.k_final0) {
+        float *dst = a.out + ((int64_t)key * a.batch + bi) * (3 * ht) + head * d;
+        if (lane < d) { dst[ht + lane] = dk0; dst[2 * ht + lane] = dv0; }
+        if (lane + 64 < d) { dst[ht + lane + 64] = dk1; dst[2 * ht + lane + 64] = dv1; }
+    } else {
+        if (lane < d) { a.dk_acc[arow + lane] = dk0; a.dv_acc[arow + lane] = dv0; }
+        if (lane + 64 < d) { a.dk_acc[arow + lane + 64] = dk1; a.dv_acc[arow + lane + 64] = dv1; }
+    }
+}
+
+}  // namespace
+
+hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
+    const int nq = x.q1 - x.q0;
+    if (nq <= 0) return hipSuccess;
+    const int bh = x.batch * x.nt;
+    if (dt == DType::BF16) {
+        AttnP p{};
+        p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
+        p.q = (const bf16 *)x.q; p.k = (const bf16 *)x.k; p.v = (const bf16 *)x.v;
+        p.out = (bf16 *)x.o; p.lse = x.lse;
+        p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
+        dim3 grid((nq + 63) / 64, bh);
+        if (x.d == 128) hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, dim3(256), 0, st, p);
+    } else {
+        AttnF p{};
+        p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.d = x.d; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
+        p.q = (const float *)x.q; p.k = (const float *)x.k; p.v = (const float *)x.v;
+        p.out = (float *)x.o; p.lse = x.lse;
+        hipLaunchKernelGGL(attn_fwd_f32, dim3(nq, bh), dim3(64), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
+    const int nq = x.q1 - x.q0;
+    if (nq <= 0) return hipSuccess;
+    const int bh = x.batch * x.nt;
+    const int64_t nd = (int64_t)nq * x.batch * x.nt;
+    const unsigned dgrid = (unsigned)((nd + 255) / 256);
+    if (dt == DType::BF16) {
+        hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(dgrid), dim3(256), 0, st, x.batch, x.nt, x.seq, x.d, x.q0,
+                           x.q1, (const bf16 *)x.o, (const bf16 *)x.dout, x.delta);
+        AttnP p{};
+        p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
+        p.k_final0 = x.k_final0; p.acc_in = x.acc_in ? 1 : 0;
+        p.q = (const bf16 *)x.q; p.k = (const bf16 *)x.k; p.v = (const bf16 *)x.v; p.o = (const bf16 *)x.o;
+        p.dout = (const bf16 *)x.dout; p.out = (bf16 *)x.dqkv; p.lse = x.lse; p.delta = x.delta;
+        p.dk_acc = x.dk_acc; p.dv_acc = x.dv_acc;
+        p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
+        dim3 gk((x.q1 + 63) / 64, bh), gq((nq + 63) / 64, bh);
+        if (x.d == 128) {
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16<128>, gk, dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_bwd_dq_bf16<128>, gq, dim3(256), 0, st, p);
+        } else {
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16<64>, gk, dim3(256), 0, st, p);
+            hipLaunchKernelGGL(attn_bwd_dq_bf16<64>, gq, dim3(256), 0, st, p);
+        }
+    } else {
+        hipLaunchKernelGGL(attn_delta_kernel<float>, dim3(dgrid), dim3(256), 0, st, x.batch, x.nt, x.seq, x.d, x.q0,
+                           x.q1, (const float *)x.o, (const float *)x.dout, x.delta);
+        AttnF p{};
+        p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.d = x.d; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
+        p.k_final0 = x.k_final0; p.acc_in = x.acc_in ? 1 : 0;
+        p.q = (const float *)x.q; p.k = (const float *)x.k; p.v = (const float *)x.v; p.o = (const float *)x.o;
+        p.dout = (const float *)x.dout; p.out = (float *)x.dqkv; p.lse = x.lse; p.delta = x.delta;
+        p.dk_acc = x.dk_acc; p.dv_acc = x.dv_acc;
+        hipLaunchKernelGGL(attn_bwd_dkdv_f32, dim3(x.q1, bh), dim3(64), 0, st, p);
+        hipLaunchKernelGGL(attn_bwd_dq_f32, dim3(nq, bh), dim3(64), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tpk

@@ -1,0 +1,89 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the gfx950
+// kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// One GEMM operand.  The product is C[m][n] = sum_k A[m][k] B[n][k].
+// kcontig: element (i, k) sits at p + i*ld + k (k contiguous); otherwise at
+// p + k*ld + i (the M/N index contiguous).
+struct Mat {
+    const void *p;
+    int64_t ld;
+    bool kcontig;
+};
+
+enum class Epi {
+    StoreF32,  // c fp32 [M][ldc] = acc
+    AccumF32,  // c fp32 [M][ldc] += acc
+    Store,     // c T [M][ldc] = acc
+    BiasGelu,  // z = acc + bias[n]; c T = z (if c != null); c2 T = GELU(z)
+    GeluGrad,  // c T = acc * GELU'(aux[m][n])  (aux T [M][ldaux])
+    Qkv,       // acc + bias[n] scattered into q/k/v [b, n_t, s, d]
+};
+
+struct EpiArgs {
+    void *c = nullptr;
+    int64_t ldc = 0;
+    void *c2 = nullptr;
+    int64_t ldc2 = 0;
+    const void *bias = nullptr;
+    const void *aux = nullptr;
+    int64_t ldaux = 0;
+    // Qkv scatter: token row m of the call is global row row0 + m = p*batch + bi
+    void *q = nullptr, *k = nullptr, *v = nullptr;
+    int batch = 1, seq = 1, nt = 1, d = 64, ht = 64, row0 = 0;
+};
+
+hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const EpiArgs &e,
+                hipStream_t st);
+
+// LayerNorm forward over rows [0, rows): u = LN(x) * g + b; mean/rstd fp32.
+hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, const void *g,
+                         const void *b, void *u, float *mean, float *rstd, hipStream_t st);
+
+// LayerNorm backward with residual: dx = resid + LN^T(du); the parameter
+// gradients are added into dg/db (fp32) through a deterministic two-stage
+// reduction that uses `partials` (fp32, layernorm_bwd_partials_floats).
+hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void *resid,
+                         const void *x, const void *g, const float *mean, const float *rstd,
+                         void *dx, float *dg, float *db, float *partials, hipStream_t st);
+size_t layernorm_bwd_partials_floats(int rows, int h);
+
+// Column sums over rows added into out (fp32), two stages via `partials`.
+hipError_t colsum_accum(DType dt, int rows, int n, const void *a, int64_t lda, float *out,
+                        float *partials, hipStream_t st);
+size_t colsum_partials_floats(int rows, int n);
+
+// out = resid + reduced + bias[c]
+hipError_t residual_combine(DType dt, int64_t rows, int h, const void *resid, const float *reduced,
+                            const void *bias, void *out, hipStream_t st);
+
+// Attention over the queries at positions [q0, q1) of every (batch row, head),
+// against keys [0, q1) of the cache.  q: [b, nt, s, d]; k, v: cache
+// [b, nt, s, d]; o: token-major [s, b, nt*d] (column head*d + j); lse fp32
+// [b, nt, s].
+struct AttnArgs {
+    int batch, nt, seq, d;
+    int q0, q1;
+    float scale;
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    // backward
+    const void *dout;     // token-major [s, b, nt*d]
+    float *delta;         // [b, nt, s] rowsum(dO * O)
+    void *dqkv;           // token-major [s, b, 3*nt*d]: dq cols [0,ht), dk [ht,2ht), dv [2ht,3ht)
+    float *dk_acc, *dv_acc;  // [b, nt, s, d] fp32 accumulators
+    int k_final0;         // keys in [k_final0, q1) are complete after this call
+    bool acc_in;          // accumulators hold earlier calls' contributions
+};
+hipError_t attn_fwd(DType dt, const AttnArgs &a, hipStream_t st);
+hipError_t attn_bwd(DType dt, const AttnArgs &a, hipStream_t st);
+
+}  // namespace tpk

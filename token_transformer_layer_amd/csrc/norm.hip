@@ -1,0 +1,292 @@
+// LayerNorm forward/backward, bias-gradient column sums and the residual
+// combine on gfx950.  All HBM-bound: each kernel reads and writes its rows
+// once, with 16-byte (bf16) or 32-byte (fp32) vector accesses, and reduces
+// within a row through wavefront shuffles and one LDS exchange.
+//
+// LayerNorm is replicated on every tensor-parallel rank ("Transformer
+// Training 11: model parallelism", sequence-parallelism slide) and applies
+// gamma and beta as matrix-vector ops ("Maximizing Parallelism in
+// Distributed Training for Huge Neural Networks", section 3.2); its backward
+// and the bias gradients follow that paper's section 3.1.3 (dA = dC * b,
+// db = sum of dC * A over rows).  Parameter gradients are reduced in two
+// deterministic stages (per-block partials, then one pass over the blocks),
+// so repeated runs give identical bits.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxVec = 8;  // 8 vectors of 8 elements per thread: h <= 16384
+
+__device__ __forceinline__ void load8(const float *p, float o[8]) {
+    float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16 *p, float o[8]) {
+    u32x4 w = *(const u32x4 *)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = bf_lo(w[i]); o[2 * i + 1] = bf_hi(w[i]); }
+}
+__device__ __forceinline__ void store8(float *p, const float v[8]) {
+    *(float4 *)p = float4{v[0], v[1], v[2], v[3]};
+    *(float4 *)(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(bf16 *p, const float v[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf2(v[2 * i], v[2 * i + 1]);
+    *(u32x4 *)p = w;
+}
+
+// Sum over the 256 threads of a block; every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, const T *__restrict__ x,
+                                                          const T *__restrict__ g, const T *__restrict__ b,
+                                                          T *__restrict__ u, float *__restrict__ mean,
+                                                          float *__restrict__ rstd) {
+    __shared__ float red[4];
+    const int row = blockIdx.x, nv = h >> 3;
+    const T *xr = x + (size_t)row * h;
+    float v[kMaxVec][8];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i) {
+        int c = threadIdx.x + i * kThreads;
+        if (c < nv) {
+            load8(xr + c * 8, v[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += v[i][j];
+        }
+    }
+    const float mu = block_sum(s, red) / (float)h;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i) {
+        int c = threadIdx.x + i * kThreads;
+        if (c < nv) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { float dlt = v[i][j] - mu; q += dlt * dlt; }
+        }
+    }
+    const float var = block_sum(q, red) / (float)h;
+    const float r = 1.0f / sqrtf(var + eps);
+    T *ur = u + (size_t)row * h;
+#pragma unroll
+    for (int i = 0; i < kMaxVec; ++i) {
+        int c = threadIdx.x + i * kThreads;
+        if (c < nv) {
+            float gg[8], bb[8], o[8];
+            load8(g + c * 8, gg);
+            load8(b + c * 8, bb);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = (v[i][j] - mu) * r * gg[j] + bb[j];
+            store8(ur + c * 8, o);
+        }
+    }
+    if (threadIdx.x == 0) {
+        mean[row] = mu;
+        rstd[row] = r;
+    }
+}
+
+// Rows [blockIdx.x * rpb, ...): dx = resid + rstd (gg - mean(gg) - xhat mean(gg xhat))
+// with gg = du * gamma; per-block partial sums of du * xhat and du go to
+// partials[block][0][:] and partials[block][1][:].
+template <typename T>
+__global__ __launch_bounds__(kThreads) void ln_bwd_kernel(int rows, int h, int rpb, const float *__restrict__ du,
+                                                          const T *__restrict__ resid, const T *__restrict__ x,
+                                                          const T *__restrict__ g, const float *__restrict__ mean,
+                                                          const float *__restrict__ rstd, T *__restrict__ dx,
+                                                          float *__restrict__ partials) {
+    extern __shared__ float accs[];  // [2][h]
+    __shared__ float red[4];
+    const int nv = h >> 3;
+    for (int c = threadIdx.x; c < 2 * h; c += kThreads) accs[c] = 0.f;
+    __syncthreads();
+    const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
+    for (int row = r0; row < r1; ++row) {
+        const float mu = mean[row], rs = rstd[row];
+        float dv[kMaxVec][8], xh[kMaxVec][8];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMaxVec; ++i) {
+            int c = threadIdx.x + i * kThreads;
+            if (c < nv) {
+                float gg[8];
+                load8(du + (size_t)row * h + c * 8, dv[i]);
+                load8(x + (size_t)row * h + c * 8, xh[i]);
+                load8(g + c * 8, gg);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    xh[i][j] = (xh[i][j] - mu) * rs;
+                    float gd = dv[i][j] * gg[j];
+                    s1 += gd;
+                    s2 += gd * xh[i][j];
+                    accs[c * 8 + j] += dv[i][j] * xh[i][j];
+                    accs[h + c * 8 + j] += dv[i][j];
+                }
+            }
+        }
+        const float m1 = block_sum(s1, red) / (float)h;
+        const float m2 = block_sum(s2, red) / (float)h;
+#pragma unroll
+        for (int i = 0; i < kMaxVec; ++i) {
+            int c = threadIdx.x + i * kThreads;
+            if (c < nv) {
+                float gg[8], rr[8], o[8];
+                load8(g + c * 8, gg);
+                load8(resid + (size_t)row * h + c * 8, rr);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) o[j] = rr[j] + rs * (dv[i][j] * gg[j] - m1 - xh[i][j] * m2);
+                store8(dx + (size_t)row * h + c * 8, o);
+            }
+        }
+    }
+    __syncthreads();
+    float *pb = partials + (size_t)blockIdx.x * 2 * h;
+    for (int c = threadIdx.x; c < 2 * h; c += kThreads) pb[c] = accs[c];
+}
+
+// out[c] += sum over blocks of partials[blk][c], for c < n; partial rows are
+// `stride` floats apart.
+__global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n, int64_t stride,
+                                                                 const float *__restrict__ partials,
+                                                                 float *__restrict__ out) {
+    int c = blockIdx.x * kThreads + threadIdx.x;
+    if (c >= n) return;
+    float s = 0.f;
+    for (int k = 0; k < nblk; ++k) s += partials[(size_t)k * stride + c];
+    out[c] += s;
+}
+
+// Per-chunk column sums: partials[chunk][c] = sum of a[r][c] over the rows of
+// chunk `blockIdx.y`; each thread owns 8 columns.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void colsum_kernel(int rows, int n, int64_t lda, int rpc,
+                                                          const T *__restrict__ a, float *__restrict__ partials) {
+    const int c8 = (blockIdx.x * kThreads + threadIdx.x) * 8;
+    if (c8 >= n) return;
+    const int r0 = blockIdx.y * rpc, r1 = min(rows, r0 + rpc);
+    float s[8] = {};
+    for (int r = r0; r < r1; ++r) {
+        float v[8];
+        load8(a + (size_t)r * lda + c8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] += v[j];
+    }
+    store8(partials + (size_t)blockIdx.y * n + c8, s);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_kernel(int64_t n8, int h, const T *__restrict__ resid,
+                                                           const float *__restrict__ red, const T *__restrict__ bias,
+                                                           T *__restrict__ out) {
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+        int64_t e = i * 8;
+        int c = (int)(e % h);
+        float a[8], r[8], b[8];
+        load8(resid + e, a);
+        load8(red + e, r);
+        load8(bias + c, b);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] += r[j] + b[j];
+        store8(out + e, a);
+    }
+}
+
+int ln_bwd_blocks(int rows) { return rows < 256 ? rows : 256; }
+int colsum_chunks(int rows) {
+    int c = (rows + 31) / 32;
+    return c < 64 ? (c < 1 ? 1 : c) : 64;
+}
+
+}  // namespace
+
+size_t layernorm_bwd_partials_floats(int rows, int h) { return (size_t)ln_bwd_blocks(rows) * 2 * h; }
+size_t colsum_partials_floats(int rows, int n) { return (size_t)colsum_chunks(rows) * n; }
+
+hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, const void *g, const void *b,
+                         void *u, float *mean, float *rstd, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (dt == DType::BF16)
+        hipLaunchKernelGGL(ln_fwd_kernel<bf16>, dim3(rows), dim3(kThreads), 0, st, h, eps, (const bf16 *)x,
+                           (const bf16 *)g, (const bf16 *)b, (bf16 *)u, mean, rstd);
+    else
+        hipLaunchKernelGGL(ln_fwd_kernel<float>, dim3(rows), dim3(kThreads), 0, st, h, eps, (const float *)x,
+                           (const float *)g, (const float *)b, (float *)u, mean, rstd);
+    return hipGetLastError();
+}
+
+hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void *resid, const void *x,
+                         const void *g, const float *mean, const float *rstd, void *dx, float *dg, float *db,
+                         float *partials, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    const int nblk = ln_bwd_blocks(rows), rpb = (rows + nblk - 1) / nblk;
+    const size_t lds = (size_t)2 * h * sizeof(float);
+    if (dt == DType::BF16) {
+        hipFuncSetAttribute((const void *)ln_bwd_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nblk), dim3(kThreads), lds, st, rows, h, rpb, du,
+                           (const bf16 *)resid, (const bf16 *)x, (const bf16 *)g, mean, rstd, (bf16 *)dx, partials);
+    } else {
+        hipFuncSetAttribute((const void *)ln_bwd_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nblk), dim3(kThreads), lds, st, rows, h, rpb, du,
+                           (const float *)resid, (const float *)x, (const float *)g, mean, rstd, (float *)dx,
+                           partials);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int gb = (h + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
+                       (const float *)partials, dg);
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
+                       (const float *)(partials + h), db);
+    return hipGetLastError();
+}
+
+hipError_t colsum_accum(DType dt, int rows, int n, const void *a, int64_t lda, float *out, float *partials,
+                        hipStream_t st) {
+    if (rows <= 0 || n <= 0) return hipSuccess;
+    const int nch = colsum_chunks(rows), rpc = (rows + nch - 1) / nch;
+    dim3 grid((n / 8 + kThreads - 1) / kThreads, nch);
+    if (dt == DType::BF16)
+        hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(kThreads), 0, st, rows, n, lda, rpc, (const bf16 *)a,
+                           partials);
+    else
+        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(kThreads), 0, st, rows, n, lda, rpc, (const float *)a,
+                           partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, nch, n,
+                       (int64_t)n, (const float *)partials, out);
+    return hipGetLastError();
+}
+
+hipError_t residual_combine(DType dt, int64_t rows, int h, const void *resid, const float *reduced,
+                            const void *bias, void *out, hipStream_t st) {
+    int64_t n8 = rows * h / 8;
+    if (n8 <= 0) return hipSuccess;
+    int64_t blocks = (n8 + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    if (dt == DType::BF16)
+        hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, st, n8, h,
+                           (const bf16 *)resid, reduced, (const bf16 *)bias, (bf16 *)out);
+    else
+        hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, st, n8, h,
+                           (const float *)resid, reduced, (const float *)bias, (float *)out);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

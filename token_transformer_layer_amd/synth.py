@@ -124,7 +124,11 @@ class _Draw:
 
 
 def _wstd(variant):
-    return 0.2 if variant == "sharp" else 0.02
+    # "sharp" (fp32 storage) and "peaked" (bf16 storage) raise the weight
+    # scale so the softmax is far from uniform; with bf16 Q and K the score
+    # rounding error grows with the score scale (std ~ w_std^2 h), so the
+    # bf16 variant stays at a scale where that error is small.
+    return {"sharp": 0.2, "peaked": 0.05}.get(variant, 0.02)
 
 
 def activations(cfg: LayerShape, seed=None):
@@ -140,7 +144,8 @@ def full_params(cfg: LayerShape, variant="standard", seed=None):
 
     variant "standard": linear weights N(0, 0.02), biases 0, gamma 1, beta 0.
     "perturbed": also biases N(0, 0.02), gamma 1 + N(0, 0.1), beta N(0, 0.02).
-    "sharp": as "perturbed" with weights N(0, 0.2) so the softmax is peaked."""
+    "sharp" / "peaked": as "perturbed" with weights N(0, 0.2) / N(0, 0.05) so
+    the softmax is far from uniform."""
     d = _Draw((cfg.seed if seed is None else seed) + 7919, cfg.dtype)
     h, f = cfg.hidden, cfg.ffn
     std = _wstd(variant)
