@@ -1,0 +1,260 @@
+"""Throughput of one rank's share of a tensor-parallel GPT decoder layer, run
+over token slices, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+One step = every phase of the layer shard over one batch: forward attention
+and MLP blocks, the two residual combines a caller runs after its
+all-reduces, and the backward MLP, attention and LN1 phases (the reduced
+gradients are this rank's own partials: on one GPU the all-reduce is the
+identity).  The headline runs each phase as one library call over all
+slices of the partition (position-wise products batch the slices' rows;
+attention covers each query against its own prefix).  A second figure runs
+one call per slice in slice order (backward in reverse), as a pipeline stage
+would receive them.
+
+Inputs are synthetic and seeded (token_transformer_layer_amd.synth): x, dY
+~ N(0, 1), linear weights ~ N(0, 0.02), biases 0, gamma 1, beta 0, all bf16.
+Gradient buffers are zeroed once before the timed steps (the optimizer's
+job, outside the layer), so the timed steps accumulate into them.
+
+Prints ONE JSON line.  value = algorithmic fwd+bwd TFLOP/s of the step:
+GEMMs 3 x 2 T h (4 h_t + 2 f_t) plus causal attention 3 x 2 b h_t s (s+1)
+flops, over the measured time per step.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def step_flops(shape):
+    """Algorithmic flops of one fwd+bwd step of the shard (see module doc)."""
+    T, h = shape.batch * shape.seq, shape.hidden
+    ht, ft = h // shape.tp, shape.ffn // shape.tp
+    gemm = 3 * 2.0 * T * h * (4 * ht + 2 * ft)
+    attn = 3 * 2.0 * shape.batch * ht * shape.seq * (shape.seq + 1)
+    return gemm, attn
+
+
+def make_step(layer, bufs, mode):
+    from token_transformer_layer_amd import abi
+    M = len(layer.shape.slices)
+    groups = [(0, M)] if mode == "whole" else [(j, j + 1) for j in range(M)]
+    sh = layer.shape
+    b = sh.batch
+    bounds = layer.bounds
+    x, dy, hm, y, dh, dx = bufs["x"], bufs["dy"], bufs["h_mid"], bufs["y"], bufs["dh"], bufs["dx"]
+    pa, pm, pu2, pu1 = bufs["p_attn"], bufs["p_mlp"], bufs["p_du2"], bufs["p_du1"]
+    b_o, b2 = layer.p["b_o"], layer.p["b2"]
+
+    def step():
+        layer.kv.filled = 0
+        layer.kvg.done_from = sh.seq
+        for j0, j1 in groups:
+            o0, o1 = bounds[j0], bounds[j1]
+            layer.fwd(abi.TP_FWD_ATTN, j0, j1, x, pa)
+            layer.combine(x[o0:], pa[o0:], b_o, hm[o0:], rows=(o1 - o0) * b)
+            layer.fwd(abi.TP_FWD_MLP, j0, j1, hm, pm)
+            layer.combine(hm[o0:], pm[o0:], b2, y[o0:], rows=(o1 - o0) * b)
+        for j0, j1 in reversed(groups):
+            layer.bwd(abi.TP_BWD_MLP, j0, j1, dy=dy, partial_out=pu2)
+            layer.bwd(abi.TP_BWD_ATTN, j0, j1, dy=dy, ln_in=hm, reduced=pu2, partial_out=pu1, dh=dh)
+            layer.bwd(abi.TP_BWD_LN1, j0, j1, ln_in=x, reduced=pu1, dh=dh, dx=dx)
+    return step
+
+
+def time_steps(torch, step, steps, warmup, trace=False):
+    from token_transformer_layer_amd import abi
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if trace:
+        abi.tp_trace_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    recs = []
+    if trace:
+        recs = abi.tp_trace_read()
+        abi.tp_trace_enable(False)
+    return ev0.elapsed_time(ev1) / steps, wall / steps * 1e3, recs
+
+
+def kernel_table(recs, steps):
+    """Per kernel name: launches per step, ms per step, average ms per launch,
+    algorithmic TFLOP/s and GB/s."""
+    agg = {}
+    for name, fl, by, ms in recs:
+        a = agg.setdefault(name, [0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += fl
+        a[2] += by
+        a[3] += ms
+    out = {}
+    for name, (n, fl, by, ms) in sorted(agg.items(), key=lambda kv: -kv[1][3]):
+        out[name] = dict(launches_per_step=n / steps, ms_per_step=round(ms / steps, 4),
+                         avg_launch_ms=round(ms / n, 5),
+                         tflops=round(fl / (ms * 1e-3) / 1e12, 1) if ms > 0 else None,
+                         gbs=round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else None)
+    return out
+
+
+def cpu_baseline(shape, budget_slices):
+    """The fp64 oracle on the host cores: one rank's fwd+bwd over the first
+    `budget_slices` slices of the sequence (a prefix of the same workload),
+    scaled to TFLOP/s by that sample's own algorithmic flops."""
+    import oracle
+    from tests import gpu_harness as H
+    from token_transformer_layer_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    seq = int(sum(shape.slices[:budget_slices]))
+    sample = shape.replace(seq=seq, slices=tuple(shape.slices[:budget_slices]))
+    x, dy = synth.activations(sample)
+    sp = synth.shard_params_direct(shape, "standard", 0)
+    h_mid, du2, du1 = H.step_inputs(sample, shape.seed + 1)
+    t0 = time.perf_counter()
+    oracle.shard_layer_step(x, h_mid, dy, du2, du1, sp, sample.as_dict(), synth.slice_bounds(sample.slices))
+    dt = time.perf_counter() - t0
+    g, a = step_flops(sample)
+    return dict(value=round((g + a) / dt / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample="%d of %d token slices (positions 0-%d, batch %d) of the same shard, fp64 numpy, %.1f s"
+                       % (budget_slices, len(shape.slices), seq - 1, shape.batch, dt),
+                seconds=round(dt, 2))
+
+
+def cube_block(torch, steps, warmup):
+    """The cube-partition FFN block (X 4096x6144, W1 6144->24576, W2
+    24576->6144, bf16): forward TFLOP/s."""
+    from token_transformer_layer_amd import abi, synth
+    c = synth.CUBE
+    dev = torch.device("cuda")
+    g = torch.Generator(device="cpu").manual_seed(c.seed)
+    x = (torch.randn((c.rows, c.hidden), generator=g)).to(dev, torch.bfloat16)
+    w1 = (torch.randn((c.ffn, c.hidden), generator=g) * 0.02).to(dev, torch.bfloat16)
+    w2 = (torch.randn((c.hidden, c.ffn), generator=g) * 0.02).to(dev, torch.bfloat16)
+    b1 = torch.zeros(c.ffn, dtype=torch.bfloat16, device=dev)
+    hb = torch.empty((c.rows, c.ffn), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((c.rows, c.hidden), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        abi.tp_cube_ffn_block(c.rows, c.hidden, c.ffn, x.data_ptr(), w1.data_ptr(), b1.data_ptr(), w2.data_ptr(),
+                              hb.data_ptr(), out.data_ptr(), st)
+    ms, _, _ = time_steps(torch, step, steps, warmup)
+    fl = 4.0 * c.rows * c.hidden * c.ffn
+    return dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt3-175b-t8")
+    ap.add_argument("--cpu-slices", type=int, default=16, help="slices of the oracle's CPU sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-slice and cube figures")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="warm up and run the timed whole-partition steps only (for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU's shard: this build has no multi-GPU path "
+                         "(the all-reduce between tensor-parallel ranks is left to the caller); "
+                         "run with --gpus 1\n")
+        sys.exit(2)
+
+    import torch
+    from token_transformer_layer_amd import synth
+    from token_transformer_layer_amd.shard import ShardLayer
+
+    shape = synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    x, dy = synth.activations(shape)
+    sp = synth.shard_params_direct(shape, "standard", 0)
+    layer = ShardLayer(shape, sp)
+    bufs = dict(x=layer.act(x), dy=layer.act(dy), h_mid=layer.act(), y=layer.act(), dh=layer.act(),
+                dx=layer.act(), p_attn=layer.f32(), p_mlp=layer.f32(), p_du2=layer.f32(), p_du1=layer.f32())
+    del x, dy, sp
+    layer.new_step()
+    g_fl, a_fl = step_flops(shape)
+    total = g_fl + a_fl
+
+    step = make_step(layer, bufs, "whole")
+    ms, wall_ms, recs = time_steps(torch, step, args.steps, args.warmup, trace=not args.profile_only)
+    if args.profile_only:
+        print(json.dumps(dict(config=shape.name, ms_per_step=ms)))
+        return
+    kt = kernel_table(recs, args.steps)
+    # the dominant kernel: the largest share of the step's time
+    dom_name = next(iter(kt))
+    dom_recs = [r for r in recs if r[0] == dom_name]
+    dom_fl = sum(r[1] for r in dom_recs)
+    dom_ms = sum(r[3] for r in dom_recs)
+    achieved = dom_fl / (dom_ms * 1e-3) / 1e12
+    roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None, kernel=dom_name,
+                    launches=len(dom_recs), avg_launch_ms=round(dom_ms / len(dom_recs), 5))
+    traced_ms = sum(r[3] for r in recs) / args.steps
+    gemm_ms = sum(r[3] for r in recs if r[0].startswith("gemm")) / args.steps
+    gemm_fl = sum(r[1] for r in recs if r[0].startswith("gemm")) / args.steps
+
+    extra = {}
+    if not args.no_extra:
+        ps_ms, _, _ = time_steps(torch, make_step(layer, bufs, "per-slice"), max(3, args.steps // 2), 2)
+        extra["per_slice_calls"] = dict(ms_per_step=round(ps_ms, 4),
+                                        tflops=round(total / (ps_ms * 1e-3) / 1e12, 1))
+        extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
+
+    out = {
+        "metric": "shard-layer fwd+bwd TFLOP/s, GPT-3 175B t=8 shard, one MI355X",
+        "value": round(total / (ms * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "hidden": shape.hidden, "heads": shape.heads,
+                   "head_dim": shape.head_dim, "ffn": shape.ffn, "tp": shape.tp, "batch": shape.batch,
+                   "seq_len": shape.seq, "slices": list(shape.slices), "calls": "one per phase over all slices",
+                   "parallelism": "one tp rank of 8 on 1 GPU"},
+        "frac_of_bf16_peak": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemm": dict(ms_per_step=round(gemm_ms, 4), tflops=round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
+                     frac=round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
+        "traced_kernel_ms_per_step": round(traced_ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roofline,
+        "kernels": kt,
+    }
+    out.update(extra)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(shape, args.cpu_slices)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

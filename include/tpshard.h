@@ -228,6 +228,25 @@ tp_status tp_cube_ffn_block(int32_t rows, int32_t hidden, int32_t ffn, const voi
                             const void *w1, const void *b1, const void *w2, void *hbuf,
                             float *out, void *stream);
 
+/* Per-kernel timing.  tp_trace_enable(1) discards earlier records and makes
+ * every later kernel launch of the library (from any thread) record two HIP
+ * events on its launch stream, with the kernel's name and the algorithmic
+ * work of its operation (flops: 2*M*N*K for a product, the matmul flops the
+ * kernel executes for attention; bytes: each operand read or written once);
+ * tp_trace_enable(0) stops recording.  tp_trace_read() waits for the
+ * recorded events, writes the first `max` records to `out` (which may be
+ * NULL), releases all records and returns how many there were.  ms is the
+ * event-measured duration (-1 if the events could not be read). */
+typedef struct {
+    char name[64];
+    double flops;
+    double bytes;
+    float ms;
+} tp_trace_record;
+
+void tp_trace_enable(int32_t on);
+int32_t tp_trace_read(tp_trace_record *out, int32_t max);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *tp_last_error(void);
 

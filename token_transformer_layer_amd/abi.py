@@ -19,7 +19,8 @@ TP_FWD_ATTN, TP_FWD_MLP = 0, 1
 TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1 = 0, 1, 2
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
-            "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_last_error"]
+            "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_trace_enable",
+            "tp_trace_read", "tp_last_error"]
 
 
 class TPError(RuntimeError):
@@ -52,6 +53,11 @@ class tp_partition(ctypes.Structure):
 
 class tp_kv_cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("filled", ctypes.c_int32)]
+
+
+class tp_trace_record(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("flops", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("ms", ctypes.c_float)]
 
 
 class tp_kv_grad(ctypes.Structure):
@@ -87,6 +93,10 @@ def lib():
     L.tp_residual_combine.restype = ctypes.c_int
     L.tp_cube_ffn_block.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.tp_cube_ffn_block.restype = ctypes.c_int
+    L.tp_trace_enable.argtypes = [i32]
+    L.tp_trace_enable.restype = None
+    L.tp_trace_read.argtypes = [P(tp_trace_record), i32]
+    L.tp_trace_read.restype = i32
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -135,3 +145,15 @@ def tp_residual_combine(cfg, rows, resid, reduced, bias, out, stream):
 
 def tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream):
     _check(lib().tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream))
+
+
+def tp_trace_enable(on):
+    lib().tp_trace_enable(1 if on else 0)
+
+
+def tp_trace_read(max_records=100000):
+    """[(name, flops, bytes, ms), ...] of the launches recorded since tracing
+    was enabled (waits for them to finish)."""
+    buf = (tp_trace_record * max_records)()
+    n = lib().tp_trace_read(buf, max_records)
+    return [(buf[i].name.decode(), buf[i].flops, buf[i].bytes, buf[i].ms) for i in range(min(n, max_records))]

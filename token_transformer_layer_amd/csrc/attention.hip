@@ -27,6 +27,7 @@
 // configuration only).
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace tpk {
 
@@ -669,10 +670,22 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32(AttnF a) {
 
 }  // namespace
 
+// (query, key) pairs of the causal product for queries [q0, q1) of every
+// (batch row, head): query p sees p + 1 keys.
+static double causal_pairs(const AttnArgs &x) {
+    double q0 = x.q0, q1 = x.q1;
+    return (q1 * (q1 + 1) - q0 * (q0 + 1)) / 2 * x.batch * x.nt;
+}
+
 hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
     const int nq = x.q1 - x.q0;
     if (nq <= 0) return hipSuccess;
     const int bh = x.batch * x.nt;
+    const int es = dt == DType::BF16 ? 2 : 4;
+    // algorithmic: 4d flops per pair (Q K^T and P V); Q and O once, the K/V
+    // prefix once per (batch row, head)
+    TraceScope ts(st, dt == DType::BF16 ? "attn_fwd_bf16" : "attn_fwd_f32", 4.0 * x.d * causal_pairs(x),
+                  (double)bh * x.d * es * (2.0 * nq + 2.0 * x.q1) + 4.0 * bh * nq);
     if (dt == DType::BF16) {
         AttnP p{};
         p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
@@ -698,9 +711,17 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
     const int bh = x.batch * x.nt;
     const int64_t nd = (int64_t)nq * x.batch * x.nt;
     const unsigned dgrid = (unsigned)((nd + 255) / 256);
+    const int es = dt == DType::BF16 ? 2 : 4;
+    const double pairs = causal_pairs(x);
+    // dK/dV kernel: S, dP, dV, dK (8d flops per pair); dQ kernel: S, dP, dQ (6d)
+    const double kv_bytes = (double)bh * x.d * (4.0 * x.q1 * es + 2.0 * nq * es * 2);
+    const double q_bytes = (double)bh * x.d * (4.0 * nq * es + 2.0 * x.q1 * es);
     if (dt == DType::BF16) {
-        hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(dgrid), dim3(256), 0, st, x.batch, x.nt, x.seq, x.d, x.q0,
-                           x.q1, (const bf16 *)x.o, (const bf16 *)x.dout, x.delta);
+        {
+            TraceScope ts(st, "attn_delta_bf16", 2.0 * x.d * nd, 2.0 * nd * x.d * es + 4.0 * nd);
+            hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(dgrid), dim3(256), 0, st, x.batch, x.nt, x.seq, x.d,
+                               x.q0, x.q1, (const bf16 *)x.o, (const bf16 *)x.dout, x.delta);
+        }
         AttnP p{};
         p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
         p.k_final0 = x.k_final0; p.acc_in = x.acc_in ? 1 : 0;
@@ -709,14 +730,18 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
         p.dk_acc = x.dk_acc; p.dv_acc = x.dv_acc;
         p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
         dim3 gk((x.q1 + 63) / 64, bh), gq((nq + 63) / 64, bh);
-        if (x.d == 128) {
-            hipLaunchKernelGGL(attn_bwd_dkdv_bf16<128>, gk, dim3(256), 0, st, p);
-            hipLaunchKernelGGL(attn_bwd_dq_bf16<128>, gq, dim3(256), 0, st, p);
-        } else {
-            hipLaunchKernelGGL(attn_bwd_dkdv_bf16<64>, gk, dim3(256), 0, st, p);
-            hipLaunchKernelGGL(attn_bwd_dq_bf16<64>, gq, dim3(256), 0, st, p);
+        {
+            TraceScope ts(st, "attn_bwd_dkdv_bf16", 8.0 * x.d * pairs, kv_bytes);
+            if (x.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_bf16<128>, gk, dim3(256), 0, st, p);
+            else hipLaunchKernelGGL(attn_bwd_dkdv_bf16<64>, gk, dim3(256), 0, st, p);
+        }
+        {
+            TraceScope ts(st, "attn_bwd_dq_bf16", 6.0 * x.d * pairs, q_bytes);
+            if (x.d == 128) hipLaunchKernelGGL(attn_bwd_dq_bf16<128>, gq, dim3(256), 0, st, p);
+            else hipLaunchKernelGGL(attn_bwd_dq_bf16<64>, gq, dim3(256), 0, st, p);
         }
     } else {
+        TraceScope ts(st, "attn_bwd_f32", 14.0 * x.d * pairs, kv_bytes + q_bytes);
         hipLaunchKernelGGL(attn_delta_kernel<float>, dim3(dgrid), dim3(256), 0, st, x.batch, x.nt, x.seq, x.d, x.q0,
                            x.q1, (const float *)x.o, (const float *)x.dout, x.delta);
         AttnF p{};

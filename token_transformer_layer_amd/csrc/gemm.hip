@@ -20,8 +20,12 @@
 // is M/N-contiguous in memory is transposed in registers on its way to LDS.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles, 4 x 4 per thread).
+#include <cmath>
+#include <cstdio>
+
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace tpk {
 
@@ -177,18 +181,45 @@ struct TileLoader {
     }
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, bool AK, bool BK_, class Epi>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g, Epi epi) {
-    constexpr int NT = WAVES_M * WAVES_N * 64;
-    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+// Maps the linear workgroup index to a (tile row, tile column) pair.
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2), so consecutive indices are first regrouped so that every XCD gets a
+// contiguous range of tiles; that range is then walked in groups of GM tile
+// rows, column by column, so the tiles resident on one XCD share A rows and
+// B columns.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int gm_rows, int &tm, int &tn) {
+    const int L = tiles_m * tiles_n, L8 = L & ~7;
+    int t = bid;
+    if (bid < L8) t = (bid & 7) * (L8 >> 3) + (bid >> 3);
+    const int per_group = gm_rows * tiles_n;
+    const int group = t / per_group, first = group * gm_rows;
+    const int rows = min(tiles_m - first, gm_rows);
+    const int r = t - group * per_group;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+struct TileCfg {
+    static constexpr int kBM = BM, kBN = BN, kBK = 64, kWM = WAVES_M, kWN = WAVES_N;
+    static constexpr int kThreads = WAVES_M * WAVES_N * 64;
+    static constexpr int kLds = 2 * (BM + BN) * 64 * 2;  // two stages of A and B tiles
+};
+
+template <class C, bool AK, bool BK_, class Epi>
+__global__ __launch_bounds__(C::kThreads) void gemm_bf16_kernel(GemmArgs g, Epi epi, int gm_rows) {
+    constexpr int BM = C::kBM, BN = C::kBN, BK = C::kBK, NT = C::kThreads;
+    constexpr int WTM = BM / C::kWM, WTN = BN / C::kWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    static_assert(BK == 64, "LDS swizzle assumes 8 chunks per row");
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-    __shared__ __attribute__((aligned(16))) char smem[2 * (A_BYTES + B_BYTES)];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid / WAVES_N, wn = wid % WAVES_N;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int wm = wid / C::kWN, wn = wid % C::kWN;
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, gm_rows, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
 
     __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
     __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
@@ -201,6 +232,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_bf16_kernel(GemmAr
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
+    // per-lane LDS byte offsets of the fragment rows (the chunk is added per k-step)
+    int a_row[FM], b_row[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) a_row[i] = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_row[j] = wn * WTN + j * 32 + (lane & 31);
+
     const int nkt = (g.K + BK - 1) / BK;
     la.load(ra, m0, 0, g.M, g.K, g.lda, tid);
     lb.load(rb, n0, 0, g.N, g.K, g.ldb, tid);
@@ -209,7 +247,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_bf16_kernel(GemmAr
     __syncthreads();
 
     for (int kt = 0; kt < nkt; ++kt) {
-        char *cur = smem + (kt & 1) * (A_BYTES + B_BYTES);
+        const char *cur = smem + (kt & 1) * (A_BYTES + B_BYTES);
         const bool more = kt + 1 < nkt;
         if (more) {
             la.load(ra, m0, (kt + 1) * BK, g.M, g.K, g.lda, tid);
@@ -220,15 +258,11 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_bf16_kernel(GemmAr
             bf16x8 fa[FM], fb[FN];
             const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                int row = wm * WTM + i * 32 + (lane & 31);
-                fa[i] = *(const bf16x8 *)(cur + row * (BK * 2) + ((ch ^ lds_swz(row)) << 4));
-            }
+            for (int i = 0; i < FM; ++i)
+                fa[i] = *(const bf16x8 *)(cur + a_row[i] * (BK * 2) + ((ch ^ lds_swz(a_row[i])) << 4));
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                int row = wn * WTN + j * 32 + (lane & 31);
-                fb[j] = *(const bf16x8 *)(cur + A_BYTES + row * (BK * 2) + ((ch ^ lds_swz(row)) << 4));
-            }
+            for (int j = 0; j < FN; ++j)
+                fb[j] = *(const bf16x8 *)(cur + A_BYTES + b_row[j] * (BK * 2) + ((ch ^ lds_swz(b_row[j])) << 4));
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -317,17 +351,53 @@ static uint32_t extent_bytes(int rows, int k, const Mat &m, int es) {
     return (uint32_t)(last * es);
 }
 
+// Tile configurations of the bf16 kernel.  Wide wave tiles cut the LDS
+// traffic per MFMA (128x128 per wave reads 1 KB of fragments per 32x32 block
+// pair); smaller tiles give more workgroups where M or N is small.
+using Cfg256x256 = TileCfg<256, 256, 2, 2>;
+using Cfg256x128 = TileCfg<256, 128, 2, 2>;
+using Cfg128x128 = TileCfg<128, 128, 2, 2>;
+
+enum class TileChoice { T256x256, T256x128, T128x128 };
+
+// Picks the tile for an M x N x K product.  Measured on MI355X: the
+// 128x128 tile (up to three workgroups per compute unit hide each other's
+// memory latency) is fastest for every product of the GPT-3 175B shard; the
+// 256x256 tile only wins on large products whose operands are both
+// K-contiguous (e.g. 8192^3, 4096x24576x6144).
+static TileChoice choose_tile(int M, int N, int K, bool ak, bool bk) {
+    const double tiles128 = (double)((M + 127) / 128) * ((N + 127) / 128);
+    if (ak && bk && tiles128 >= 4096 && K >= 1024) return TileChoice::T256x256;
+    return TileChoice::T128x128;
+}
+
+template <class C, bool AK, bool BK_, class E>
+static hipError_t launch_cfg(const GemmArgs &g, const E &epi, hipStream_t st) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_kernel<C, AK, BK_, E>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, AK, BK_, E>), dim3(tiles), dim3(C::kThreads), C::kLds, st, g, epi, 4);
+    return hipGetLastError();
+}
+
 template <typename T, bool AK, bool BK_, class E>
 static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        constexpr int BM = 128, BN = 128, BK = 64;
-        dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, 2, 2, AK, BK_, E>), grid, dim3(256), 0, st, g, epi);
+        switch (choose_tile(g.M, g.N, g.K, AK, BK_)) {
+        case TileChoice::T256x256: return launch_cfg<Cfg256x256, AK, BK_>(g, epi, st);
+        case TileChoice::T256x128: return launch_cfg<Cfg256x128, AK, BK_>(g, epi, st);
+        default: return launch_cfg<Cfg128x128, AK, BK_>(g, epi, st);
+        }
     } else {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
         hipLaunchKernelGGL((gemm_f32_kernel<AK, BK_, E>), grid, dim3(256), 0, st, g, epi);
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 template <typename T, bool AK, bool BK_>
@@ -384,6 +454,19 @@ hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const Epi
     }
     g.a_bytes = K > 0 ? extent_bytes(M, K, A, es) : 0;
     g.b_bytes = K > 0 ? extent_bytes(N, K, B, es) : 0;
+    // algorithmic work: 2MNK flops; A and B read once, C written once (read
+    // too when accumulated), plus the epilogue's extra operand or output
+    static const char *kEpiName[] = {"store_f32", "accum_f32", "store", "bias_gelu", "gelu_grad", "qkv"};
+    const char *lay = A.kcontig ? (B.kcontig ? "nt" : "nn") : "tn";
+    char name[64];
+    snprintf(name, sizeof name, "gemm_%s_%s_%s", dt == DType::BF16 ? "bf16" : "f32", lay, kEpiName[(int)kind]);
+    const double mn = (double)M * N;
+    double out_b = mn * es;
+    if (kind == Epi::StoreF32) out_b = mn * 4;
+    if (kind == Epi::AccumF32) out_b = mn * 8;
+    if (kind == Epi::BiasGelu && e.c) out_b = 2 * mn * es;
+    if (kind == Epi::GeluGrad) out_b = 2 * mn * es;
+    TraceScope ts(st, name, 2.0 * mn * K, ((double)M * K + (double)N * K) * es + out_b);
     if (dt == DType::BF16) return dispatch_layout<bf16>(g, A.kcontig, B.kcontig, kind, e, st);
     return dispatch_layout<float>(g, A.kcontig, B.kcontig, kind, e, st);
 }

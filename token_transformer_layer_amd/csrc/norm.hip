@@ -13,6 +13,7 @@
 // so repeated runs give identical bits.
 #include "common.h"
 #include "kernels.h"
+#include "trace.h"
 
 namespace tpk {
 
@@ -161,15 +162,26 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(int rows, int h, int r
 }
 
 // out[c] += sum over blocks of partials[blk][c], for c < n; partial rows are
-// `stride` floats apart.
+// `stride` floats apart.  A workgroup owns 32 columns; its 8 row groups each
+// sum every 8th partial row, and the 8 sums are added in a fixed order.
+constexpr int kRedCols = 32, kRedGroups = kThreads / kRedCols;
 __global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n, int64_t stride,
                                                                  const float *__restrict__ partials,
                                                                  float *__restrict__ out) {
-    int c = blockIdx.x * kThreads + threadIdx.x;
-    if (c >= n) return;
+    __shared__ float part[kRedGroups][kRedCols];
+    const int cx = threadIdx.x % kRedCols, gy = threadIdx.x / kRedCols;
+    const int c = blockIdx.x * kRedCols + cx;
     float s = 0.f;
-    for (int k = 0; k < nblk; ++k) s += partials[(size_t)k * stride + c];
-    out[c] += s;
+    if (c < n)
+        for (int k = gy; k < nblk; k += kRedGroups) s += partials[(size_t)k * stride + c];
+    part[gy][cx] = s;
+    __syncthreads();
+    if (gy == 0 && c < n) {
+        float t = 0.f;
+#pragma unroll
+        for (int k = 0; k < kRedGroups; ++k) t += part[k][cx];
+        out[c] += t;
+    }
 }
 
 // Per-chunk column sums: partials[chunk][c] = sum of a[r][c] over the rows of
@@ -221,6 +233,9 @@ size_t colsum_partials_floats(int rows, int n) { return (size_t)colsum_chunks(ro
 hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, const void *g, const void *b,
                          void *u, float *mean, float *rstd, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
+    const int es = dt == DType::BF16 ? 2 : 4;
+    TraceScope ts(st, dt == DType::BF16 ? "ln_fwd_bf16" : "ln_fwd_f32", 0.0,
+                  (double)rows * h * 2 * es + 8.0 * rows + 2.0 * h * es);
     if (dt == DType::BF16)
         hipLaunchKernelGGL(ln_fwd_kernel<bf16>, dim3(rows), dim3(kThreads), 0, st, h, eps, (const bf16 *)x,
                            (const bf16 *)g, (const bf16 *)b, (bf16 *)u, mean, rstd);
@@ -236,6 +251,10 @@ hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void 
     if (rows <= 0) return hipSuccess;
     const int nblk = ln_bwd_blocks(rows), rpb = (rows + nblk - 1) / nblk;
     const size_t lds = (size_t)2 * h * sizeof(float);
+    const int es = dt == DType::BF16 ? 2 : 4;
+    {
+    TraceScope ts(st, dt == DType::BF16 ? "ln_bwd_bf16" : "ln_bwd_f32", 0.0,
+                  (double)rows * h * (4 + 3 * es) + 8.0 * rows + (double)nblk * 2 * h * 4);
     if (dt == DType::BF16) {
         hipFuncSetAttribute((const void *)ln_bwd_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nblk), dim3(kThreads), lds, st, rows, h, rpb, du,
@@ -246,13 +265,20 @@ hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void 
                            (const float *)resid, (const float *)x, (const float *)g, mean, rstd, (float *)dx,
                            partials);
     }
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int gb = (h + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
-                       (const float *)partials, dg);
-    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
-                       (const float *)(partials + h), db);
+    const int gb = (h + kRedCols - 1) / kRedCols;
+    {
+        TraceScope ts(st, "block_reduce", 0.0, (double)nblk * h * 4 + 8.0 * h);
+        hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
+                           (const float *)partials, dg);
+    }
+    {
+        TraceScope ts(st, "block_reduce", 0.0, (double)nblk * h * 4 + 8.0 * h);
+        hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
+                           (const float *)(partials + h), db);
+    }
     return hipGetLastError();
 }
 
@@ -261,15 +287,21 @@ hipError_t colsum_accum(DType dt, int rows, int n, const void *a, int64_t lda, f
     if (rows <= 0 || n <= 0) return hipSuccess;
     const int nch = colsum_chunks(rows), rpc = (rows + nch - 1) / nch;
     dim3 grid((n / 8 + kThreads - 1) / kThreads, nch);
+    const int es = dt == DType::BF16 ? 2 : 4;
+    {
+    TraceScope ts(st, dt == DType::BF16 ? "colsum_bf16" : "colsum_f32", (double)rows * n,
+                  (double)rows * n * es + (double)nch * n * 4);
     if (dt == DType::BF16)
         hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(kThreads), 0, st, rows, n, lda, rpc, (const bf16 *)a,
                            partials);
     else
         hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(kThreads), 0, st, rows, n, lda, rpc, (const float *)a,
                            partials);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, st, nch, n,
+    TraceScope ts(st, "block_reduce", 0.0, (double)nch * n * 4 + 8.0 * n);
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kRedCols - 1) / kRedCols), dim3(kThreads), 0, st, nch, n,
                        (int64_t)n, (const float *)partials, out);
     return hipGetLastError();
 }
@@ -280,6 +312,9 @@ hipError_t residual_combine(DType dt, int64_t rows, int h, const void *resid, co
     if (n8 <= 0) return hipSuccess;
     int64_t blocks = (n8 + kThreads - 1) / kThreads;
     if (blocks > 4096) blocks = 4096;
+    const int es = dt == DType::BF16 ? 2 : 4;
+    TraceScope ts(st, dt == DType::BF16 ? "combine_bf16" : "combine_f32", 2.0 * rows * h,
+                  (double)rows * h * (2 * es + 4) + (double)h * es);
     if (dt == DType::BF16)
         hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)blocks), dim3(kThreads), 0, st, n8, h,
                            (const bf16 *)resid, reduced, (const bf16 *)bias, (bf16 *)out);
