@@ -15,8 +15,10 @@ would receive them.
 
 Inputs are synthetic and seeded (token_transformer_layer_amd.synth): x, dY
 ~ N(0, 1), linear weights ~ N(0, 0.02), biases 0, gamma 1, beta 0, all bf16.
-Gradient buffers are zeroed once before the timed steps (the optimizer's
-job, outside the layer), so the timed steps accumulate into them.
+Each gradient is overwritten by the call that first produces it in a step
+(accumulate = 0), so no zeroing pass is needed.  In the per-slice schedule
+the backward runs the data phases per slice (reverse order) and every weight
+gradient in one call over all slices afterwards.
 
 Prints ONE JSON line.  value = algorithmic fwd+bwd TFLOP/s of the step:
 GEMMs 3 x 2 T h (4 h_t + 2 f_t) plus causal attention 3 x 2 b h_t s (s+1)
@@ -67,10 +69,24 @@ def make_step(layer, bufs, mode):
             layer.combine(x[o0:], pa[o0:], b_o, hm[o0:], rows=(o1 - o0) * b)
             layer.fwd(abi.TP_FWD_MLP, j0, j1, hm, pm)
             layer.combine(hm[o0:], pm[o0:], b2, y[o0:], rows=(o1 - o0) * b)
+        if mode == "whole":
+            # one call per phase: every gradient is produced once, so the
+            # calls overwrite the gradient buffers (no zeroing needed)
+            layer.bwd(abi.TP_BWD_MLP, 0, M, dy=dy, partial_out=pu2, accumulate=False)
+            layer.bwd(abi.TP_BWD_ATTN, 0, M, dy=dy, ln_in=hm, reduced=pu2, partial_out=pu1, dh=dh,
+                      accumulate=False)
+            layer.bwd(abi.TP_BWD_LN1, 0, M, ln_in=x, reduced=pu1, dh=dh, dx=dx, accumulate=False)
+            return
+        # per slice, in reverse: the data phases only; then every weight
+        # gradient in one call over all slices
+        first = True
         for j0, j1 in reversed(groups):
-            layer.bwd(abi.TP_BWD_MLP, j0, j1, dy=dy, partial_out=pu2)
-            layer.bwd(abi.TP_BWD_ATTN, j0, j1, dy=dy, ln_in=hm, reduced=pu2, partial_out=pu1, dh=dh)
-            layer.bwd(abi.TP_BWD_LN1, j0, j1, ln_in=x, reduced=pu1, dh=dh, dx=dx)
+            layer.bwd(abi.TP_BWD_MLP_DATA, j0, j1, dy=dy, partial_out=pu2, accumulate=not first)
+            layer.bwd(abi.TP_BWD_ATTN_DATA, j0, j1, dy=dy, ln_in=hm, reduced=pu2, partial_out=pu1, dh=dh,
+                      accumulate=not first)
+            layer.bwd(abi.TP_BWD_LN1, j0, j1, ln_in=x, reduced=pu1, dh=dh, dx=dx, accumulate=not first)
+            first = False
+        layer.bwd(abi.TP_BWD_WGRAD, 0, M, dy=dy, dh=dh, accumulate=False)
     return step
 
 

@@ -117,9 +117,13 @@ typedef struct {
     const void *w2;
 } tp_shard_weights;
 
-/* fp32 device gradient buffers, accumulated (+=); the caller zeroes them
- * before the first backward call of a step.  b_o and b2 are the replicated
- * row-split biases: every rank computes the same value. */
+/* fp32 device gradient buffers.  accumulate = 1: every gradient a call
+ * produces is added into its buffer (+=); accumulate = 0: the call
+ * overwrites each gradient buffer it produces (=), as BLAS does with
+ * beta = 0.  A step that runs one call per phase over all slices can use 0
+ * and skip zeroing; a step over several calls passes 0 on the first call
+ * that produces a given gradient and 1 afterwards.  b_o and b2 are the
+ * replicated row-split biases: every rank computes the same value. */
 typedef struct {
     float *ln1_g, *ln1_b;
     float *w_qkv, *b_qkv;
@@ -127,6 +131,7 @@ typedef struct {
     float *ln2_g, *ln2_b;
     float *w1, *b1;
     float *w2, *b2;
+    int32_t accumulate;
 } tp_shard_grads;
 
 /* Token-slice partition l_1..l_M of the sequence (host memory): every
@@ -158,15 +163,34 @@ typedef struct {
 } tp_kv_grad;
 
 typedef enum { TP_FWD_ATTN = 0, TP_FWD_MLP = 1 } tp_fwd_phase;
-typedef enum { TP_BWD_MLP = 0, TP_BWD_ATTN = 1, TP_BWD_LN1 = 2 } tp_bwd_phase;
+/* Backward phases.  TP_BWD_MLP = TP_BWD_MLP_DATA + the MLP weight and bias
+ * gradients of the call's rows; TP_BWD_ATTN = TP_BWD_ATTN_DATA + the
+ * attention block's weight and bias gradients.  The _DATA phases produce
+ * only what the next phase needs (the partial sums, dH, dK/dV and the
+ * LayerNorm parameter gradients), so a pipeline stage can run them per slice
+ * and take every weight gradient afterwards in one TP_BWD_WGRAD call over all
+ * slices (dW2, db1, db2, dW1, dW_o, db_o, dW_qkv, db_qkv), which reads dY, dH,
+ * the saved activations and the per-row intermediates the _DATA calls left in
+ * scratch. */
+typedef enum {
+    TP_BWD_MLP = 0,
+    TP_BWD_ATTN = 1,
+    TP_BWD_LN1 = 2,
+    TP_BWD_MLP_DATA = 3,
+    TP_BWD_ATTN_DATA = 4,
+    TP_BWD_WGRAD = 5
+} tp_bwd_phase;
 
 /* Bytes of the opaque "saved" buffer: activations the forward keeps for the
  * backward, for the whole sequence (u1, LN statistics, Q, O, log-sum-exp,
  * u2, Z, GELU(Z)).  0 if cfg is invalid. */
 size_t tp_shard_saved_bytes(const tp_shard_cfg *cfg);
 
-/* Bytes of the per-call "scratch" buffer (any call, any slice range); its
- * contents do not survive a call.  0 if cfg is invalid. */
+/* Bytes of the "scratch" buffer (any call, any slice range).  The backward
+ * keeps its per-row intermediates there (dZ, dO, dQKV at the call's rows) for
+ * a later TP_BWD_WGRAD call over the same rows, so a step's backward calls
+ * must share one scratch buffer; nothing else in it survives a call.  0 if
+ * cfg is invalid. */
 size_t tp_shard_scratch_bytes(const tp_shard_cfg *cfg);
 
 /* Forward of one phase over slices [slice_begin, slice_end) of part.
@@ -185,8 +209,9 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
                              tp_kv_cache *kv, void *saved, void *scratch, void *stream);
 
 /* Backward of one phase over slices [slice_begin, slice_end).  Phases of one
- * slice range run in the order MLP, ATTN, LN1; slice ranges run in reverse.
- *   dy           TP_BWD_MLP, TP_BWD_ATTN: gradient of the layer output y
+ * slice range run in the order MLP, ATTN, LN1 (or their _DATA forms); slice
+ * ranges run in reverse; TP_BWD_WGRAD runs after the _DATA calls of its rows.
+ *   dy           MLP, ATTN and WGRAD phases: gradient of the layer output y
  *                [s, b, h]; TP_BWD_LN1: unused.
  *   ln_in        TP_BWD_ATTN: h_mid (the input of LN2); TP_BWD_LN1: x (the
  *                input of LN1); TP_BWD_MLP: unused.
@@ -194,9 +219,10 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
  *                sum_r dU1,r; TP_BWD_MLP: unused.
  *   partial_out  fp32 [s, b, h], overwritten at the call's rows:
  *                TP_BWD_MLP: dU2,r; TP_BWD_ATTN: dU1,r; TP_BWD_LN1: unused.
- *   dh           [s, b, h]: written by TP_BWD_ATTN, read by TP_BWD_LN1.
+ *   dh           [s, b, h]: written by TP_BWD_ATTN(_DATA), read by TP_BWD_LN1
+ *                and TP_BWD_WGRAD.
  *   dx           [s, b, h]: written by TP_BWD_LN1.
- *   g            gradients, accumulated (+=).
+ *   g            gradients (accumulated or overwritten, see tp_shard_grads).
  *   kv, kvg      TP_BWD_ATTN only: the cache the forward filled and the
  *                dK/dV accumulators (protocol above).
  *   saved        the buffer the forward filled for these rows. */

@@ -46,10 +46,14 @@ def groups_of(mode, nslices):
     raise ValueError(mode)
 
 
-def run_shard_step(layer, x, h_mid, dy, du2, du1, groups):
+def run_shard_step(layer, x, h_mid, dy, du2, du1, groups, split_wgrad=False):
     """Forward (groups in order: ATTN then MLP per group) and backward
-    (groups in reverse: MLP, ATTN, LN1) of one rank, with the caller's
-    reduced tensors given.  Returns host float64 arrays."""
+    (groups in reverse) of one rank, with the caller's reduced tensors given.
+    split_wgrad=False: MLP, ATTN, LN1 per group, gradients accumulated into
+    zeroed buffers.  split_wgrad=True: MLP_DATA, ATTN_DATA, LN1 per group,
+    then one WGRAD call over all slices; every gradient is overwritten by its
+    first producer (the buffers start as NaN, so a missed overwrite shows).
+    Returns host float64 arrays."""
     import torch
 
     xt, hm, dyt = layer.act(x), layer.act(h_mid), layer.act(dy)
@@ -57,14 +61,23 @@ def run_shard_step(layer, x, h_mid, dy, du2, du1, groups):
     du1t = torch.from_numpy(du1).to(layer.device)
     p_attn, p_mlp, p_du2, p_du1 = layer.f32(), layer.f32(), layer.f32(), layer.f32()
     dh, dx = layer.act(), layer.act()
-    layer.new_step()
+    layer.new_step(float("nan") if split_wgrad else 0.0)
     for j0, j1 in groups:
         layer.fwd(0, j0, j1, xt, p_attn)
         layer.fwd(1, j0, j1, hm, p_mlp)
+    first = True
     for j0, j1 in reversed(groups):
-        layer.bwd(0, j0, j1, dy=dyt, partial_out=p_du2)
-        layer.bwd(1, j0, j1, dy=dyt, ln_in=hm, reduced=du2t, partial_out=p_du1, dh=dh)
-        layer.bwd(2, j0, j1, ln_in=xt, reduced=du1t, dh=dh, dx=dx)
+        if split_wgrad:
+            layer.bwd(3, j0, j1, dy=dyt, partial_out=p_du2, accumulate=not first)
+            layer.bwd(4, j0, j1, dy=dyt, ln_in=hm, reduced=du2t, partial_out=p_du1, dh=dh, accumulate=not first)
+            layer.bwd(2, j0, j1, ln_in=xt, reduced=du1t, dh=dh, dx=dx, accumulate=not first)
+        else:
+            layer.bwd(0, j0, j1, dy=dyt, partial_out=p_du2)
+            layer.bwd(1, j0, j1, dy=dyt, ln_in=hm, reduced=du2t, partial_out=p_du1, dh=dh)
+            layer.bwd(2, j0, j1, ln_in=xt, reduced=du1t, dh=dh, dx=dx)
+        first = False
+    if split_wgrad:
+        layer.bwd(5, groups[0][0], groups[-1][1], dy=dyt, dh=dh, accumulate=False)
     torch.cuda.synchronize()
 
     def h(t):

@@ -125,7 +125,7 @@ def test_forward_slice_order_is_enforced():
 def test_backward_slice_order_is_enforced():
     c = cfg_of(synth.CONFIGS["tiny-fp32"])
     part = abi.make_partition([32, 32, 32, 32])
-    g = abi.tp_shard_grads(*[FAKE] * len(abi.GRAD_FIELDS))
+    g = abi.tp_shard_grads(*[FAKE] * len(abi.GRAD_FIELDS), 1)
     kv = abi.tp_kv_cache(FAKE, FAKE, 128)
     kvg = abi.tp_kv_grad(FAKE, FAKE, 128)
 
@@ -139,6 +139,19 @@ def test_backward_slice_order_is_enforced():
     kv.filled = 32
     kvg.done_from = 128
     assert _status(lambda: bwd(3, 4)) == abi.TP_EORDER  # forward has not reached slice 3
+    kv.filled = 128
+    g.accumulate = 2
+    assert _status(lambda: bwd(3, 4)) == abi.TP_EINVAL  # accumulate must be 0 or 1
+    g.accumulate = 1
+
+    def bwd_phase(phase):
+        abi.tp_shard_layer_bwd(c, _weights(), part, 3, 4, phase, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               g, kv, kvg, FAKE, FAKE, None)
+
+    assert _status(lambda: bwd_phase(6)) == abi.TP_EINVAL
+    assert _status(lambda: bwd_phase(-1)) == abi.TP_EINVAL
+    kvg.done_from = 32
+    assert _status(lambda: bwd_phase(abi.TP_BWD_ATTN_DATA)) == abi.TP_EORDER
 
 
 def test_combine_and_cube_checks():

@@ -36,16 +36,17 @@ def _oracle_step(shape, sp, x, h_mid, dy, du2, du1):
     return oracle.shard_layer_step(x, h_mid, dy, du2, du1, sp, shape.as_dict(), [0, shape.seq])
 
 
-def _check_shard(shape, variant, mode, rank=0, full=True):
+def _check_shard(shape, variant, mode, rank=0, full=True, split_wgrad=False):
     x, dy = synth.activations(shape)
     if full:
         sp = oracle.shard_params(synth.full_params(shape, variant), rank, shape.as_dict())
     else:
         sp = synth.shard_params_direct(shape, variant, rank)
     h_mid, du2, du1 = H.step_inputs(shape, shape.seed + 1)
-    print("[case] %s variant=%s mode=%s rank=%d" % (shape.name, variant, mode, rank), flush=True)
+    print("[case] %s variant=%s mode=%s rank=%d split_wgrad=%s" % (shape.name, variant, mode, rank, split_wgrad),
+          flush=True)
     layer = _layer(shape, sp)
-    got = H.run_shard_step(layer, x, h_mid, dy, du2, du1, H.groups_of(mode, len(shape.slices)))
+    got = H.run_shard_step(layer, x, h_mid, dy, du2, du1, H.groups_of(mode, len(shape.slices)), split_wgrad)
     ref = _oracle_step(shape, sp, x, h_mid, dy, du2, du1)
     bad = H.compare_step(got, ref, TOL[shape.dtype])
     assert not bad, bad
@@ -65,6 +66,18 @@ def test_tiny_fp32_ragged_sharp():
 @pytest.mark.parametrize("shape", [RAGGED_D64, RAGGED_D128], ids=lambda s: s.name)
 def test_bf16_shard_ragged(shape, mode):
     _check_shard(shape, "perturbed", mode, rank=1)
+
+
+@pytest.mark.parametrize("shape", [TINY_RAGGED_F32, RAGGED_D64, RAGGED_D128], ids=lambda s: s.name)
+def test_split_weight_gradients(shape):
+    """Per-slice data phases, then one weight-gradient call over all slices,
+    every gradient overwritten by its first producer."""
+    _check_shard(shape, "perturbed", "per-slice", rank=1, split_wgrad=True)
+
+
+def test_full_size_split_weight_gradients():
+    """The benchmark's per-slice schedule at the GPT-3 175B shard."""
+    _check_shard(synth.CONFIGS["gpt3-175b-t8"], "standard", "per-slice", rank=0, full=False, split_wgrad=True)
 
 
 def test_bf16_peaked_softmax():

@@ -16,7 +16,7 @@ STATUS_NAMES = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_ESHAPE", 3: "TP_EALIGN", 4: "
                 5: "TP_EUNSUPPORTED", 6: "TP_EHIP"}
 TP_F32, TP_BF16 = 0, 1
 TP_FWD_ATTN, TP_FWD_MLP = 0, 1
-TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1 = 0, 1, 2
+TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1, TP_BWD_MLP_DATA, TP_BWD_ATTN_DATA, TP_BWD_WGRAD = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_trace_enable",
@@ -44,7 +44,7 @@ class tp_shard_weights(ctypes.Structure):
 
 
 class tp_shard_grads(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS] + [("accumulate", ctypes.c_int32)]
 
 
 class tp_partition(ctypes.Structure):

@@ -271,75 +271,41 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     if (s != TP_OK) return s;
     if (!w) return fail(TP_EINVAL, "weights is NULL");
     if (!g) return fail(TP_EINVAL, "grads is NULL");
+    if (g->accumulate != 0 && g->accumulate != 1) return fail(TP_EINVAL, "grads.accumulate must be 0 or 1");
     int64_t o0, o1;
     if ((s = check_range(d, part, slice_begin, slice_end, &o0, &o1)) != TP_OK) return s;
-    if (phase != TP_BWD_MLP && phase != TP_BWD_ATTN && phase != TP_BWD_LN1)
-        return fail(TP_EINVAL, "backward phase %d is not valid", phase);
+    if (phase < TP_BWD_MLP || phase > TP_BWD_WGRAD) return fail(TP_EINVAL, "backward phase %d is not valid", phase);
     NEED(saved, "saved");
     NEED(scratch, "scratch");
-    const Saved L = saved_layout(d);
-    const Scratch S = scratch_layout(d);
-    const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
-    hipStream_t st = (hipStream_t)stream;
-    const int es = d.es;
-    float *red = at<float *>(scratch, S.red);
-    EpiArgs e;
-
-    if (phase == TP_BWD_MLP) {
-        NEED(dy, "dy");
-        NEED(partial_out, "partial_out");
+    const bool mlp = phase == TP_BWD_MLP || phase == TP_BWD_MLP_DATA;
+    const bool attn = phase == TP_BWD_ATTN || phase == TP_BWD_ATTN_DATA;
+    const bool mlp_w = phase == TP_BWD_MLP || phase == TP_BWD_WGRAD;
+    const bool attn_w = phase == TP_BWD_ATTN || phase == TP_BWD_WGRAD;
+    const bool acc = g->accumulate != 0;
+    // every check runs before anything is enqueued
+    if (mlp || attn || mlp_w || attn_w) NEED(dy, "dy");
+    if (mlp || attn) NEED(partial_out, "partial_out");
+    if (mlp) {
         NEED(w->w1, "w.w1");
         NEED(w->w2, "w.w2");
+    }
+    if (mlp_w) {
         NEED(g->w1, "g.w1");
         NEED(g->b1, "g.b1");
         NEED(g->w2, "g.w2");
         NEED(g->b2, "g.b2");
-        const void *dyr = at<const char *>(dy, r0 * d.h * es);
-        void *dz = at<char *>(scratch, S.dz + r0 * d.ft * es);
-        const void *z = at<const char *>(saved, L.z + r0 * d.ft * es);
-        const void *gg = at<const char *>(saved, L.g + r0 * d.ft * es);
-        const void *u2 = at<const char *>(saved, L.u2 + r0 * d.h * es);
-        e = EpiArgs{};
-        e.c = dz; e.ldc = d.ft; e.aux = z; e.ldaux = d.ft;
-        HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{dyr, d.h, true}, Mat{w->w2, d.ft, false}, Epi::GeluGrad,
-                     e, st),
-                "FC2 input-gradient product");
-        e = EpiArgs{};
-        e.c = partial_out + r0 * d.h; e.ldc = d.h;
-        HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ft, Mat{dz, d.ft, true}, Mat{w->w1, d.h, false}, Epi::StoreF32,
-                     e, st),
-                "FC1 input-gradient product");
-        e = EpiArgs{};
-        e.c = g->w2; e.ldc = d.ft;
-        HIPCALL(gemm(d.dt, (int)d.h, (int)d.ft, (int)nrows, Mat{dyr, d.h, false}, Mat{gg, d.ft, false}, Epi::AccumF32, e,
-                     st),
-                "FC2 weight-gradient product");
-        e = EpiArgs{};
-        e.c = g->w1; e.ldc = d.h;
-        HIPCALL(gemm(d.dt, (int)d.ft, (int)d.h, (int)nrows, Mat{dz, d.ft, false}, Mat{u2, d.h, false}, Epi::AccumF32, e,
-                     st),
-                "FC1 weight-gradient product");
-        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)d.ft, dz, d.ft, g->b1, red, st), "b1 gradient");
-        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)d.h, dyr, d.h, g->b2, red, st), "b2 gradient");
-        return TP_OK;
     }
-
-    if (phase == TP_BWD_ATTN) {
-        NEED(dy, "dy");
+    if (attn || phase == TP_BWD_LN1) {
         NEED(ln_in, "ln_in");
         NEED(reduced_in, "reduced_in");
-        NEED(partial_out, "partial_out");
-        NEED(dh, "dh");
+    }
+    if (attn || attn_w || phase == TP_BWD_LN1) NEED(dh, "dh");
+    if (attn) {
         NEED(w->ln2_g, "w.ln2_g");
-        NEED(w->w_qkv, "w.w_qkv");
         NEED(w->w_o, "w.w_o");
         NEED(g->ln2_g, "g.ln2_g");
         NEED(g->ln2_b, "g.ln2_b");
-        NEED(g->w_o, "g.w_o");
-        NEED(g->b_o, "g.b_o");
-        NEED(g->w_qkv, "g.w_qkv");
-        NEED(g->b_qkv, "g.b_qkv");
-        if (!kv || !kvg) return fail(TP_EINVAL, "kv and kvg are required for TP_BWD_ATTN");
+        if (!kv || !kvg) return fail(TP_EINVAL, "kv and kvg are required for the attention backward");
         NEED(kv->k, "kv.k");
         NEED(kv->v, "kv.v");
         NEED(kvg->dk, "kvg.dk");
@@ -349,24 +315,76 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         if (kvg->done_from != o1)
             return fail(TP_EORDER, "backward slices must run in reverse: done_from is %d, call ends at %lld",
                         kvg->done_from, (long long)o1);
-        void *dhr = at<char *>(dh, r0 * d.h * es);
-        HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, at<const char *>(dy, r0 * d.h * es),
+    }
+    if (phase == TP_BWD_ATTN) NEED(w->w_qkv, "w.w_qkv");
+    if (phase == TP_BWD_ATTN_DATA) NEED(w->w_qkv, "w.w_qkv");
+    if (attn_w) {
+        NEED(g->w_o, "g.w_o");
+        NEED(g->b_o, "g.b_o");
+        NEED(g->w_qkv, "g.w_qkv");
+        NEED(g->b_qkv, "g.b_qkv");
+    }
+    if (phase == TP_BWD_LN1) {
+        NEED(dx, "dx");
+        NEED(w->ln1_g, "w.ln1_g");
+        NEED(g->ln1_g, "g.ln1_g");
+        NEED(g->ln1_b, "g.ln1_b");
+    }
+
+    const Saved L = saved_layout(d);
+    const Scratch S = scratch_layout(d);
+    const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
+    hipStream_t st = (hipStream_t)stream;
+    const int es = d.es;
+    float *red = at<float *>(scratch, S.red);
+    const Epi wepi = acc ? Epi::AccumF32 : Epi::StoreF32;  // weight-gradient epilogue
+    EpiArgs e;
+    // rows of the call in each per-row tensor
+    const void *dyr = dy ? at<const char *>(dy, r0 * d.h * es) : nullptr;
+    void *dz = at<char *>(scratch, S.dz + r0 * d.ft * es);
+    void *dO = at<char *>(scratch, S.dO + r0 * d.ht * es);
+    void *dqkv = at<char *>(scratch, S.dqkv + r0 * 3 * d.ht * es);
+    void *dhr = dh ? at<char *>(dh, r0 * d.h * es) : nullptr;
+
+    if (mlp) {
+        // dZ = (dY W2) * GELU'(Z); dU2,r = dZ W1
+        e = EpiArgs{};
+        e.c = dz; e.ldc = d.ft; e.aux = at<const char *>(saved, L.z + r0 * d.ft * es); e.ldaux = d.ft;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{dyr, d.h, true}, Mat{w->w2, d.ft, false}, Epi::GeluGrad,
+                     e, st),
+                "FC2 input-gradient product");
+        e = EpiArgs{};
+        e.c = partial_out + r0 * d.h; e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ft, Mat{dz, d.ft, true}, Mat{w->w1, d.h, false}, Epi::StoreF32,
+                     e, st),
+                "FC1 input-gradient product");
+    }
+    if (mlp_w) {
+        // dW2 = dY^T G, dW1 = dZ^T u2, db1 = sum dZ, db2 = sum dY
+        e = EpiArgs{};
+        e.c = g->w2; e.ldc = d.ft;
+        HIPCALL(gemm(d.dt, (int)d.h, (int)d.ft, (int)nrows, Mat{dyr, d.h, false},
+                     Mat{at<const char *>(saved, L.g + r0 * d.ft * es), d.ft, false}, wepi, e, st),
+                "FC2 weight-gradient product");
+        e = EpiArgs{};
+        e.c = g->w1; e.ldc = d.h;
+        HIPCALL(gemm(d.dt, (int)d.ft, (int)d.h, (int)nrows, Mat{dz, d.ft, false},
+                     Mat{at<const char *>(saved, L.u2 + r0 * d.h * es), d.h, false}, wepi, e, st),
+                "FC1 weight-gradient product");
+        HIPCALL(colsum(d.dt, (int)nrows, (int)d.ft, dz, d.ft, g->b1, acc, red, st), "b1 gradient");
+        HIPCALL(colsum(d.dt, (int)nrows, (int)d.h, dyr, d.h, g->b2, acc, red, st), "b2 gradient");
+    }
+    if (attn) {
+        // dH = dY + LN2^T(sum_r dU2,r); dO = dH W_o; attention backward
+        HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dyr,
                               at<const char *>(ln_in, r0 * d.h * es), w->ln2_g, at<const float *>(saved, L.mu2 + r0 * 4),
-                              at<const float *>(saved, L.rs2 + r0 * 4), dhr, g->ln2_g, g->ln2_b, red, st),
+                              at<const float *>(saved, L.rs2 + r0 * 4), dhr, g->ln2_g, g->ln2_b, acc, red, st),
                 "layernorm backward (LN2)");
-        void *dO = at<char *>(scratch, S.dO + r0 * d.ht * es);
-        const void *o = at<const char *>(saved, L.o + r0 * d.ht * es);
         e = EpiArgs{};
         e.c = dO; e.ldc = d.ht;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.ht, (int)d.h, Mat{dhr, d.h, true}, Mat{w->w_o, d.ht, false}, Epi::Store, e,
                      st),
                 "out-projection input-gradient product");
-        e = EpiArgs{};
-        e.c = g->w_o; e.ldc = d.ht;
-        HIPCALL(gemm(d.dt, (int)d.h, (int)d.ht, (int)nrows, Mat{dhr, d.h, false}, Mat{o, d.ht, false}, Epi::AccumF32, e,
-                     st),
-                "out-projection weight-gradient product");
-        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)d.h, dhr, d.h, g->b_o, red, st), "b_o gradient");
         AttnArgs a{};
         a.batch = (int)d.b; a.nt = (int)d.nt; a.seq = (int)d.s; a.d = (int)d.d; a.q0 = (int)o0; a.q1 = (int)o1;
         a.scale = 1.0f / std::sqrt((float)d.d);
@@ -380,36 +398,36 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         a.k_final0 = (int)o0;
         a.acc_in = kvg->done_from != d.s;
         HIPCALL(attn_bwd(d.dt, a, st), "attention backward");
-        const void *dqkv = at<const char *>(scratch, S.dqkv + r0 * 3 * d.ht * es);
-        const void *u1 = at<const char *>(saved, L.u1 + r0 * d.h * es);
+        // dU1,r = dQKV W_qkv
         e = EpiArgs{};
         e.c = partial_out + r0 * d.h; e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)(3 * d.ht), Mat{dqkv, 3 * d.ht, true}, Mat{w->w_qkv, d.h, false},
                      Epi::StoreF32, e, st),
                 "QKV input-gradient product");
+        kvg->done_from = (int32_t)o0;
+    }
+    if (attn_w) {
+        // dW_o = dH^T O, db_o = sum dH, dW_qkv = dQKV^T u1, db_qkv = sum dQKV
+        e = EpiArgs{};
+        e.c = g->w_o; e.ldc = d.ht;
+        HIPCALL(gemm(d.dt, (int)d.h, (int)d.ht, (int)nrows, Mat{dhr, d.h, false},
+                     Mat{at<const char *>(saved, L.o + r0 * d.ht * es), d.ht, false}, wepi, e, st),
+                "out-projection weight-gradient product");
+        HIPCALL(colsum(d.dt, (int)nrows, (int)d.h, dhr, d.h, g->b_o, acc, red, st), "b_o gradient");
         e = EpiArgs{};
         e.c = g->w_qkv; e.ldc = d.h;
-        HIPCALL(gemm(d.dt, (int)(3 * d.ht), (int)d.h, (int)nrows, Mat{dqkv, 3 * d.ht, false}, Mat{u1, d.h, false},
-                     Epi::AccumF32, e, st),
+        HIPCALL(gemm(d.dt, (int)(3 * d.ht), (int)d.h, (int)nrows, Mat{dqkv, 3 * d.ht, false},
+                     Mat{at<const char *>(saved, L.u1 + r0 * d.h * es), d.h, false}, wepi, e, st),
                 "QKV weight-gradient product");
-        HIPCALL(colsum_accum(d.dt, (int)nrows, (int)(3 * d.ht), dqkv, 3 * d.ht, g->b_qkv, red, st), "b_qkv gradient");
-        kvg->done_from = (int32_t)o0;
-        return TP_OK;
+        HIPCALL(colsum(d.dt, (int)nrows, (int)(3 * d.ht), dqkv, 3 * d.ht, g->b_qkv, acc, red, st), "b_qkv gradient");
     }
-
-    // TP_BWD_LN1
-    NEED(ln_in, "ln_in");
-    NEED(reduced_in, "reduced_in");
-    NEED(dh, "dh");
-    NEED(dx, "dx");
-    NEED(w->ln1_g, "w.ln1_g");
-    NEED(g->ln1_g, "g.ln1_g");
-    NEED(g->ln1_b, "g.ln1_b");
-    HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, at<const char *>(dh, r0 * d.h * es),
-                          at<const char *>(ln_in, r0 * d.h * es), w->ln1_g, at<const float *>(saved, L.mu1 + r0 * 4),
-                          at<const float *>(saved, L.rs1 + r0 * 4), at<char *>(dx, r0 * d.h * es), g->ln1_g, g->ln1_b,
-                          red, st),
-            "layernorm backward (LN1)");
+    if (phase == TP_BWD_LN1) {
+        HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dhr,
+                              at<const char *>(ln_in, r0 * d.h * es), w->ln1_g, at<const float *>(saved, L.mu1 + r0 * 4),
+                              at<const float *>(saved, L.rs1 + r0 * 4), at<char *>(dx, r0 * d.h * es), g->ln1_g,
+                              g->ln1_b, acc, red, st),
+                "layernorm backward (LN1)");
+    }
     return TP_OK;
 }
 

@@ -8,16 +8,13 @@
 // weight gradient dW = dY^T X (a reduction over tokens: both operands are
 // M/N-contiguous).
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on LDS-staged tiles.  Each workgroup of
-// 4 waves computes a BM x BN tile; each wave a (BM/2) x (BN/2) sub-tile as a
-// grid of 32x32 MFMA blocks.  Global loads are raw buffer loads (16 bytes per
-// lane, zero-filled outside the matrix), prefetched one K-tile ahead into
-// registers while the MFMAs run on the current LDS buffer (two LDS buffers,
-// one barrier per K-tile).  LDS rows hold 8 chunks of 16 bytes (BK = 64);
-// chunk c of row r is stored at c ^ ((r ^ (r >> 3)) & 7), which keeps both
-// the MFMA fragment reads (8 consecutive rows, same chunk) and the
-// transposing stores (rows 8 apart) free of bank conflicts.  An operand that
-// is M/N-contiguous in memory is transposed in registers on its way to LDS.
+// bf16 path: v_mfma_f32_32x32x16_bf16.  A workgroup of 4 waves computes a
+// 128x128 (or 256x256) tile, each wave a quarter of it as a grid of 32x32
+// MFMA blocks.  K-tiles of 64 travel from HBM straight into LDS (buffer
+// loads that write LDS, two stages, the next K-tile in flight while the
+// current one feeds the MFMAs); fragments are read from LDS with
+// ds_read_b128 (K-contiguous operands) or ds_read_b64_tr_b16 (M/N-contiguous
+// operands, read transposed).  Tiles are mapped to workgroups XCD-aware.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles, 4 x 4 per thread).
 #include <cmath>
@@ -116,67 +113,91 @@ struct GemmArgs {
 
 __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Loads a ROWS x BK tile (ROWS along M or N) of one bf16 operand into
-// registers and stores it to LDS as [ROWS][BK] with the chunk swizzle.
-template <int ROWS, int BK, int NT, bool KCONTIG>
-struct TileLoader {
-    static constexpr int VEC = ROWS * BK / 8 / NT;  // 16-byte vectors per thread
-    static_assert(VEC >= 1, "tile too small for the thread count");
-    u32x4 r[VEC];
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel with direct-to-LDS loads
+//
+// Tiles travel from HBM to LDS by buffer loads that write LDS directly (each
+// lane's 16 bytes land at the instruction's LDS base + 16 * lane), so no
+// registers stage them and several K-tiles can be in flight (S LDS stages).
+// A K-contiguous operand is stored [rows][64 k] with its 16-byte chunks
+// XOR-swizzled by row (the permutation is applied to the global addresses,
+// since the LDS side of the copy is fixed); fragments are read with
+// ds_read_b128.  An M/N-contiguous operand is stored as it lies in memory,
+// [64 k][rows], with 16-byte units XOR-swizzled by k, and its fragments are
+// read transposed with ds_read_b64_tr_b16: in a group of 16 lanes, lane i
+// receives element i%4 of the 8-byte pieces addressed by lanes i/4 + 4j
+// (j = 0..3), which gives each lane 4 consecutive k of one row of the tile.
+// Loads outside the matrix write zeros to LDS, which masks ragged edges.
+// ---------------------------------------------------------------------------
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int mn0, int k0, int MN, int K,
-                                         int64_t ld, int tid) {
-        if constexpr (KCONTIG) {
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One operand tile of ROWS (M or N) x 64 (K) bf16 in LDS: ROWS * 128 bytes.
+template <int ROWS, bool KCONTIG, int NWAVES>
+struct DlOperand {
+    static constexpr int kBytes = ROWS * 128;
+    static constexpr int kInstr = kBytes / 1024;          // 1 KB per wave-wide load
+    static_assert(kInstr % NWAVES == 0, "tile must split evenly over the waves");
+    static constexpr int kPerWave = kInstr / NWAVES;      // loads per wave per K-tile
+    static constexpr int kPitch = ROWS * 2;               // row pitch of the [64][ROWS] layout
+    static constexpr int kUnits = ROWS / 8;               // 16-byte units per [64][ROWS] row
+
+    __device__ static __forceinline__ int swz_k(int k) { return (k & 3) * 4 & (kUnits - 1); }
+
+    __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char *stage, int mn0, int k0, int MN,
+                                                 int K, int64_t ld, int wave, int lane) {
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                int v = tid + i * NT;
-                int row = v / (BK / 8), ch = v % (BK / 8);
-                int gm = mn0 + row, gk = k0 + ch * 8;
-                uint32_t off = (gm < MN && gk < K) ? (uint32_t)((gm * ld + gk) * 2) : kOOB;
-                r[i] = buf_load16(rs, off);
+        for (int q = 0; q < kPerWave; ++q) {
+            const int I = wave * kPerWave + q;
+            uint32_t off;
+            if constexpr (KCONTIG) {
+                const int row = I * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ lds_swz(row);
+                const int gm = mn0 + row, gk = k0 + c * 8;
+                off = (gm < MN && gk < K) ? (uint32_t)((gm * ld + gk) * 2) : kOOB;
+            } else {
+                const int byte = I * 1024 + lane * 16;
+                const int k = byte / kPitch;
+                const int u = ((byte % kPitch) >> 4) ^ swz_k(k);
+                const int gk = k0 + k, gm = mn0 + u * 8;
+                off = (gm < MN && gk < K) ? (uint32_t)((gk * ld + gm) * 2) : kOOB;
             }
-        } else {
-            static_assert(VEC == 4 || VEC == 8, "transposing loader needs 4 or 8 vectors");
-            int mnb = tid % (ROWS / 8), kg = tid / (ROWS / 8);
-            int gm = mn0 + mnb * 8;
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                int gk = k0 + kg * VEC + i;
-                uint32_t off = (gm < MN && gk < K) ? (uint32_t)((gk * ld + gm) * 2) : kOOB;
-                r[i] = buf_load16(rs, off);
-            }
+            lds_dma16(r, stage + I * 1024, off);
         }
     }
 
-    __device__ __forceinline__ void store(char *lds, int tid) const {
+    // MFMA 32x32x16 operand: row (M or N index) `mn` = base + lane % 32 of
+    // the fragment, k = kk*16 + 8*(lane/32) + j for j = 0..7.
+    __device__ static __forceinline__ bf16x8 frag(const char *stage, int base, int kk, int lane) {
         if constexpr (KCONTIG) {
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                int v = tid + i * NT;
-                int row = v / (BK / 8), ch = v % (BK / 8);
-                *(u32x4 *)(lds + row * (BK * 2) + ((ch ^ lds_swz(row)) << 4)) = r[i];
-            }
+            const int row = base + (lane & 31);
+            const int c = kk * 2 + (lane >> 5);
+            return *(const bf16x8 *)(stage + row * 128 + ((c ^ lds_swz(row)) << 4));
         } else {
-            int mnb = tid % (ROWS / 8), kg = tid / (ROWS / 8);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                int row = mnb * 8 + c;
-                // word w of the output: element c of r[2w] (low) and of r[2w+1] (high)
-                uint32_t w[VEC / 2];
-#pragma unroll
-                for (int ww = 0; ww < VEC / 2; ++ww) {
-                    uint32_t lo = r[2 * ww][c >> 1], hi = r[2 * ww + 1][c >> 1];
-                    w[ww] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-                }
-                int kbyte = kg * VEC * 2;  // byte offset of this thread's k-range in the row
-                int ch = kbyte >> 4, within = kbyte & 15;
-                char *dst = lds + row * (BK * 2) + ((ch ^ lds_swz(row)) << 4) + within;
-                if constexpr (VEC == 4) {
-                    *(u32x2 *)dst = u32x2{w[0], w[1]};
-                } else {
-                    *(u32x4 *)dst = u32x4{w[0], w[1], w[2], w[3]};
-                }
-            }
+            const int L = lane & 15;
+            const int mn = base + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+            const int k = kk * 16 + 8 * (lane >> 5) + (L >> 2);
+            const int u = mn >> 3, within = (mn & 7) * 2;
+            const char *p0 = stage + k * kPitch + ((u ^ swz_k(k)) << 4) + within;
+            const char *p1 = stage + (k + 4) * kPitch + ((u ^ swz_k(k + 4)) << 4) + within;
+            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+            u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+            return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
         }
     }
 };
@@ -199,20 +220,24 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
     tn = r / rows;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-struct TileCfg {
-    static constexpr int kBM = BM, kBN = BN, kBK = 64, kWM = WAVES_M, kWN = WAVES_N;
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+struct DlCfg {
+    static constexpr int kBM = BM, kBN = BN, kBK = 64, kWM = WAVES_M, kWN = WAVES_N, kStages = STAGES;
     static constexpr int kThreads = WAVES_M * WAVES_N * 64;
-    static constexpr int kLds = 2 * (BM + BN) * 64 * 2;  // two stages of A and B tiles
+    static constexpr int kLds = STAGES * (BM + BN) * 128;
 };
 
 template <class C, bool AK, bool BK_, class Epi>
-__global__ __launch_bounds__(C::kThreads) void gemm_bf16_kernel(GemmArgs g, Epi epi, int gm_rows) {
-    constexpr int BM = C::kBM, BN = C::kBN, BK = C::kBK, NT = C::kThreads;
+__global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, Epi epi, int gm_rows) {
+    constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
+    constexpr int NW = C::kWM * C::kWN;
     constexpr int WTM = BM / C::kWM, WTN = BN / C::kWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using OpA = DlOperand<BM, AK, NW>;
+    using OpB = DlOperand<BN, BK_, NW>;
+    constexpr int STAGE = OpA::kBytes + OpB::kBytes;
+    constexpr int LPT = OpA::kPerWave + OpB::kPerWave;  // loads per wave per K-tile
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid / C::kWN, wn = wid % C::kWN;
@@ -223,8 +248,6 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_kernel(GemmArgs g, Epi 
 
     __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
     __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
-    TileLoader<BM, BK, NT, AK> la;
-    TileLoader<BN, BK, NT, BK_> lb;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -232,53 +255,44 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_kernel(GemmArgs g, Epi 
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    // per-lane LDS byte offsets of the fragment rows (the chunk is added per k-step)
-    int a_row[FM], b_row[FN];
+    const int nkt = (g.K + 63) / 64;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a_row[i] = wm * WTM + i * 32 + (lane & 31);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b_row[j] = wn * WTN + j * 32 + (lane & 31);
-
-    const int nkt = (g.K + BK - 1) / BK;
-    la.load(ra, m0, 0, g.M, g.K, g.lda, tid);
-    lb.load(rb, n0, 0, g.N, g.K, g.ldb, tid);
-    la.store(smem, tid);
-    lb.store(smem + A_BYTES, tid);
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const char *cur = smem + (kt & 1) * (A_BYTES + B_BYTES);
-        const bool more = kt + 1 < nkt;
-        if (more) {
-            la.load(ra, m0, (kt + 1) * BK, g.M, g.K, g.lda, tid);
-            lb.load(rb, n0, (kt + 1) * BK, g.N, g.K, g.ldb, tid);
+    for (int s = 0; s < S - 1; ++s) {
+        if (s < nkt) {
+            OpA::issue(ra, smem + s * STAGE, m0, s * 64, g.M, g.K, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, s * 64, g.N, g.K, g.ldb, wid, lane);
         }
+    }
+    for (int kt = 0; kt < nkt; ++kt) {
+        // tile kt must have landed; the S-2 tiles after it may still be in flight
+        if constexpr (S == 3) {
+            if (kt + 1 < nkt) wait_vmcnt<LPT>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        if (kt + S - 1 < nkt) {
+            char *st = smem + ((kt + S - 1) % S) * STAGE;
+            OpA::issue(ra, st, m0, (kt + S - 1) * 64, g.M, g.K, g.lda, wid, lane);
+            OpB::issue(rb, st + OpA::kBytes, n0, (kt + S - 1) * 64, g.N, g.K, g.ldb, wid, lane);
+        }
+        const char *cur = smem + (kt % S) * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
+        for (int kk = 0; kk < 4; ++kk) {
             bf16x8 fa[FM], fb[FN];
-            const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[i] = *(const bf16x8 *)(cur + a_row[i] * (BK * 2) + ((ch ^ lds_swz(a_row[i])) << 4));
+            for (int i = 0; i < FM; ++i) fa[i] = OpA::frag(cur, wm * WTM + i * 32, kk, lane);
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                fb[j] = *(const bf16x8 *)(cur + A_BYTES + b_row[j] * (BK * 2) + ((ch ^ lds_swz(b_row[j])) << 4));
+            for (int j = 0; j < FN; ++j) fb[j] = OpB::frag(cur + OpA::kBytes, wn * WTN + j * 32, kk, lane);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if (more) {
-            char *nxt = smem + ((kt + 1) & 1) * (A_BYTES + B_BYTES);
-            la.store(nxt, tid);
-            lb.store(nxt + A_BYTES, tid);
-        }
-        __syncthreads();
     }
 
-    // 32x32 accumulator layout: register v of lane l holds
-    // row 8*(v/4) + 4*(l/32) + v%4, column l%32 of the block.
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -351,48 +365,38 @@ static uint32_t extent_bytes(int rows, int k, const Mat &m, int es) {
     return (uint32_t)(last * es);
 }
 
-// Tile configurations of the bf16 kernel.  Wide wave tiles cut the LDS
-// traffic per MFMA (128x128 per wave reads 1 KB of fragments per 32x32 block
-// pair); smaller tiles give more workgroups where M or N is small.
-using Cfg256x256 = TileCfg<256, 256, 2, 2>;
-using Cfg256x128 = TileCfg<256, 128, 2, 2>;
-using Cfg128x128 = TileCfg<128, 128, 2, 2>;
-
-enum class TileChoice { T256x256, T256x128, T128x128 };
-
-// Picks the tile for an M x N x K product.  Measured on MI355X: the
-// 128x128 tile (up to three workgroups per compute unit hide each other's
-// memory latency) is fastest for every product of the GPT-3 175B shard; the
-// 256x256 tile only wins on large products whose operands are both
-// K-contiguous (e.g. 8192^3, 4096x24576x6144).
-static TileChoice choose_tile(int M, int N, int K, bool ak, bool bk) {
-    const double tiles128 = (double)((M + 127) / 128) * ((N + 127) / 128);
-    if (ak && bk && tiles128 >= 4096 && K >= 1024) return TileChoice::T256x256;
-    return TileChoice::T128x128;
-}
-
 template <class C, bool AK, bool BK_, class E>
-static hipError_t launch_cfg(const GemmArgs &g, const E &epi, hipStream_t st) {
+static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_kernel<C, AK, BK_, E>,
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_dl_kernel<C, AK, BK_, E>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
-    hipLaunchKernelGGL((gemm_bf16_kernel<C, AK, BK_, E>), dim3(tiles), dim3(C::kThreads), C::kLds, st, g, epi, 4);
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<C, AK, BK_, E>), dim3(tiles), dim3(C::kThreads), C::kLds, st, g, epi, 4);
     return hipGetLastError();
+}
+
+using Dl128 = DlCfg<128, 128, 2, 2, 2>;  // 64 KB of LDS: two workgroups per compute unit
+using Dl256 = DlCfg<256, 256, 2, 2, 2>;  // 128 KB of LDS: one workgroup per compute unit
+
+// The 256x256 tile reads half the LDS bytes per MFMA but runs one workgroup
+// per compute unit; measured on MI355X it wins only when there are at least
+// two full rounds of its tiles over the 256 compute units (8192^3,
+// 4096x24576x6144); every product of the GPT-3 175B shard runs faster on the
+// 128x128 tile.
+static bool use_256(int M, int N) {
+    const double tiles256 = (double)((M + 255) / 256) * ((N + 255) / 256);
+    return tiles256 >= 512;
 }
 
 template <typename T, bool AK, bool BK_, class E>
 static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        switch (choose_tile(g.M, g.N, g.K, AK, BK_)) {
-        case TileChoice::T256x256: return launch_cfg<Cfg256x256, AK, BK_>(g, epi, st);
-        case TileChoice::T256x128: return launch_cfg<Cfg256x128, AK, BK_>(g, epi, st);
-        default: return launch_cfg<Cfg128x128, AK, BK_>(g, epi, st);
-        }
+        if (use_256(g.M, g.N)) return launch_dl<Dl256, AK, BK_>(g, epi, st);
+        return launch_dl<Dl128, AK, BK_>(g, epi, st);
     } else {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
         hipLaunchKernelGGL((gemm_f32_kernel<AK, BK_, E>), grid, dim3(256), 0, st, g, epi);

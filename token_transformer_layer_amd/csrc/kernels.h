@@ -48,16 +48,19 @@ hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, co
                          const void *b, void *u, float *mean, float *rstd, hipStream_t st);
 
 // LayerNorm backward with residual: dx = resid + LN^T(du); the parameter
-// gradients are added into dg/db (fp32) through a deterministic two-stage
-// reduction that uses `partials` (fp32, layernorm_bwd_partials_floats).
+// gradients go to dg/db (fp32; added when accumulate, else stored) through a
+// deterministic two-stage reduction that uses `partials` (fp32,
+// layernorm_bwd_partials_floats).
 hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void *resid,
                          const void *x, const void *g, const float *mean, const float *rstd,
-                         void *dx, float *dg, float *db, float *partials, hipStream_t st);
+                         void *dx, float *dg, float *db, bool accumulate, float *partials,
+                         hipStream_t st);
 size_t layernorm_bwd_partials_floats(int rows, int h);
 
-// Column sums over rows added into out (fp32), two stages via `partials`.
-hipError_t colsum_accum(DType dt, int rows, int n, const void *a, int64_t lda, float *out,
-                        float *partials, hipStream_t st);
+// Column sums over rows into out (fp32; added when accumulate, else
+// stored), two stages via `partials`.
+hipError_t colsum(DType dt, int rows, int n, const void *a, int64_t lda, float *out, bool accumulate,
+                  float *partials, hipStream_t st);
 size_t colsum_partials_floats(int rows, int n);
 
 // out = resid + reduced + bias[c]

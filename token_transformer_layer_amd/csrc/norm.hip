@@ -161,13 +161,13 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(int rows, int h, int r
     for (int c = threadIdx.x; c < 2 * h; c += kThreads) pb[c] = accs[c];
 }
 
-// out[c] += sum over blocks of partials[blk][c], for c < n; partial rows are
+// out[c] (+)= sum over blocks of partials[blk][c], for c < n; partial rows are
 // `stride` floats apart.  A workgroup owns 32 columns; its 8 row groups each
 // sum every 8th partial row, and the 8 sums are added in a fixed order.
 constexpr int kRedCols = 32, kRedGroups = kThreads / kRedCols;
 __global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n, int64_t stride,
                                                                  const float *__restrict__ partials,
-                                                                 float *__restrict__ out) {
+                                                                 float *__restrict__ out, int accumulate) {
     __shared__ float part[kRedGroups][kRedCols];
     const int cx = threadIdx.x % kRedCols, gy = threadIdx.x / kRedCols;
     const int c = blockIdx.x * kRedCols + cx;
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n
         float t = 0.f;
 #pragma unroll
         for (int k = 0; k < kRedGroups; ++k) t += part[k][cx];
-        out[c] += t;
+        out[c] = accumulate ? out[c] + t : t;
     }
 }
 
@@ -247,7 +247,7 @@ hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, co
 
 hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void *resid, const void *x,
                          const void *g, const float *mean, const float *rstd, void *dx, float *dg, float *db,
-                         float *partials, hipStream_t st) {
+                         bool accumulate, float *partials, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     const int nblk = ln_bwd_blocks(rows), rpb = (rows + nblk - 1) / nblk;
     const size_t lds = (size_t)2 * h * sizeof(float);
@@ -272,18 +272,18 @@ hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void 
     {
         TraceScope ts(st, "block_reduce", 0.0, (double)nblk * h * 4 + 8.0 * h);
         hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
-                           (const float *)partials, dg);
+                           (const float *)partials, dg, accumulate ? 1 : 0);
     }
     {
         TraceScope ts(st, "block_reduce", 0.0, (double)nblk * h * 4 + 8.0 * h);
         hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
-                           (const float *)(partials + h), db);
+                           (const float *)(partials + h), db, accumulate ? 1 : 0);
     }
     return hipGetLastError();
 }
 
-hipError_t colsum_accum(DType dt, int rows, int n, const void *a, int64_t lda, float *out, float *partials,
-                        hipStream_t st) {
+hipError_t colsum(DType dt, int rows, int n, const void *a, int64_t lda, float *out, bool accumulate,
+                  float *partials, hipStream_t st) {
     if (rows <= 0 || n <= 0) return hipSuccess;
     const int nch = colsum_chunks(rows), rpc = (rows + nch - 1) / nch;
     dim3 grid((n / 8 + kThreads - 1) / kThreads, nch);
@@ -302,7 +302,7 @@ hipError_t colsum_accum(DType dt, int rows, int n, const void *a, int64_t lda, f
     if (e != hipSuccess) return e;
     TraceScope ts(st, "block_reduce", 0.0, (double)nch * n * 4 + 8.0 * n);
     hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kRedCols - 1) / kRedCols), dim3(kThreads), 0, st, nch, n,
-                       (int64_t)n, (const float *)partials, out);
+                       (int64_t)n, (const float *)partials, out, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 

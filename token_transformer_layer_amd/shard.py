@@ -2,8 +2,7 @@
 wrappers that pass their addresses to the C-ABI.
 
 torch provides device memory and the stream only; every step of the layer
-runs in libtpshard.so.  Gradient buffers are zeroed by the caller before a
-step, as the C-ABI specifies (``zero_grads``).
+runs in libtpshard.so.
 """
 import numpy as np
 import torch
@@ -57,7 +56,7 @@ class ShardLayer:
         self.kvg = abi.tp_kv_grad(_ptr(self.dk), _ptr(self.dv), s)
         self.g = {n: torch.zeros(self.p[n].shape if n in self.p else (h,), dtype=torch.float32, device=device)
                   for n in abi.GRAD_FIELDS}
-        self.gs = abi.tp_shard_grads(*[_ptr(self.g[n]) for n in abi.GRAD_FIELDS])
+        self.gs = abi.tp_shard_grads(*[_ptr(self.g[n]) for n in abi.GRAD_FIELDS], 1)
 
     def upload(self, arr):
         return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(self.device).to(self.dtype)
@@ -73,19 +72,23 @@ class ShardLayer:
         sh = self.shape
         return torch.empty((sh.seq, sh.batch, sh.hidden), dtype=torch.float32, device=self.device)
 
-    def new_step(self):
-        """Reset the cache protocol and zero the gradient accumulators."""
+    def new_step(self, fill=0.0):
+        """Reset the cache protocol and fill the gradient buffers (zeros for
+        steps that accumulate from the first call; any value for steps whose
+        first call of each gradient overwrites)."""
         self.kv.filled = 0
         self.kvg.done_from = self.shape.seq
         for t in self.g.values():
-            t.zero_()
+            t.fill_(fill)
 
     # phases -----------------------------------------------------------------
     def fwd(self, phase, j0, j1, inp, partial_out):
         abi.tp_shard_layer_fwd(self.cfg, self.w, self.part, j0, j1, phase, _ptr(inp), _ptr(partial_out),
                                self.kv, _ptr(self.saved), _ptr(self.scratch), stream_handle())
 
-    def bwd(self, phase, j0, j1, dy=None, ln_in=None, reduced=None, partial_out=None, dh=None, dx=None):
+    def bwd(self, phase, j0, j1, dy=None, ln_in=None, reduced=None, partial_out=None, dh=None, dx=None,
+            accumulate=True):
+        self.gs.accumulate = 1 if accumulate else 0
         abi.tp_shard_layer_bwd(self.cfg, self.w, self.part, j0, j1, phase, _ptr(dy), _ptr(ln_in), _ptr(reduced),
                                _ptr(partial_out), _ptr(dh), _ptr(dx), self.gs, self.kv, self.kvg,
                                _ptr(self.saved), _ptr(self.scratch), stream_handle())
