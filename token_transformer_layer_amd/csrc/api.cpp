@@ -97,7 +97,7 @@ Saved saved_layout(const Dims &d) {
 }
 
 struct Scratch {
-    int64_t dz, dO, delta, dqkv, red, total;
+    int64_t dz, dO, delta, dqkv, red, attn, total;
 };
 Scratch scratch_layout(const Dims &d) {
     Scratch L;
@@ -113,6 +113,7 @@ Scratch scratch_layout(const Dims &d) {
     if (3 * d.ht > widest) widest = 3 * d.ht;
     int64_t cs = (int64_t)colsum_partials_floats((int)d.T, (int)widest);
     L.red = take((red > cs ? red : cs) * 4);
+    L.attn = take((int64_t)attn_fwd_work_floats((int)d.b, (int)d.nt, (int)d.s, (int)d.d) * 4);
     L.total = off;
     return L;
 }
@@ -192,8 +193,9 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     NEED(in, "in");
     NEED(partial_out, "partial_out");
     NEED(saved, "saved");
-    (void)scratch;
+    NEED(scratch, "scratch");
     const Saved L = saved_layout(d);
+    const Scratch S = scratch_layout(d);
     const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
     hipStream_t st = (hipStream_t)stream;
     const int es = d.es;
@@ -228,6 +230,7 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         a.scale = 1.0f / std::sqrt((float)d.d);
         a.q = at<char *>(saved, L.q); a.k = kv->k; a.v = kv->v;
         a.o = at<char *>(saved, L.o); a.lse = at<float *>(saved, L.lse);
+        a.work = at<float *>(scratch, S.attn);
         HIPCALL(attn_fwd(d.dt, a, st), "attention forward");
         e = EpiArgs{};
         e.c = partial_out + r0 * d.h;

@@ -25,6 +25,9 @@
 //
 // fp32 kernels are plain one-wave-per-row loops (used for the fp32 storage
 // configuration only).
+#include <algorithm>
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -668,6 +671,258 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32(AttnF a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Forward, MFMA 32x32x16 with direct-to-LDS K/V tiles and split-KV
+//
+// A workgroup of 4 waves owns 128 queries (32 per wave) of one (batch row,
+// head) and a chunk of its key tiles (64 keys each).  K and V tiles travel
+// from HBM straight into LDS in their natural [key][d] layout (16-byte chunks
+// XOR-swizzled by key), two stages deep.  S^T = K Q^T leaves one query's 32
+// scores of a 32-key block in one lane (rows 8(v/4) + 4g + v%4), so eight
+// consecutive registers are the B operand of a 16-key step of O^T += V^T P^T;
+// V^T comes from LDS through transposed reads in the same key order.  When a
+// query tile's keys are split over several workgroups, each writes its
+// unnormalised O with its running maximum and sum, and a combine kernel
+// merges them (the merge of partial softmaxes over disjoint key blocks).
+// ---------------------------------------------------------------------------
+
+constexpr int kFwdBQ = 128;  // queries per workgroup
+constexpr int kFwdMaxChunks = 8;
+
+struct AttnFwdP {
+    int batch, nt, seq, q0, q1, nqt, chunk_tiles, max_chunks;
+    float sl2;  // scale * log2(e)
+    const bf16 *q, *k, *v;
+    bf16 *o;
+    float *lse;
+    float *part;  // [bh][nqt][max_chunks][BQ][D] unnormalised O, then [..][BQ][2] (m, l)
+    uint32_t kv_bytes;
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ int kv_chunk_off(int row, int c) {
+    return row * (D * 2) + ((c ^ (row & (D / 8 - 1))) << 4);
+}
+
+// one 64-key tile of K or V (rows [key0, key0+64), rows >= kend zero) into LDS
+template <int D>
+__device__ __forceinline__ void kv_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst, int64_t slab, int key0, int kend,
+                                            int wave, int lane) {
+    constexpr int INSTR = 64 * D * 2 / 1024, PER_WAVE = INSTR / 4;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+        const int I = wave * PER_WAVE + q;
+        const int byte = I * 1024 + lane * 16;
+        const int row = byte / (D * 2);
+        const int c = ((byte % (D * 2)) >> 4) ^ (row & (D / 8 - 1));
+        const int key = key0 + row;
+        const uint32_t off = key < kend ? (uint32_t)((slab + (int64_t)key * D + c * 8) * 2) : kOOB;
+        lds_dma16(r, dst + I * 1024, off);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_mfma32(AttnFwdP a) {
+    constexpr int KS = D / 16;  // k-steps of S^T = K Q^T
+    constexpr int DB = D / 32;  // 32-row blocks of O^T
+    constexpr int TILE = 64 * D * 2;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
+    const int c = blockIdx.x, qi = blockIdx.y, bh = blockIdx.z;
+    const int qt0 = a.q0 + qi * kFwdBQ;
+    const int kend = min(a.q1, qt0 + kFwdBQ);
+    const int ntiles = (kend + 63) / 64;
+    const int nch = (ntiles + a.chunk_tiles - 1) / a.chunk_tiles;
+    if (c >= nch) return;  // whole workgroup
+    const int t0 = c * a.chunk_tiles, t1 = min(ntiles, t0 + a.chunk_tiles);
+    const int bi = bh / a.nt, head = bh % a.nt;
+    const int my_q = qt0 + w * 32 + li;
+    const int q_eff = min(my_q, a.q1 - 1);  // padding queries act as the last query
+    const int64_t slab = (int64_t)bh * a.seq * D;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+
+    // B operand of S^T = K Q^T: lane (query li, g) holds Q[query][16 s + 8 g + j]
+    bf16x8 qreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint32_t off = my_q < a.q1 ? (uint32_t)((slab + (int64_t)my_q * D + s * 16 + g * 8) * 2) : kOOB;
+        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    }
+    f32x16 acc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    kv_tile_dma<D>(rk, smem, slab, t0 * 64, kend, w, lane);
+    kv_tile_dma<D>(rv, smem + TILE, slab, t0 * 64, kend, w, lane);
+    for (int t = t0; t < t1; ++t) {
+        // this tile's loads are done for this wave; the barrier (with its LDS
+        // fences, which keep the compiler from moving LDS reads across it)
+        // makes them done for all waves
+        wait_vmcnt<0>();
+        __syncthreads();
+        const char *ks = smem + ((t - t0) & 1) * 2 * TILE;
+        const char *vs = ks + TILE;
+        if (t + 1 < t1) {
+            char *nx = smem + ((t + 1 - t0) & 1) * 2 * TILE;
+            kv_tile_dma<D>(rk, nx, slab, (t + 1) * 64, kend, w, lane);
+            kv_tile_dma<D>(rv, nx + TILE, slab, (t + 1) * 64, kend, w, lane);
+        }
+        const int key0 = t * 64;
+        if (key0 > qt0 + w * 32 + 31) continue;  // every key of the tile is after this wave's queries
+        f32x16 sc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = f32x16{};
+            const int row = kb * 32 + li;
+#pragma unroll
+            for (int st = 0; st < KS; ++st)
+                sc[kb] = mfma32(*(const bf16x8 *)(ks + kv_chunk_off<D>(row, 2 * st + g)), qreg[st], sc[kb]);
+        }
+        // sc[kb][v]: score of key key0 + 32 kb + 8(v/4) + 4g + v%4 for query my_q
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
+                const float x = key <= q_eff ? sc[kb][v] * a.sl2 : -INFINITY;
+                sc[kb][v] = x;
+                mt = fmaxf(mt, x);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        // a query may see no key yet when its key range is split (m = -inf):
+        // then every weight is 0 and nothing is rescaled
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __builtin_amdgcn_exp2f(sc[kb][v] - m_use);
+                sc[kb][v] = p;
+                ls += p;
+            }
+        l_run = l_run * alpha + ls;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+        // P^T for key step ks (16 keys): registers 8h..8h+7 of block ks/2, h = ks%2
+        bf16x8 pb[4];
+#pragma unroll
+        for (int ks4 = 0; ks4 < 4; ++ks4) {
+            const f32x16 &src = sc[ks4 >> 1];
+            const int h = (ks4 & 1) * 8;
+            u32x4 wv{pack_bf2(src[h], src[h + 1]), pack_bf2(src[h + 2], src[h + 3]), pack_bf2(src[h + 4], src[h + 5]),
+                     pack_bf2(src[h + 6], src[h + 7])};
+            pb[ks4] = __builtin_bit_cast(bf16x8, wv);
+        }
+        const int G = lane >> 4, L = lane & 15;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (G & 1) + 4 * (L & 3);
+            const int cc = col >> 3, within = (col & 7) * 2;
+#pragma unroll
+            for (int ks4 = 0; ks4 < 4; ++ks4) {
+                const int r0 = 16 * ks4 + 4 * g + (L >> 2);
+                u32x2 lo = lds_read_tr16(vs + kv_chunk_off<D>(r0, cc) + within);
+                u32x2 hi = lds_read_tr16(vs + kv_chunk_off<D>(r0 + 8, cc) + within);
+                acc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks4], acc[db]);
+            }
+        }
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (my_q >= a.q1) return;
+    if (nch == 1) {
+        const float inv = 1.0f / l_tot;
+        const int ht = a.nt * D;
+        bf16 *orow = a.o + ((int64_t)my_q * a.batch + bi) * ht + head * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = db * 32 + 8 * r + 4 * g;
+                *(u32x2 *)(orow + d) = u32x2{pack_bf2(acc[db][4 * r] * inv, acc[db][4 * r + 1] * inv),
+                                             pack_bf2(acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv)};
+            }
+        if (g == 0) a.lse[(int64_t)bh * a.seq + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    } else {
+        const int64_t item = ((int64_t)bh * a.nqt + qi) * a.max_chunks + c;
+        float *po = a.part + (item * kFwdBQ + (w * 32 + li)) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *(f32x4 *)(po + db * 32 + 8 * r + 4 * g) =
+                    f32x4{acc[db][4 * r], acc[db][4 * r + 1], acc[db][4 * r + 2], acc[db][4 * r + 3]};
+        if (g == 0) {
+            float *pml = a.part + (int64_t)a.batch * a.nt * a.nqt * a.max_chunks * kFwdBQ * D +
+                         (item * kFwdBQ + (w * 32 + li)) * 2;
+            pml[0] = m_run;
+            pml[1] = l_tot;
+        }
+    }
+}
+
+// Merges the partial softmaxes of the key chunks of one query tile:
+// m = max_c m_c, l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l.
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_combine(AttnFwdP a) {
+    const int qi = blockIdx.x, bh = blockIdx.y;
+    const int qt0 = a.q0 + qi * kFwdBQ;
+    const int kend = min(a.q1, qt0 + kFwdBQ);
+    const int ntiles = (kend + 63) / 64;
+    const int nch = (ntiles + a.chunk_tiles - 1) / a.chunk_tiles;
+    if (nch == 1) return;
+    const int bi = bh / a.nt, head = bh % a.nt;
+    const int ql = threadIdx.x >> 1, half = threadIdx.x & 1;  // 2 threads per query, D/2 columns each
+    const int q = qt0 + ql;
+    if (q >= a.q1) return;
+    const int64_t item0 = ((int64_t)bh * a.nqt + qi) * a.max_chunks;
+    const float *pml = a.part + (int64_t)a.batch * a.nt * a.nqt * a.max_chunks * kFwdBQ * D;
+    float m = -INFINITY;
+    for (int cc = 0; cc < nch; ++cc) m = fmaxf(m, pml[((item0 + cc) * kFwdBQ + ql) * 2]);
+    float l = 0.f;
+    float o[D / 2];
+#pragma unroll
+    for (int j = 0; j < D / 2; ++j) o[j] = 0.f;
+    for (int cc = 0; cc < nch; ++cc) {
+        const float *e = pml + ((item0 + cc) * kFwdBQ + ql) * 2;
+        const float wgt = e[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(e[0] - m);
+        l += wgt * e[1];
+        const float *po = a.part + ((item0 + cc) * kFwdBQ + ql) * D + half * (D / 2);
+#pragma unroll
+        for (int j = 0; j < D / 2; j += 4) {
+            const f32x4 x = *(const f32x4 *)(po + j);
+            o[j] += wgt * x[0];
+            o[j + 1] += wgt * x[1];
+            o[j + 2] += wgt * x[2];
+            o[j + 3] += wgt * x[3];
+        }
+    }
+    const float inv = 1.0f / l;
+    bf16 *orow = a.o + ((int64_t)q * a.batch + bi) * (a.nt * D) + head * D + half * (D / 2);
+#pragma unroll
+    for (int j = 0; j < D / 2; j += 8) {
+        float v8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v8[i] = o[j + i] * inv;
+        store8(orow + j, v8);
+    }
+    if (half == 0) a.lse[(int64_t)bh * a.seq + q] = (m + __log2f(l)) * kLn2;
+}
+
 }  // namespace
 
 // (query, key) pairs of the causal product for queries [q0, q1) of every
@@ -675,6 +930,27 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32(AttnF a) {
 static double causal_pairs(const AttnArgs &x) {
     double q0 = x.q0, q1 = x.q1;
     return (q1 * (q1 + 1) - q0 * (q0 + 1)) / 2 * x.batch * x.nt;
+}
+
+// Key-chunk size of the split forward: enough work items to fill the chip
+// (about two per compute unit), at most kFwdMaxChunks chunks per query tile.
+static void fwd_split(const AttnArgs &x, AttnFwdP &p) {
+    const int nq = x.q1 - x.q0;
+    p.nqt = (nq + kFwdBQ - 1) / kFwdBQ;
+    const int max_tiles = (x.q1 + 63) / 64;
+    double total = 0;
+    for (int i = 0; i < p.nqt; ++i) total += (std::min(x.q1, x.q0 + (i + 1) * kFwdBQ) + 63) / 64;
+    total *= (double)x.batch * x.nt;
+    int ch = (int)std::ceil(total / 512.0);
+    ch = std::max(ch, (max_tiles + kFwdMaxChunks - 1) / kFwdMaxChunks);
+    ch = std::max(ch, 2);
+    p.chunk_tiles = std::min(ch, max_tiles);
+    p.max_chunks = (max_tiles + p.chunk_tiles - 1) / p.chunk_tiles;
+}
+
+size_t attn_fwd_work_floats(int batch, int nt, int seq, int d) {
+    const int nqt = (seq + kFwdBQ - 1) / kFwdBQ;
+    return (size_t)batch * nt * nqt * kFwdMaxChunks * kFwdBQ * (d + 2);
 }
 
 hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
@@ -687,14 +963,26 @@ hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
     TraceScope ts(st, dt == DType::BF16 ? "attn_fwd_bf16" : "attn_fwd_f32", 4.0 * x.d * causal_pairs(x),
                   (double)bh * x.d * es * (2.0 * nq + 2.0 * x.q1) + 4.0 * bh * nq);
     if (dt == DType::BF16) {
-        AttnP p{};
-        p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
+        AttnFwdP p{};
+        p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1;
+        p.sl2 = x.scale * kLog2e;
         p.q = (const bf16 *)x.q; p.k = (const bf16 *)x.k; p.v = (const bf16 *)x.v;
-        p.out = (bf16 *)x.o; p.lse = x.lse;
-        p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
-        dim3 grid((nq + 63) / 64, bh);
-        if (x.d == 128) hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, dim3(256), 0, st, p);
+        p.o = (bf16 *)x.o; p.lse = x.lse; p.part = x.work;
+        p.kv_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
+        fwd_split(x, p);
+        const int lds = 2 * 2 * 64 * x.d * 2;
+        dim3 grid(p.max_chunks, p.nqt, bh);
+        if (x.d == 128) {
+            hipFuncSetAttribute((const void *)attn_fwd_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            hipLaunchKernelGGL(attn_fwd_mfma32<128>, grid, dim3(256), lds, st, p);
+        } else {
+            hipFuncSetAttribute((const void *)attn_fwd_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            hipLaunchKernelGGL(attn_fwd_mfma32<64>, grid, dim3(256), lds, st, p);
+        }
+        if (p.max_chunks > 1) {
+            if (x.d == 128) hipLaunchKernelGGL(attn_fwd_combine<128>, dim3(p.nqt, bh), dim3(256), 0, st, p);
+            else hipLaunchKernelGGL(attn_fwd_combine<64>, dim3(p.nqt, bh), dim3(256), 0, st, p);
+        }
     } else {
         AttnF p{};
         p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.d = x.d; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;

@@ -30,6 +30,32 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Direct-to-LDS buffer load: each lane's 16 bytes land at lds_base + 16 *
+// lane (lds_base must be the same for the whole wave); an out-of-bounds
+// offset writes zeros.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes i/4 + 4j (j = 0..3), in j
+// order; with lane L addressing row r0 + L/4, columns c0 + 4(L%4)..+3 of a
+// row-major bf16 tile, lane i gets rows r0..r0+3 of column c0 + i.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p));
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16>(bf16 v) { return (float)v; }
@@ -44,6 +70,29 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
     bf16 a = (bf16)lo, b = (bf16)hi;
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// 8 consecutive elements (16 bytes of bf16 or 32 bytes of fp32; the address
+// is aligned to that size) converted to and from fp32.
+__device__ __forceinline__ void load8(const float *p, float o[8]) {
+    float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16 *p, float o[8]) {
+    u32x4 w = *(const u32x4 *)p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { o[2 * i] = bf_lo(w[i]); o[2 * i + 1] = bf_hi(w[i]); }
+}
+__device__ __forceinline__ void store8(float *p, const float v[8]) {
+    *(float4 *)p = float4{v[0], v[1], v[2], v[3]};
+    *(float4 *)(p + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+__device__ __forceinline__ void store8(bf16 *p, const float v[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf2(v[2 * i], v[2 * i + 1]);
+    *(u32x4 *)p = w;
 }
 
 // Unsigned division by a runtime constant d >= 1 (n < 2^31): q = n / d via a

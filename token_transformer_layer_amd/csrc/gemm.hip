@@ -27,7 +27,9 @@
 namespace tpk {
 
 // ---------------------------------------------------------------------------
-// Epilogues: called once per output element (m, n) inside the matrix.
+// Epilogues.  operator()(m, n, v) handles one output element (fp32 kernel);
+// row8(m, n, v[8]) handles 8 consecutive columns n..n+7 of row m with vector
+// loads and stores (bf16 kernel; every N the layer uses is a multiple of 8).
 // ---------------------------------------------------------------------------
 
 template <typename T>
@@ -35,6 +37,7 @@ struct EpiStoreF32 {
     float *c;
     int64_t ldc;
     __device__ __forceinline__ void operator()(int m, int n, float v) const { c[m * ldc + n] = v; }
+    __device__ __forceinline__ void row8(int m, int n, const float v[8]) const { store8(c + m * ldc + n, v); }
 };
 
 template <typename T>
@@ -42,6 +45,13 @@ struct EpiAccumF32 {
     float *c;
     int64_t ldc;
     __device__ __forceinline__ void operator()(int m, int n, float v) const { c[m * ldc + n] += v; }
+    __device__ __forceinline__ void row8(int m, int n, const float v[8]) const {
+        float o[8];
+        load8(c + m * ldc + n, o);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] += v[i];
+        store8(c + m * ldc + n, o);
+    }
 };
 
 template <typename T>
@@ -49,6 +59,7 @@ struct EpiStore {
     T *c;
     int64_t ldc;
     __device__ __forceinline__ void operator()(int m, int n, float v) const { c[m * ldc + n] = from_f32<T>(v); }
+    __device__ __forceinline__ void row8(int m, int n, const float v[8]) const { store8(c + m * ldc + n, v); }
 };
 
 template <typename T>
@@ -63,6 +74,17 @@ struct EpiBiasGelu {
         if (z) z[m * ldz + n] = from_f32<T>(zz);
         g[m * ldg + n] = from_f32<T>(gelu_f(zz));
     }
+    __device__ __forceinline__ void row8(int m, int n, const float v[8]) const {
+        float b[8], zz[8], gg[8];
+        load8(bias + n, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            zz[i] = v[i] + b[i];
+            gg[i] = gelu_f(zz[i]);
+        }
+        if (z) store8(z + m * ldz + n, zz);
+        store8(g + m * ldg + n, gg);
+    }
 };
 
 template <typename T>
@@ -73,6 +95,13 @@ struct EpiGeluGrad {
     int64_t ldz;
     __device__ __forceinline__ void operator()(int m, int n, float v) const {
         c[m * ldc + n] = from_f32<T>(v * gelu_grad_f(to_f32(z[m * ldz + n])));
+    }
+    __device__ __forceinline__ void row8(int m, int n, const float v[8]) const {
+        float zz[8], o[8];
+        load8(z + m * ldz + n, zz);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = v[i] * gelu_grad_f(zz[i]);
+        store8(c + m * ldc + n, o);
     }
 };
 
@@ -94,6 +123,24 @@ struct EpiQkv {
         size_t off = ((((size_t)bi * nt + head) * seq + p) << dshift) + j;
         T *dst = which == 0 ? q : (which == 1 ? k : v);
         dst[off] = from_f32<T>(val);
+    }
+    // the 8 columns lie in one head of one of Q, K, V (d is a multiple of 8),
+    // so they land on 8 consecutive elements of the destination
+    __device__ __forceinline__ void row8(int m, int n, const float acc[8]) const {
+        float b[8], o[8];
+        load8(bias + n, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = acc[i] + b[i];
+        uint32_t gm = (uint32_t)(row0 + m);
+        uint32_t p = fdiv(gm, bdiv);
+        uint32_t bi = gm - p * bdiv.d;
+        int which = (n >= ht) + (n >= 2 * ht);
+        int c = n - which * ht;
+        int head = c >> dshift;
+        int j = c & ((1 << dshift) - 1);
+        size_t off = ((((size_t)bi * nt + head) * seq + p) << dshift) + j;
+        T *dst = which == 0 ? q : (which == 1 ? k : this->v);
+        store8(dst + off, o);
     }
 };
 
@@ -130,32 +177,26 @@ __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3)) & 7;
 // Loads outside the matrix write zeros to LDS, which masks ragged edges.
 // ---------------------------------------------------------------------------
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, 0, 0, 0);
-}
-
-// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt out of range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One operand tile of ROWS (M or N) x 64 (K) bf16 in LDS: ROWS * 128 bytes.
-template <int ROWS, bool KCONTIG, int NWAVES>
+// One operand tile of ROWS (M or N) x BK (K, 32 or 64) bf16 in LDS:
+// ROWS * BK * 2 bytes.
+template <int ROWS, bool KCONTIG, int NWAVES, int BK>
 struct DlOperand {
-    static constexpr int kBytes = ROWS * 128;
+    static_assert(BK == 32 || BK == 64, "K-tile of 32 or 64");
+    static constexpr int kRowBytes = BK * 2;              // [ROWS][BK] layout: bytes per row
+    static constexpr int kChunks = BK / 8;                // 16-byte chunks per [ROWS][BK] row
+    static constexpr int kBytes = ROWS * kRowBytes;
     static constexpr int kInstr = kBytes / 1024;          // 1 KB per wave-wide load
     static_assert(kInstr % NWAVES == 0, "tile must split evenly over the waves");
     static constexpr int kPerWave = kInstr / NWAVES;      // loads per wave per K-tile
-    static constexpr int kPitch = ROWS * 2;               // row pitch of the [64][ROWS] layout
-    static constexpr int kUnits = ROWS / 8;               // 16-byte units per [64][ROWS] row
+    static constexpr int kPitch = ROWS * 2;               // row pitch of the [BK][ROWS] layout
+    static constexpr int kUnits = ROWS / 8;               // 16-byte units per [BK][ROWS] row
 
+    // chunk swizzle of the [ROWS][BK] layout: the rows that one MFMA fragment
+    // read touches together (same logical chunk) land on distinct banks
+    __device__ static __forceinline__ int swz_row(int r) {
+        if constexpr (BK == 64) return lds_swz(r);
+        else return (r >> 2) & 3;
+    }
     __device__ static __forceinline__ int swz_k(int k) { return (k & 3) * 4 & (kUnits - 1); }
 
     __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char *stage, int mn0, int k0, int MN,
@@ -165,8 +206,8 @@ struct DlOperand {
             const int I = wave * kPerWave + q;
             uint32_t off;
             if constexpr (KCONTIG) {
-                const int row = I * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ lds_swz(row);
+                const int row = I * (1024 / kRowBytes) + lane / kChunks;
+                const int c = (lane % kChunks) ^ swz_row(row);
                 const int gm = mn0 + row, gk = k0 + c * 8;
                 off = (gm < MN && gk < K) ? (uint32_t)((gm * ld + gk) * 2) : kOOB;
             } else {
@@ -186,7 +227,7 @@ struct DlOperand {
         if constexpr (KCONTIG) {
             const int row = base + (lane & 31);
             const int c = kk * 2 + (lane >> 5);
-            return *(const bf16x8 *)(stage + row * 128 + ((c ^ lds_swz(row)) << 4));
+            return *(const bf16x8 *)(stage + row * kRowBytes + ((c ^ swz_row(row)) << 4));
         } else {
             const int L = lane & 15;
             const int mn = base + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
@@ -194,9 +235,7 @@ struct DlOperand {
             const int u = mn >> 3, within = (mn & 7) * 2;
             const char *p0 = stage + k * kPitch + ((u ^ swz_k(k)) << 4) + within;
             const char *p1 = stage + (k + 4) * kPitch + ((u ^ swz_k(k + 4)) << 4) + within;
-            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
-            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
-            u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+            u32x2 a = lds_read_tr16(p0), b = lds_read_tr16(p1);
             return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
         }
     }
@@ -220,23 +259,25 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
     tn = r / rows;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK = 64>
 struct DlCfg {
-    static constexpr int kBM = BM, kBN = BN, kBK = 64, kWM = WAVES_M, kWN = WAVES_N, kStages = STAGES;
+    static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WAVES_M, kWN = WAVES_N, kStages = STAGES;
     static constexpr int kThreads = WAVES_M * WAVES_N * 64;
-    static constexpr int kLds = STAGES * (BM + BN) * 128;
+    static constexpr int kLds = STAGES * (BM + BN) * BK * 2;
 };
 
 template <class C, bool AK, bool BK_, class Epi>
 __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, Epi epi, int gm_rows) {
-    constexpr int BM = C::kBM, BN = C::kBN, S = C::kStages;
+    constexpr int BM = C::kBM, BN = C::kBN, BK = C::kBK, S = C::kStages;
     constexpr int NW = C::kWM * C::kWN;
     constexpr int WTM = BM / C::kWM, WTN = BN / C::kWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
-    using OpA = DlOperand<BM, AK, NW>;
-    using OpB = DlOperand<BN, BK_, NW>;
+    constexpr int KSTEPS = BK / 16;
+    using OpA = DlOperand<BM, AK, NW, BK>;
+    using OpB = DlOperand<BN, BK_, NW, BK>;
     constexpr int STAGE = OpA::kBytes + OpB::kBytes;
     constexpr int LPT = OpA::kPerWave + OpB::kPerWave;  // loads per wave per K-tile
+    static_assert(LPT * (S - 2) < 64, "vmcnt range");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -255,31 +296,38 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int nkt = (g.K + 63) / 64;
+    const int nkt = (g.K + BK - 1) / BK;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
         if (s < nkt) {
-            OpA::issue(ra, smem + s * STAGE, m0, s * 64, g.M, g.K, g.lda, wid, lane);
-            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, s * 64, g.N, g.K, g.ldb, wid, lane);
+            OpA::issue(ra, smem + s * STAGE, m0, s * BK, g.M, g.K, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, s * BK, g.N, g.K, g.ldb, wid, lane);
         }
     }
     for (int kt = 0; kt < nkt; ++kt) {
-        // tile kt must have landed; the S-2 tiles after it may still be in flight
-        if constexpr (S == 3) {
-            if (kt + 1 < nkt) wait_vmcnt<LPT>();
+        // tile kt must have landed; the tiles after it that are already in
+        // flight (at most S-2) may still be pending
+        const int later = min(S - 2, nkt - 1 - kt);
+        if constexpr (S >= 4) {
+            if (later >= 2) wait_vmcnt<LPT * 2 < 64 ? LPT * 2 : 63>();
+            else if (later == 1) wait_vmcnt<LPT>();
+            else wait_vmcnt<0>();
+        } else if constexpr (S == 3) {
+            if (later >= 1) wait_vmcnt<LPT>();
             else wait_vmcnt<0>();
         } else {
             wait_vmcnt<0>();
         }
         __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // no LDS read moves above the barrier
         if (kt + S - 1 < nkt) {
             char *st = smem + ((kt + S - 1) % S) * STAGE;
-            OpA::issue(ra, st, m0, (kt + S - 1) * 64, g.M, g.K, g.lda, wid, lane);
-            OpB::issue(rb, st + OpA::kBytes, n0, (kt + S - 1) * 64, g.N, g.K, g.ldb, wid, lane);
+            OpA::issue(ra, st, m0, (kt + S - 1) * BK, g.M, g.K, g.lda, wid, lane);
+            OpB::issue(rb, st + OpA::kBytes, n0, (kt + S - 1) * BK, g.N, g.K, g.ldb, wid, lane);
         }
         const char *cur = smem + (kt % S) * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < KSTEPS; ++kk) {
             bf16x8 fa[FM], fb[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[i] = OpA::frag(cur, wm * WTM + i * 32, kk, lane);
@@ -291,21 +339,46 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
+        // every wave is done reading this stage before any wave refills it
+        // (the refill is issued after the next iteration's barrier)
     }
 
+    // Epilogue through LDS, 32 tile rows at a time: the waves holding those
+    // rows write their fp32 accumulators (32x32 layout: register v of lane l
+    // is row 8*(v/4) + 4*(l/32) + v%4, column l%32 of a block) into a
+    // [32][BN + 8] buffer, then all threads apply the epilogue to 8
+    // consecutive columns each with vector loads and stores.
+    constexpr int EP = BN + 8;  // row pitch in floats: the two half-waves' rows land 32 banks apart
+    float *ep = (float *)smem;
+    wait_vmcnt<0>();
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int c = 0; c < BM / 32; ++c) {
+        if (wm == c / FM) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            int col = n0 + wn * WTN + j * 32 + (lane & 31);
-            if (col < g.N) {
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    if (row < g.M) epi(row, col, acc[i][j][v]);
+                    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ep[r * EP + wn * WTN + j * 32 + (lane & 31)] = acc[c % FM][j][v];
                 }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = tid; q < 32 * BN / 8; q += C::kThreads) {
+            const int r = q / (BN / 8), cv = q % (BN / 8);
+            const int gm = m0 + c * 32 + r, gn = n0 + cv * 8;
+            if (gm < g.M && gn < g.N) {
+                float v[8];
+                const float4 a = *(const float4 *)(ep + r * EP + cv * 8);
+                const float4 b = *(const float4 *)(ep + r * EP + cv * 8 + 4);
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+                epi.row8(gm, gn, v);
             }
         }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -383,19 +456,19 @@ using Dl128 = DlCfg<128, 128, 2, 2, 2>;  // 64 KB of LDS: two workgroups per com
 using Dl256 = DlCfg<256, 256, 2, 2, 2>;  // 128 KB of LDS: one workgroup per compute unit
 
 // The 256x256 tile reads half the LDS bytes per MFMA but runs one workgroup
-// per compute unit; measured on MI355X it wins only when there are at least
-// two full rounds of its tiles over the 256 compute units (8192^3,
-// 4096x24576x6144); every product of the GPT-3 175B shard runs faster on the
-// 128x128 tile.
-static bool use_256(int M, int N) {
+// per compute unit; measured on MI355X it wins only for products whose
+// operands are both K-contiguous and that give at least two full rounds of
+// its tiles over the 256 compute units (8192^3, 4096x24576x6144); every
+// product of the GPT-3 175B shard runs faster on the 128x128 tile.
+static bool use_256(int M, int N, bool ak, bool bk) {
     const double tiles256 = (double)((M + 255) / 256) * ((N + 255) / 256);
-    return tiles256 >= 512;
+    return ak && bk && tiles256 >= 512;
 }
 
 template <typename T, bool AK, bool BK_, class E>
 static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        if (use_256(g.M, g.N)) return launch_dl<Dl256, AK, BK_>(g, epi, st);
+        if (use_256(g.M, g.N, AK, BK_)) return launch_dl<Dl256, AK, BK_>(g, epi, st);
         return launch_dl<Dl128, AK, BK_>(g, epi, st);
     } else {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
@@ -463,7 +536,9 @@ hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const Epi
     static const char *kEpiName[] = {"store_f32", "accum_f32", "store", "bias_gelu", "gelu_grad", "qkv"};
     const char *lay = A.kcontig ? (B.kcontig ? "nt" : "nn") : "tn";
     char name[64];
-    snprintf(name, sizeof name, "gemm_%s_%s_%s", dt == DType::BF16 ? "bf16" : "f32", lay, kEpiName[(int)kind]);
+    const char *tile = dt == DType::BF16 ? (use_256(M, N, A.kcontig, B.kcontig) ? "_256" : "_128") : "";
+    snprintf(name, sizeof name, "gemm_%s%s_%s_%s", dt == DType::BF16 ? "bf16" : "f32", tile, lay,
+             kEpiName[(int)kind]);
     const double mn = (double)M * N;
     double out_b = mn * es;
     if (kind == Epi::StoreF32) out_b = mn * 4;

@@ -22,27 +22,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxVec = 8;  // 8 vectors of 8 elements per thread: h <= 16384
 
-__device__ __forceinline__ void load8(const float *p, float o[8]) {
-    float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
-    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-}
-__device__ __forceinline__ void load8(const bf16 *p, float o[8]) {
-    u32x4 w = *(const u32x4 *)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { o[2 * i] = bf_lo(w[i]); o[2 * i + 1] = bf_hi(w[i]); }
-}
-__device__ __forceinline__ void store8(float *p, const float v[8]) {
-    *(float4 *)p = float4{v[0], v[1], v[2], v[3]};
-    *(float4 *)(p + 4) = float4{v[4], v[5], v[6], v[7]};
-}
-__device__ __forceinline__ void store8(bf16 *p, const float v[8]) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf2(v[2 * i], v[2 * i + 1]);
-    *(u32x4 *)p = w;
-}
-
 // Sum over the 256 threads of a block; every thread gets the result.
 __device__ __forceinline__ float block_sum(float v, float *red) {
     v = wave_sum(v);
