@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the per-slice and cube figures")
     ap.add_argument("--profile-only", action="store_true",
                     help="warm up and run the timed whole-partition steps only (for rocprofv3)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="with --profile-only: also run one plain streaming kernel over this many MiB "
+                         "(read once, written once), the calibration of rocprofv3's HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU's shard: this build has no multi-GPU path "
@@ -218,6 +221,14 @@ def main():
     step = make_step(layer, bufs, "whole")
     ms, wall_ms, recs = time_steps(torch, step, args.steps, args.warmup, trace=not args.profile_only)
     if args.profile_only:
+        if args.copy_mib > 0:
+            n = args.copy_mib * (1 << 20) // 4
+            src = torch.full((n,), 7, dtype=torch.int32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            torch.bitwise_not(src, out=dst)
+            torch.cuda.synchronize()
+            del src, dst
         print(json.dumps(dict(config=shape.name, ms_per_step=ms)))
         return
     kt = kernel_table(recs, args.steps)
@@ -227,9 +238,15 @@ def main():
     dom_fl = sum(r[1] for r in dom_recs)
     dom_ms = sum(r[3] for r in dom_recs)
     achieved = dom_fl / (dom_ms * 1e-3) / 1e12
+    # measured HBM bytes per launch of the dominant kernel, from the committed
+    # counter summary when it was taken on the current sources (else null)
+    from token_transformer_layer_amd import profiling
+    traffic = profiling.load_traffic(os.path.join(ROOT, "profiles"), dom_name, shape.name)
     roofline = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=None, kernel=dom_name,
-                    launches=len(dom_recs), avg_launch_ms=round(dom_ms / len(dom_recs), 5))
+                    frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=dom_name,
+                    launches=len(dom_recs), avg_launch_ms=round(dom_ms / len(dom_recs), 5),
+                    algorithmic_bytes_per_launch=round(sum(r[2] for r in dom_recs) / len(dom_recs)),
+                    traffic_unit="HBM bytes per launch")
     traced_ms = sum(r[3] for r in recs) / args.steps
     gemm_ms = sum(r[3] for r in recs if r[0].startswith("gemm")) / args.steps
     gemm_fl = sum(r[1] for r in recs if r[0].startswith("gemm")) / args.steps

@@ -1,0 +1,24 @@
+"""The rocprofv3 summary helpers: kernel-symbol naming and the staleness
+check of committed traffic figures (host only)."""
+import json
+
+from token_transformer_layer_amd import profiling
+
+
+def test_gemm_symbols_map_to_trace_names():
+    m = "_ZN3tpk19gemm_bf16_dl_kernelINS_5DlCfgILi128ELi128ELi2ELi2ELi2ELi64EEELb0ELb0ENS_11EpiStoreF32IDF16bEEEEvNS_8GemmArgsET2_i"
+    assert profiling.trace_name(m) == "gemm_bf16_128_tn_store_f32"
+    d = "void tpk::gemm_bf16_dl_kernel<tpk::DlCfg<256, 256, 2, 2, 2, 64>, true, true, tpk::EpiQkv<__bf16> >(tpk::GemmArgs)"
+    assert profiling.trace_name(d) == "gemm_bf16_256_nt_qkv"
+    assert profiling.trace_name("_ZN3tpk12_GLOBAL__N_113ln_bwd_kernelIDF16bEEviiiPKf") == "ln_bwd_kernel<bf16>"
+
+
+def test_traffic_is_dropped_when_sources_change(tmp_path):
+    k, w = "gemm_bf16_128_tn_store_f32", "wl"
+    rec = dict(kernel=k, workload=w, bytes_per_launch=123, source_sha256=profiling.source_hash(k))
+    (tmp_path / ("traffic_%s_%s.json" % (k, w))).write_text(json.dumps(rec))
+    assert profiling.load_traffic(str(tmp_path), k, w) == 123
+    rec["source_sha256"] = "0" * 64
+    (tmp_path / ("traffic_%s_%s.json" % (k, w))).write_text(json.dumps(rec))
+    assert profiling.load_traffic(str(tmp_path), k, w) is None
+    assert profiling.load_traffic(str(tmp_path), k, "other") is None
