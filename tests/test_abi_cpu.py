@@ -168,3 +168,10 @@ def test_last_error_names_the_problem():
     c = cfg_of(synth.CONFIGS["tiny-fp32"])
     _status(lambda: _fwd(c, abi.make_partition([100]), 0, 1))
     assert b"seq_len" in abi.lib().tp_last_error()
+
+
+def test_force_tile_range():
+    for bad in (-2, 4, 100):
+        assert _status(lambda: abi.tp_gemm_force_tile(bad)) == abi.TP_EINVAL
+    abi.tp_gemm_force_tile(3)
+    abi.tp_gemm_force_tile(-1)

@@ -75,6 +75,21 @@ def test_split_weight_gradients(shape):
     _check_shard(shape, "perturbed", "per-slice", rank=1, split_wgrad=True)
 
 
+@pytest.mark.parametrize("tile", [0, 1, 2, 3], ids=["t128", "p128", "t256x128", "t256"])
+@pytest.mark.parametrize("shape", [RAGGED_D64, RAGGED_D128], ids=lambda s: s.name)
+def test_forced_gemm_tiles(shape, tile):
+    """Every tile configuration of the bf16 products, forced on every product
+    of a ragged shard (rows, widths and reductions that are not multiples of
+    any tile), whole-partition and split-weight-gradient schedules."""
+    from token_transformer_layer_amd import abi
+    abi.tp_gemm_force_tile(tile)
+    try:
+        _check_shard(shape, "perturbed", "whole", rank=1)
+        _check_shard(shape, "perturbed", "per-slice", rank=0, split_wgrad=True)
+    finally:
+        abi.tp_gemm_force_tile(-1)
+
+
 def test_full_size_split_weight_gradients():
     """The benchmark's per-slice schedule at the GPT-3 175B shard."""
     _check_shard(synth.CONFIGS["gpt3-175b-t8"], "standard", "per-slice", rank=0, full=False, split_wgrad=True)

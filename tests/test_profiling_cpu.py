@@ -8,8 +8,12 @@ from token_transformer_layer_amd import profiling
 def test_gemm_symbols_map_to_trace_names():
     m = "_ZN3tpk19gemm_bf16_dl_kernelINS_5DlCfgILi128ELi128ELi2ELi2ELi2ELi64EEELb0ELb0ENS_11EpiStoreF32IDF16bEEEEvNS_8GemmArgsET2_i"
     assert profiling.trace_name(m) == "gemm_bf16_128_tn_store_f32"
-    d = "void tpk::gemm_bf16_dl_kernel<tpk::DlCfg<256, 256, 2, 2, 2, 64>, true, true, tpk::EpiQkv<__bf16> >(tpk::GemmArgs)"
+    d = "void tpk::gemm_bf16_pp_kernel<tpk::DlCfg<256, 256, 2, 2, 4, 32, 1>, true, true, tpk::EpiQkv<__bf16> >(tpk::GemmArgs)"
     assert profiling.trace_name(d) == "gemm_bf16_256_nt_qkv"
+    p = "_ZN3tpk19gemm_bf16_pp_kernelINS_5DlCfgILi256ELi128ELi2ELi2ELi3ELi32ELi2EEELb0ELb0ENS_11EpiStoreF32IDF16bEEEEvNS_8GemmArgsET2_i"
+    assert profiling.trace_name(p) == "gemm_bf16_256x128_tn_store_f32"
+    p = "_ZN3tpk19gemm_bf16_pp_kernelINS_5DlCfgILi128ELi128ELi2ELi2ELi2ELi64ELi1EEELb1ELb0ENS_11EpiStoreF32IDF16bEEEEvNS_8GemmArgsET2_i"
+    assert profiling.trace_name(p) == "gemm_bf16_p128_nn_store_f32"
     assert profiling.trace_name("_ZN3tpk12_GLOBAL__N_113ln_bwd_kernelIDF16bEEviiiPKf") == "ln_bwd_kernel<bf16>"
 
 

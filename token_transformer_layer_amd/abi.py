@@ -20,7 +20,7 @@ TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1, TP_BWD_MLP_DATA, TP_BWD_ATTN_DATA, TP_BWD_W
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_trace_enable",
-            "tp_trace_read", "tp_last_error"]
+            "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
 
 
 class TPError(RuntimeError):
@@ -97,6 +97,8 @@ def lib():
     L.tp_trace_enable.restype = None
     L.tp_trace_read.argtypes = [P(tp_trace_record), i32]
     L.tp_trace_read.restype = i32
+    L.tp_gemm_force_tile.argtypes = [i32]
+    L.tp_gemm_force_tile.restype = ctypes.c_int
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -106,6 +108,11 @@ def lib():
 def _check(status):
     if status != TP_OK:
         raise TPError(status, lib().tp_last_error().decode())
+
+
+def tp_gemm_force_tile(tile):
+    """-1: the library picks the bf16 product tiles per shape; 0..3 force one."""
+    _check(lib().tp_gemm_force_tile(int(tile)))
 
 
 def make_partition(lengths):

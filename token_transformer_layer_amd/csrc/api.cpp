@@ -180,6 +180,13 @@ size_t tp_shard_scratch_bytes(const tp_shard_cfg *cfg) {
 
 const char *tp_last_error(void) { return g_err.c_str(); }
 
+tp_status tp_gemm_force_tile(int32_t tile) {
+    if (tile < -1 || tile > 3) return fail(TP_EINVAL, "tile must be -1 (automatic) or 0..3");
+    tpk::gemm_force_tile(tile);
+    g_err.clear();
+    return TP_OK;
+}
+
 tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part,
                              int32_t slice_begin, int32_t slice_end, int32_t phase, const void *in,
                              float *partial_out, tp_kv_cache *kv, void *saved, void *scratch, void *stream) {

@@ -46,6 +46,10 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt with only the LDS/scalar-memory counter drained (vmcnt and
+// expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); }
+
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
 // i % 4 of the 8-byte pieces addressed by lanes i/4 + 4j (j = 0..3), in j
 // order; with lane L addressing row r0 + L/4, columns c0 + 4(L%4)..+3 of a

@@ -22,6 +22,8 @@
 
 #include "common.h"
 #include "kernels.h"
+#include <atomic>
+
 #include "trace.h"
 
 namespace tpk {
@@ -259,12 +261,55 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int g
     tn = r / rows;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK = 64>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int BK = 64, int OCC = 1>
 struct DlCfg {
     static constexpr int kBM = BM, kBN = BN, kBK = BK, kWM = WAVES_M, kWN = WAVES_N, kStages = STAGES;
+    static constexpr int kOcc = OCC;  // workgroups per compute unit the register budget is sized for
     static constexpr int kThreads = WAVES_M * WAVES_N * 64;
     static constexpr int kLds = STAGES * (BM + BN) * BK * 2;
 };
+
+// Epilogue through LDS, 32 tile rows at a time: the waves holding those
+// rows write their fp32 accumulators (32x32 layout: register v of lane l is
+// row 8*(v/4) + 4*(l/32) + v%4, column l%32 of a block) into a [32][BN + 8]
+// buffer, then all threads apply the epilogue to 8 consecutive columns each
+// with vector loads and stores.  The caller has synchronised the workgroup
+// (the LDS stages are free).
+template <class C, int FM, int FN, class Epi>
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[FM][FN], char *smem, Epi &epi, const GemmArgs &g, int m0,
+                                           int n0, int wm, int wn, int tid, int lane) {
+    constexpr int BM = C::kBM, BN = C::kBN;
+    constexpr int WTN = BN / C::kWN;
+    constexpr int EP = BN + 8;  // row pitch in floats: the two half-waves' rows land 32 banks apart
+    float *ep = (float *)smem;
+#pragma unroll
+    for (int c = 0; c < BM / 32; ++c) {
+        if (wm == c / FM) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                    ep[r * EP + wn * WTN + j * 32 + (lane & 31)] = acc[c % FM][j][v];
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = tid; q < 32 * BN / 8; q += C::kThreads) {
+            const int r = q / (BN / 8), cv = q % (BN / 8);
+            const int gm = m0 + c * 32 + r, gn = n0 + cv * 8;
+            if (gm < g.M && gn < g.N) {
+                float v[8];
+                const float4 a = *(const float4 *)(ep + r * EP + cv * 8);
+                const float4 b = *(const float4 *)(ep + r * EP + cv * 8 + 4);
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+                epi.row8(gm, gn, v);
+            }
+        }
+        __syncthreads();
+    }
+}
 
 template <class C, bool AK, bool BK_, class Epi>
 __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, Epi epi, int gm_rows) {
@@ -343,42 +388,141 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
         // (the refill is issued after the next iteration's barrier)
     }
 
-    // Epilogue through LDS, 32 tile rows at a time: the waves holding those
-    // rows write their fp32 accumulators (32x32 layout: register v of lane l
-    // is row 8*(v/4) + 4*(l/32) + v%4, column l%32 of a block) into a
-    // [32][BN + 8] buffer, then all threads apply the epilogue to 8
-    // consecutive columns each with vector loads and stores.
-    constexpr int EP = BN + 8;  // row pitch in floats: the two half-waves' rows land 32 banks apart
-    float *ep = (float *)smem;
     wait_vmcnt<0>();
     __syncthreads();
+    store_tile<C>(acc, smem, epi, g, m0, n0, wm, wn, tid, lane);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel, software-pipelined
+//
+// Same LDS layout and direct-to-LDS staging as above, with the work of each
+// wave ordered so that the matrix cores never wait on LDS: the fragments of
+// k-step ks+1 are read into a second register set while the MFMAs of k-step
+// ks run, and the hand-over between K-tiles (wait for the next tile's DMA,
+// workgroup barrier, refill of the stage just consumed) happens before the
+// MFMAs of a tile's last k-step, so those MFMAs cover the barrier and the
+// first fragment reads of the next tile.  All S stages are filled ahead; the
+// stage of tile kt is refilled with tile kt + S once every wave has its last
+// fragments of tile kt in registers.  Scheduling-group barriers interleave
+// the LDS reads (and the DMA issues) with the MFMAs.
+// ---------------------------------------------------------------------------
+
+template <int NR, int NM, int NV>
+__device__ __forceinline__ void sched_interleave() {
+    // NM MFMAs with NR LDS reads and NV VMEM issues spread between them
+    constexpr int RPM = (NR + NM - 1) / NM;
+    constexpr int VPM = (NV + NM - 1) / NM;
 #pragma unroll
-    for (int c = 0; c < BM / 32; ++c) {
-        if (wm == c / FM) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                    ep[r * EP + wn * WTN + j * 32 + (lane & 31)] = acc[c % FM][j][v];
-                }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = tid; q < 32 * BN / 8; q += C::kThreads) {
-            const int r = q / (BN / 8), cv = q % (BN / 8);
-            const int gm = m0 + c * 32 + r, gn = n0 + cv * 8;
-            if (gm < g.M && gn < g.N) {
-                float v[8];
-                const float4 a = *(const float4 *)(ep + r * EP + cv * 8);
-                const float4 b = *(const float4 *)(ep + r * EP + cv * 8 + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-                epi.row8(gm, gn, v);
-            }
-        }
-        __syncthreads();
+    for (int i = 0; i < NM; ++i) {
+        if constexpr (RPM > 0) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        if constexpr (VPM > 0) __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
+}
+
+template <class C, bool AK, bool BK_, class Epi>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kOcc * C::kThreads / 256)))
+void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
+    constexpr int BM = C::kBM, BN = C::kBN, BK = C::kBK, S = C::kStages;
+    constexpr int NW = C::kWM * C::kWN;
+    constexpr int WTM = BM / C::kWM, WTN = BN / C::kWN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int KSTEPS = BK / 16;
+    static_assert(KSTEPS % 2 == 0, "register sets alternate by k-step parity");
+    using OpA = DlOperand<BM, AK, NW, BK>;
+    using OpB = DlOperand<BN, BK_, NW, BK>;
+    constexpr int STAGE = OpA::kBytes + OpB::kBytes;
+    constexpr int LPT = OpA::kPerWave + OpB::kPerWave;  // DMA issues per wave per K-tile
+    constexpr int NREAD = (AK ? 1 : 2) * FM + (BK_ ? 1 : 2) * FN;
+    static_assert(LPT * (S - 1) < 64, "vmcnt range");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / C::kWN, wn = wid % C::kWN;
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, gm_rows, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, g.a_bytes);
+    __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, g.b_bytes);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    const int nkt = (g.K + BK - 1) / BK;
+    if (nkt > 0) {
+        // Stages are always filled S tiles ahead: loads past the end of K
+        // read as zeros (their stages are never consumed), so the number of
+        // loads in flight is the same at every hand-over and the loop body
+        // has no branches for the scheduler to stop at.
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            OpA::issue(ra, smem + s * STAGE, m0, s * BK, g.M, g.K, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, s * BK, g.N, g.K, g.ldb, wid, lane);
+        }
+        wait_vmcnt<LPT * (S - 1)>();  // tile 0 has landed
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+        bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[0][i] = OpA::frag(smem, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[0][j] = OpB::frag(smem + OpA::kBytes, wn * WTN + j * 32, 0, lane);
+
+        auto mfmas = [&](int set) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+        };
+        auto reads = [&](const char *stage, int kk, int set) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[set][i] = OpA::frag(stage, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) fb[set][j] = OpB::frag(stage + OpA::kBytes, wn * WTN + j * 32, kk, lane);
+        };
+        // k-steps 0 .. KSTEPS-2 of a tile: next k-step's fragments are read
+        // while this one's MFMAs run
+        auto inner = [&](const char *cur) {
+#pragma unroll
+            for (int kk = 0; kk + 1 < KSTEPS; ++kk) {
+                reads(cur, kk + 1, (kk + 1) & 1);
+                mfmas(kk & 1);
+                sched_interleave<NREAD, FM * FN, 0>();
+            }
+        };
+
+        int stage = 0;
+        for (int kt = 0; kt + 1 < nkt; ++kt) {
+            const char *cur = smem + stage * STAGE;
+            inner(cur);
+            // hand-over to tile kt + 1 (last k-step's fragments are in
+            // registers once lgkmcnt drains; tiles kt + 2 .. kt + S - 1 may
+            // still be in flight)
+            wait_lgkm0();
+            wait_vmcnt<LPT * (S - 2)>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            OpA::issue(ra, smem + stage * STAGE, m0, (kt + S) * BK, g.M, g.K, g.lda, wid, lane);
+            OpB::issue(rb, smem + stage * STAGE + OpA::kBytes, n0, (kt + S) * BK, g.N, g.K, g.ldb, wid, lane);
+            stage = stage + 1 == S ? 0 : stage + 1;
+            reads(smem + stage * STAGE, 0, 0);
+            mfmas((KSTEPS - 1) & 1);
+            sched_interleave<NREAD, FM * FN, LPT>();
+        }
+        inner(smem + stage * STAGE);
+        mfmas((KSTEPS - 1) & 1);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    store_tile<C>(acc, smem, epi, g, m0, n0, wm, wn, tid, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,23 +596,79 @@ static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
     return hipGetLastError();
 }
 
-using Dl128 = DlCfg<128, 128, 2, 2, 2>;  // 64 KB of LDS: two workgroups per compute unit
-using Dl256 = DlCfg<256, 256, 2, 2, 2>;  // 128 KB of LDS: one workgroup per compute unit
+template <class C, bool AK, bool BK_, class E>
+static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_pp_kernel<C, AK, BK_, E>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
+    hipLaunchKernelGGL((gemm_bf16_pp_kernel<C, AK, BK_, E>), dim3(tiles), dim3(C::kThreads), C::kLds, st, g, epi, 4);
+    return hipGetLastError();
+}
 
-// The 256x256 tile reads half the LDS bytes per MFMA but runs one workgroup
-// per compute unit; measured on MI355X it wins only for products whose
-// operands are both K-contiguous and that give at least two full rounds of
-// its tiles over the 256 compute units (8192^3, 4096x24576x6144); every
-// product of the GPT-3 175B shard runs faster on the 128x128 tile.
-static bool use_256(int M, int N, bool ak, bool bk) {
-    const double tiles256 = (double)((M + 255) / 256) * ((N + 255) / 256);
-    return ak && bk && tiles256 >= 512;
+using Dl128 = DlCfg<128, 128, 2, 2, 2>;              // 64 KB of LDS: two workgroups per compute unit
+using Pp256 = DlCfg<256, 256, 2, 2, 4, 32>;          // 128 KB, three K-tiles in flight, one workgroup
+using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups per compute unit
+
+// Tile configurations, chosen per product shape from measurements on MI355X
+// (TFLOP/s of each candidate on the GPT-3 175B t=8 shard's products and on
+// large square products).  A 128x128 tile needs 64 bytes of operand per
+// clock per compute unit to keep the matrix cores busy, close to what the
+// load path delivers, so larger tiles win wherever there are enough of them
+// to fill the 256 compute units; the plain (non-pipelined) 128x128 kernel
+// is the best fit for short reductions and narrow outputs.
+enum class Tile { Dl128, Pp128, Pp256x128, Pp256 };
+
+static std::atomic<int> g_force_tile{-1};
+
+void gemm_force_tile(int tile) { g_force_tile.store(tile); }
+
+static Tile pick_tile(int M, int N, int K, bool ak, bool bk) {
+    const int forced = g_force_tile.load(std::memory_order_relaxed);
+    if (forced >= 0) return (Tile)forced;
+    const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+    const long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);
+    if (ak && bk) {
+        // forward form: long reductions with at least half a round of
+        // 256x256 tiles run best on them (QKV, FC1, large squares)
+        if (K >= 6144 && t256 >= 128 && (t256 >= 512 || t256 < 256)) return Tile::Pp256;
+        if (K >= 16384) return Tile::Pp128;
+        return Tile::Dl128;
+    }
+    if (ak && !bk) {
+        // input-gradient form
+        if (K >= 12288 && N >= 4096 && t256x128 >= 256) return Tile::Pp256x128;
+        if (K >= 6144 && N >= 8192) return Tile::Pp128;
+        return Tile::Dl128;
+    }
+    // weight-gradient form: wide outputs on both sides
+    if (M >= 4096 && N >= 4096 && t256x128 >= 512) return Tile::Pp256x128;
+    return Tile::Dl128;
+}
+
+static const char *tile_name(Tile t) {
+    switch (t) {
+    case Tile::Dl128: return "128";
+    case Tile::Pp128: return "p128";
+    case Tile::Pp256x128: return "256x128";
+    case Tile::Pp256: return "256";
+    }
+    return "?";
 }
 
 template <typename T, bool AK, bool BK_, class E>
 static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
-        if (use_256(g.M, g.N, AK, BK_)) return launch_dl<Dl256, AK, BK_>(g, epi, st);
+        switch (pick_tile(g.M, g.N, g.K, AK, BK_)) {
+        case Tile::Pp256: return launch_pp<Pp256, AK, BK_>(g, epi, st);
+        case Tile::Pp256x128: return launch_pp<Pp256x128, AK, BK_>(g, epi, st);
+        case Tile::Pp128: return launch_pp<Dl128, AK, BK_>(g, epi, st);
+        case Tile::Dl128: break;
+        }
         return launch_dl<Dl128, AK, BK_>(g, epi, st);
     } else {
         dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
@@ -536,9 +736,11 @@ hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const Epi
     static const char *kEpiName[] = {"store_f32", "accum_f32", "store", "bias_gelu", "gelu_grad", "qkv"};
     const char *lay = A.kcontig ? (B.kcontig ? "nt" : "nn") : "tn";
     char name[64];
-    const char *tile = dt == DType::BF16 ? (use_256(M, N, A.kcontig, B.kcontig) ? "_256" : "_128") : "";
-    snprintf(name, sizeof name, "gemm_%s%s_%s_%s", dt == DType::BF16 ? "bf16" : "f32", tile, lay,
-             kEpiName[(int)kind]);
+    if (dt == DType::BF16)
+        snprintf(name, sizeof name, "gemm_bf16_%s_%s_%s", tile_name(pick_tile(M, N, K, A.kcontig, B.kcontig)), lay,
+                 kEpiName[(int)kind]);
+    else
+        snprintf(name, sizeof name, "gemm_f32_%s_%s", lay, kEpiName[(int)kind]);
     const double mn = (double)M * N;
     double out_b = mn * es;
     if (kind == Epi::StoreF32) out_b = mn * 4;

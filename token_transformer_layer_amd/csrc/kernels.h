@@ -42,6 +42,8 @@ struct EpiArgs {
 
 hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const EpiArgs &e,
                 hipStream_t st);
+// -1: tile configuration chosen per shape; 0..3: forced (see tp_gemm_force_tile)
+void gemm_force_tile(int tile);
 
 // LayerNorm forward over rows [0, rows): u = LN(x) * g + b; mean/rstd fp32.
 hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, const void *g,

@@ -57,19 +57,29 @@ def source_hash(trace_name):
     return h.hexdigest()
 
 
+def _tile_tag(pp, bm, bn):
+    """The library's name for a tile configuration (see pick_tile in gemm.hip)."""
+    if bm == bn == "128":
+        return "p128" if pp else "128"
+    return bm if bm == bn else "%sx%s" % (bm, bn)
+
+
 def trace_name(symbol):
     """The library's trace name for a kernel symbol as rocprofv3 reports it
     (mangled or demangled); symbols it does not know pass through, shortened."""
     s = symbol.strip()
-    if "gemm_bf16_dl_kernel" in s:
+    if "gemm_bf16_dl_kernel" in s or "gemm_bf16_pp_kernel" in s:
+        pp = "gemm_bf16_pp_kernel" in s
         mm = re.search(r"DlCfgILi(\d+)ELi(\d+)E.*?EEELb(\d)ELb(\d)ENS_\d+(\w+?)I", s)
         if mm:
-            lay = _LAYOUT[(mm.group(3), mm.group(4))]
-            return "gemm_bf16_%s_%s_%s" % (mm.group(1), lay, _EPI.get(mm.group(5), mm.group(5)))
-        mm = re.search(r"DlCfg<(\d+), (\d+),.*?>, (true|false), (true|false), tpk::(?:\(anonymous namespace\)::)?(\w+)<", s)
-        if mm:
+            bm, bn, key, epi = mm.group(1), mm.group(2), (mm.group(3), mm.group(4)), mm.group(5)
+        else:
+            mm = re.search(r"DlCfg<(\d+), (\d+),.*?>, (true|false), (true|false), tpk::(?:\(anonymous namespace\)::)?(\w+)<", s)
+        if mm and not mm.group(3).isdigit():
+            bm, bn, epi = mm.group(1), mm.group(2), mm.group(5)
             key = ("1" if mm.group(3) == "true" else "0", "1" if mm.group(4) == "true" else "0")
-            return "gemm_bf16_%s_%s_%s" % (mm.group(1), _LAYOUT[key], _EPI.get(mm.group(5), mm.group(5)))
+        if mm:
+            return "gemm_bf16_%s_%s_%s" % (_tile_tag(pp, bm, bn), _LAYOUT[key], _EPI.get(epi, epi))
     mm = re.match(r"_ZN3tpk(?:12_GLOBAL__N_1)?(\d+)", s)
     if mm:  # mangled name in the library's namespace: the kernel's own name
         n = int(mm.group(1))
