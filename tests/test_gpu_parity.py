@@ -90,6 +90,21 @@ def test_forced_gemm_tiles(shape, tile):
         abi.tp_gemm_force_tile(-1)
 
 
+WIDE = [
+    # hidden widths that give the LayerNorm kernels 4, 7 and 8 vectors of 8
+    # columns per thread, with and without the next-row prefetch
+    LayerShape("wide-8192-bf16", 8192, 64, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2011),
+    LayerShape("wide-14336-bf16", 14336, 112, 128, 1792, 16, 1, 24, (10, 14), "bf16", seed=2012),
+    LayerShape("wide-16384-bf16", 16384, 128, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2013),
+    LayerShape("wide-12288-f32", 12288, 96, 128, 1536, 16, 1, 16, (7, 9), "f32", seed=2014),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: s.name)
+def test_wide_hidden(shape):
+    _check_shard(shape, "perturbed", "per-slice", rank=3, full=False)
+
+
 def test_full_size_split_weight_gradients():
     """The benchmark's per-slice schedule at the GPT-3 175B shard."""
     _check_shard(synth.CONFIGS["gpt3-175b-t8"], "standard", "per-slice", rank=0, full=False, split_wgrad=True)

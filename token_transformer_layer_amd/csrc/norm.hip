@@ -83,61 +83,130 @@ __global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, cons
 }
 
 // Rows [blockIdx.x * rpb, ...): dx = resid + rstd (gg - mean(gg) - xhat mean(gg xhat))
-// with gg = du * gamma; per-block partial sums of du * xhat and du go to
-// partials[block][0][:] and partials[block][1][:].
+// with gg = du * gamma; the block's sums of du * xhat and du over its rows go
+// to partials[block][0][:] and partials[block][1][:].  Each thread owns NV
+// vectors of 8 columns (column vector c = threadIdx.x + i * 256) and keeps
+// its gamma, its parameter-gradient sums and the next row's inputs in
+// registers: the loads of row r + 1 are in flight while row r is reduced and
+// written.
+// 8 consecutive elements as loaded: packed bf16, or fp32.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    u32x4 w;
+    __device__ __forceinline__ void load(const bf16 *p) { w = *(const u32x4 *)p; }
+    __device__ __forceinline__ float operator[](int j) const { return j & 1 ? bf_hi(w[j >> 1]) : bf_lo(w[j >> 1]); }
+};
+template <> struct Raw8<float> {
+    float v[8];
+    __device__ __forceinline__ void load(const float *p) { load8(p, v); }
+    __device__ __forceinline__ float operator[](int j) const { return v[j]; }
+};
+
 template <typename T>
+struct LnRow {
+    // one thread's share of a row: du fp32, x and resid as stored
+    float du[8];
+    Raw8<T> x, res;
+};
+
+template <typename T, int NV>
 __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(int rows, int h, int rpb, const float *__restrict__ du,
                                                           const T *__restrict__ resid, const T *__restrict__ x,
                                                           const T *__restrict__ g, const float *__restrict__ mean,
                                                           const float *__restrict__ rstd, T *__restrict__ dx,
                                                           float *__restrict__ partials) {
-    extern __shared__ float accs[];  // [2][h]
-    __shared__ float red[4];
+    __shared__ float red[2][2][4];
     const int nv = h >> 3;
-    for (int c = threadIdx.x; c < 2 * h; c += kThreads) accs[c] = 0.f;
-    __syncthreads();
     const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
-    for (int row = r0; row < r1; ++row) {
-        const float mu = mean[row], rs = rstd[row];
-        float dv[kMaxVec][8], xh[kMaxVec][8];
-        float s1 = 0.f, s2 = 0.f;
+    float gg[NV][8], adg[NV][8], adb[NV][8];
 #pragma unroll
-        for (int i = 0; i < kMaxVec; ++i) {
-            int c = threadIdx.x + i * kThreads;
+    for (int i = 0; i < NV; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) adg[i][j] = adb[i][j] = 0.f;
+        if (c < nv) load8(g + c * 8, gg[i]);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; ++j) gg[i][j] = 0.f;
+    }
+    LnRow<T> cur[NV], nxt[NV];
+    auto load_row = [&](int row, LnRow<T> (&d)[NV]) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = threadIdx.x + i * kThreads;
             if (c < nv) {
-                float gg[8];
-                load8(du + (size_t)row * h + c * 8, dv[i]);
-                load8(x + (size_t)row * h + c * 8, xh[i]);
-                load8(g + c * 8, gg);
+                load8(du + (size_t)row * h + c * 8, d[i].du);
+                d[i].x.load(x + (size_t)row * h + c * 8);
+                d[i].res.load(resid + (size_t)row * h + c * 8);
+            }
+        }
+    };
+    // the next row is prefetched while the register budget allows (h up to
+    // 14336 in bf16, 10240 in fp32, at one wave per SIMD)
+    constexpr bool kPrefetch = NV * (sizeof(T) == 2 ? 1 : 5) <= (sizeof(T) == 2 ? 7 : 25);
+    if (kPrefetch && r0 < r1) load_row(r0, cur);
+    for (int row = r0; row < r1; ++row) {
+        if constexpr (kPrefetch) {
+            if (row + 1 < r1) load_row(row + 1, nxt);
+        } else {
+            load_row(row, cur);
+        }
+        const float mu = mean[row], rs = rstd[row];
+        float s1 = 0.f, s2 = 0.f;
+        float xh[NV][8];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = threadIdx.x + i * kThreads;
+            if (c < nv) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    xh[i][j] = (xh[i][j] - mu) * rs;
-                    float gd = dv[i][j] * gg[j];
+                    xh[i][j] = (cur[i].x[j] - mu) * rs;
+                    const float gd = cur[i].du[j] * gg[i][j];
                     s1 += gd;
                     s2 += gd * xh[i][j];
-                    accs[c * 8 + j] += dv[i][j] * xh[i][j];
-                    accs[h + c * 8 + j] += dv[i][j];
+                    adg[i][j] += cur[i].du[j] * xh[i][j];
+                    adb[i][j] += cur[i].du[j];
                 }
             }
         }
-        const float m1 = block_sum(s1, red) / (float)h;
-        const float m2 = block_sum(s2, red) / (float)h;
+        // both row sums in one exchange; the two LDS buffers alternate by
+        // row, so a buffer is rewritten only after every thread has passed
+        // the next row's barrier
+        s1 = wave_sum(s1);
+        s2 = wave_sum(s2);
+        float(*rb)[4] = red[row & 1];
+        if ((threadIdx.x & 63) == 0) {
+            rb[0][threadIdx.x >> 6] = s1;
+            rb[1][threadIdx.x >> 6] = s2;
+        }
+        __syncthreads();
+        const float m1 = (rb[0][0] + rb[0][1] + rb[0][2] + rb[0][3]) / (float)h;
+        const float m2 = (rb[1][0] + rb[1][1] + rb[1][2] + rb[1][3]) / (float)h;
 #pragma unroll
-        for (int i = 0; i < kMaxVec; ++i) {
-            int c = threadIdx.x + i * kThreads;
+        for (int i = 0; i < NV; ++i) {
+            const int c = threadIdx.x + i * kThreads;
             if (c < nv) {
-                float gg[8], rr[8], o[8];
-                load8(g + c * 8, gg);
-                load8(resid + (size_t)row * h + c * 8, rr);
+                float o[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) o[j] = rr[j] + rs * (dv[i][j] * gg[j] - m1 - xh[i][j] * m2);
+                for (int j = 0; j < 8; ++j)
+                    o[j] = cur[i].res[j] + rs * (cur[i].du[j] * gg[i][j] - m1 - xh[i][j] * m2);
                 store8(dx + (size_t)row * h + c * 8, o);
             }
         }
+        if constexpr (kPrefetch) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+        }
     }
-    __syncthreads();
     float *pb = partials + (size_t)blockIdx.x * 2 * h;
-    for (int c = threadIdx.x; c < 2 * h; c += kThreads) pb[c] = accs[c];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        if (c < nv) {
+            store8(pb + c * 8, adg[i]);
+            store8(pb + h + c * 8, adb[i]);
+        }
+    }
 }
 
 // out[c] (+)= sum over blocks of partials[blk][c], for c < n; partial rows are
@@ -224,26 +293,44 @@ hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, co
     return hipGetLastError();
 }
 
+template <typename T, int NV>
+static void launch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du, const void *resid, const void *x,
+                          const void *g, const float *mean, const float *rstd, void *dx, float *partials,
+                          hipStream_t st) {
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(nblk), dim3(kThreads), 0, st, rows, h, rpb, du,
+                       (const T *)resid, (const T *)x, (const T *)g, mean, rstd, (T *)dx, partials);
+}
+
+template <typename T>
+static void dispatch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du, const void *resid, const void *x,
+                            const void *g, const float *mean, const float *rstd, void *dx, float *partials,
+                            hipStream_t st) {
+    const int nvt = ((h >> 3) + kThreads - 1) / kThreads;  // vectors per thread, 1..kMaxVec
+    switch (nvt) {
+    case 1: launch_ln_bwd<T, 1>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 2: launch_ln_bwd<T, 2>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 3: launch_ln_bwd<T, 3>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 4: launch_ln_bwd<T, 4>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 5: launch_ln_bwd<T, 5>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 6: launch_ln_bwd<T, 6>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 7: launch_ln_bwd<T, 7>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    default: launch_ln_bwd<T, 8>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    }
+}
+
 hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void *resid, const void *x,
                          const void *g, const float *mean, const float *rstd, void *dx, float *dg, float *db,
                          bool accumulate, float *partials, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     const int nblk = ln_bwd_blocks(rows), rpb = (rows + nblk - 1) / nblk;
-    const size_t lds = (size_t)2 * h * sizeof(float);
     const int es = dt == DType::BF16 ? 2 : 4;
     {
-    TraceScope ts(st, dt == DType::BF16 ? "ln_bwd_bf16" : "ln_bwd_f32", 0.0,
-                  (double)rows * h * (4 + 3 * es) + 8.0 * rows + (double)nblk * 2 * h * 4);
-    if (dt == DType::BF16) {
-        hipFuncSetAttribute((const void *)ln_bwd_kernel<bf16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nblk), dim3(kThreads), lds, st, rows, h, rpb, du,
-                           (const bf16 *)resid, (const bf16 *)x, (const bf16 *)g, mean, rstd, (bf16 *)dx, partials);
-    } else {
-        hipFuncSetAttribute((const void *)ln_bwd_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nblk), dim3(kThreads), lds, st, rows, h, rpb, du,
-                           (const float *)resid, (const float *)x, (const float *)g, mean, rstd, (float *)dx,
-                           partials);
-    }
+        TraceScope ts(st, dt == DType::BF16 ? "ln_bwd_bf16" : "ln_bwd_f32", 0.0,
+                      (double)rows * h * (4 + 3 * es) + 8.0 * rows + (double)nblk * 2 * h * 4);
+        if (dt == DType::BF16)
+            dispatch_ln_bwd<bf16>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
+        else
+            dispatch_ln_bwd<float>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
