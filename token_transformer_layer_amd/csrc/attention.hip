@@ -923,6 +923,330 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(AttnFwdP a) {
     if (half == 0) a.lse[(int64_t)bh * a.seq + q] = (m + __log2f(l)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Backward on 32x32x16 MFMAs
+//
+// dK, dV: a workgroup owns 128 keys of one (batch row, head), 32 per wave,
+// held in registers; the query tiles that see them (64 queries each: Q and
+// dO rows, and the tile's log-sum-exp and rowsum(dO * O)) stream through LDS
+// by direct-to-LDS loads, two stages deep.  Per query tile a wave forms
+// S = Q K^T and dP = dO V^T with keys along the lanes and queries along the
+// registers, which is already the B operand (keys as columns, queries as the
+// reduction) of dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T fragments
+// come from the same LDS tiles through transposing reads.
+//
+// dQ: a workgroup owns 128 queries, 32 per wave, Q and dO in registers; the
+// key tiles before the queries stream through LDS; S^T = K Q^T and
+// dP^T = V dO^T put queries along the lanes, so dS^T is the B operand of
+// dQ^T += K^T dS^T (K^T through transposing reads), as in the forward.
+// ---------------------------------------------------------------------------
+
+constexpr int kBwdBK = 128;  // keys per dK/dV workgroup
+constexpr int kBwdBQ = 128;  // queries per dQ workgroup
+
+// one 64-row tile of a [rows][D] bf16 matrix whose rows are `ld` elements
+// apart (rows [row0, row0 + 64), rows >= rend zero) into LDS [64][D], 16-byte
+// chunks swizzled by row
+template <int D>
+__device__ __forceinline__ void rows_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst, int64_t base, int64_t ld,
+                                              int row0, int rend, int wave, int lane) {
+    constexpr int INSTR = 64 * D * 2 / 1024, PER_WAVE = INSTR / 4;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+        const int I = wave * PER_WAVE + q;
+        const int byte = I * 1024 + lane * 16;
+        const int row = byte / (D * 2);
+        const int c = ((byte % (D * 2)) >> 4) ^ (row & (D / 8 - 1));
+        const int gr = row0 + row;
+        const uint32_t off = gr < rend ? (uint32_t)((base + (int64_t)gr * ld + c * 8) * 2) : kOOB;
+        lds_dma16(r, dst + I * 1024, off);
+    }
+}
+
+// A operand of a 32x32x16 MFMA taken transposed from a [64][D] LDS tile: lane
+// l gets column db*32 + l%32 at rows r0..r0+3 and r0+8..r0+11 of the tile,
+// r0 = row_base + 4*(l/32) (the order in which a score block's registers
+// 8h..8h+7 hold their rows).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char *tile, int row_base, int db, int lane) {
+    const int G = lane >> 4, L = lane & 15, g = lane >> 5;
+    const int col = db * 32 + 16 * (G & 1) + 4 * (L & 3);
+    const int cc = col >> 3, within = (col & 7) * 2;
+    const int r0 = row_base + 4 * g + (L >> 2);
+    const u32x2 lo = lds_read_tr16(tile + kv_chunk_off<D>(r0, cc) + within);
+    const u32x2 hi = lds_read_tr16(tile + kv_chunk_off<D>(r0 + 8, cc) + within);
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// registers 8h..8h+7 of a 32x32 score block as bf16 (the B operand of one
+// 16-step of the reduction over the block's rows)
+__device__ __forceinline__ bf16x8 pack_half(const f32x16 &s, int h) {
+    const int b = 8 * h;
+    return __builtin_bit_cast(bf16x8, u32x4{pack_bf2(s[b], s[b + 1]), pack_bf2(s[b + 2], s[b + 3]),
+                                            pack_bf2(s[b + 4], s[b + 5]), pack_bf2(s[b + 6], s[b + 7])});
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE = 64 * D * 2;
+    constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, lse * log2(e) and delta (64 floats each), 1 KB aligned
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int kb0 = blockIdx.x * kBwdBK;
+    const int kw0 = kb0 + w * 32;
+    const int my_k = kw0 + li;
+    const int ht = a.nt * D;
+    const int64_t slab = (int64_t)bh * a.seq * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+    const uint32_t do_bytes = (uint32_t)(((int64_t)a.seq * a.batch * ht) * 2);
+    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, do_bytes);
+
+    // B operands of S = Q K^T and dP = dO V^T: lane holds key my_k, d = 16 s + 8 g + j
+    bf16x8 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint32_t off = my_k < a.q1 ? (uint32_t)((slab + (int64_t)my_k * D + s * 16 + g * 8) * 2) : kOOB;
+        kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+        vreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    }
+    f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x16{}; acc_dv[i] = f32x16{}; }
+
+    const int qstart = max(a.q0, kb0);
+    const int nqt = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
+    const int64_t do_base = (int64_t)bi * ht + head * D;  // dO row p at do_base + p * batch * ht
+    const int64_t do_ld = (int64_t)a.batch * ht;
+    const int64_t stat0 = (int64_t)bh * a.seq;
+
+    auto issue = [&](int t, char *st) {
+        const int p0 = qstart + t * 64;
+        rows_tile_dma<D>(rq, st, slab, D, p0, a.q1, w, lane);
+        rows_tile_dma<D>(rdo, st + TILE, do_base, do_ld, p0, a.q1, w, lane);
+    };
+    // the tile's statistics go through registers of the first two waves
+    float stat = 0.f;
+    auto load_stat = [&](int t) {
+        if (tid < 128) {
+            const int p = qstart + t * 64 + (tid & 63);
+            stat = p < a.q1 ? (tid < 64 ? a.lse[stat0 + p] * kLog2e : a.delta[stat0 + p]) : 0.f;
+        }
+    };
+    auto store_stat = [&](char *st) {
+        if (tid < 128) ((float *)(st + 2 * TILE))[tid] = stat;
+    };
+    if (nqt > 0) {
+        issue(0, smem);
+        load_stat(0);
+        store_stat(smem);
+    }
+    for (int t = 0; t < nqt; ++t) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        const char *st = smem + (t & 1) * STAGE;
+        if (t + 1 < nqt) {
+            issue(t + 1, smem + ((t + 1) & 1) * STAGE);
+            load_stat(t + 1);
+        }
+        const int p0 = qstart + t * 64;
+        const float *lse_s = (const float *)(st + 2 * TILE);
+        const float *del_s = lse_s + 64;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qr0 = p0 + qb * 32;          // first query of the block
+            if (qr0 + 31 < kw0) continue;          // every query precedes every key of this wave
+            f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = kv_chunk_off<D>(qb * 32 + li, 2 * s + g);
+                sc = mfma32(*(const bf16x8 *)(st + off), kreg[s], sc);
+                dp = mfma32(*(const bf16x8 *)(st + TILE + off), vreg[s], dp);
+            }
+            // register v: query qr0 + 8(v/4) + 4g + v%4, key my_k
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ql = qb * 32 + 8 * r + 4 * g;
+                const f32x4 l4 = *(const f32x4 *)(lse_s + ql);
+                const f32x4 d4 = *(const f32x4 *)(del_s + ql);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int q = p0 + ql + u;
+                    const float pr =
+                        (my_k <= q && q < a.q1) ? __builtin_amdgcn_exp2f(sc[4 * r + u] * sl2 - l4[u]) : 0.f;
+                    sc[4 * r + u] = pr;
+                    dp[4 * r + u] = pr * (dp[4 * r + u] - d4[u]);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8 pb = pack_half(sc, h), sb = pack_half(dp, h);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    acc_dv[db] = mfma32(tr_frag<D>(st + TILE, qb * 32 + 16 * h, db, lane), pb, acc_dv[db]);
+                    acc_dk[db] = mfma32(tr_frag<D>(st, qb * 32 + 16 * h, db, lane), sb, acc_dk[db]);
+                }
+            }
+        }
+        if (t + 1 < nqt) store_stat(smem + ((t + 1) & 1) * STAGE);
+    }
+    if (my_k >= a.q1) return;
+    // acc[db] register v: d = db*32 + 8(v/4) + 4g + v%4 of key my_k
+    const int64_t arow = slab + (int64_t)my_k * D;
+    const bool final_key = my_k >= a.k_final0;
+    bf16 *dst = a.out + ((int64_t)my_k * a.batch + bi) * (3 * ht) + head * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = db * 32 + 8 * r + 4 * g;
+            f32x4 dk{acc_dk[db][4 * r], acc_dk[db][4 * r + 1], acc_dk[db][4 * r + 2], acc_dk[db][4 * r + 3]};
+            f32x4 dv{acc_dv[db][4 * r], acc_dv[db][4 * r + 1], acc_dv[db][4 * r + 2], acc_dv[db][4 * r + 3]};
+            dk *= a.scale;
+            if (a.acc_in) {
+                dk += *(const f32x4 *)(a.dk_acc + arow + j);
+                dv += *(const f32x4 *)(a.dv_acc + arow + j);
+            }
+            if (final_key) {
+                *(u32x2 *)(dst + ht + j) = u32x2{pack_bf2(dk[0], dk[1]), pack_bf2(dk[2], dk[3])};
+                *(u32x2 *)(dst + 2 * ht + j) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
+            } else {
+                *(f32x4 *)(a.dk_acc + arow + j) = dk;
+                *(f32x4 *)(a.dv_acc + arow + j) = dv;
+            }
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_mfma32(AttnP a) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE = 64 * D * 2;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int qt0 = a.q0 + blockIdx.x * kBwdBQ;
+    const int my_q = qt0 + w * 32 + li;
+    const int q_eff = min(my_q, a.q1 - 1);
+    const int kend = min(a.q1, qt0 + kBwdBQ);
+    const int ntiles = (kend + 63) / 64;
+    const int ht = a.nt * D;
+    const int64_t slab = (int64_t)bh * a.seq * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+    const uint32_t do_bytes = (uint32_t)(((int64_t)a.seq * a.batch * ht) * 2);
+    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, do_bytes);
+
+    // B operands of S^T = K Q^T and dP^T = V dO^T: lane holds query my_q, d = 16 s + 8 g + j
+    bf16x8 qreg[KS], doreg[KS];
+    const bool qok = my_q < a.q1;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint32_t off = qok ? (uint32_t)((slab + (int64_t)my_q * D + s * 16 + g * 8) * 2) : kOOB;
+        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+        const uint32_t offd =
+            qok ? (uint32_t)((((int64_t)my_q * a.batch + bi) * ht + head * D + s * 16 + g * 8) * 2) : kOOB;
+        doreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, offd));
+    }
+    const float lse2 = qok ? a.lse[(int64_t)bh * a.seq + my_q] * kLog2e : INFINITY;
+    const float del = qok ? a.delta[(int64_t)bh * a.seq + my_q] : 0.f;
+    f32x16 acc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+    kv_tile_dma<D>(rk, smem, slab, 0, kend, w, lane);
+    kv_tile_dma<D>(rv, smem + TILE, slab, 0, kend, w, lane);
+    for (int t = 0; t < ntiles; ++t) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        const char *ks = smem + (t & 1) * 2 * TILE;
+        const char *vs = ks + TILE;
+        if (t + 1 < ntiles) {
+            char *nx = smem + ((t + 1) & 1) * 2 * TILE;
+            kv_tile_dma<D>(rk, nx, slab, (t + 1) * 64, kend, w, lane);
+            kv_tile_dma<D>(rv, nx + TILE, slab, (t + 1) * 64, kend, w, lane);
+        }
+        const int key0 = t * 64;
+        if (key0 > qt0 + w * 32 + 31) continue;  // every key of the tile is after this wave's queries
+        bf16x8 sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sc = f32x16{}, dp = f32x16{};
+            const int row = kb * 32 + li;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = kv_chunk_off<D>(row, 2 * s + g);
+                sc = mfma32(*(const bf16x8 *)(ks + off), qreg[s], sc);
+                dp = mfma32(*(const bf16x8 *)(vs + off), doreg[s], dp);
+            }
+            // register v: key key0 + 32 kb + 8(v/4) + 4g + v%4, query my_q
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
+                const float pr = key <= q_eff ? __builtin_amdgcn_exp2f(sc[v] * sl2 - lse2) : 0.f;
+                dp[v] = pr * (dp[v] - del);
+            }
+            sb[2 * kb] = pack_half(dp, 0);
+            sb[2 * kb + 1] = pack_half(dp, 1);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) acc[db] = mfma32(tr_frag<D>(ks, 16 * k4, db, lane), sb[k4], acc[db]);
+    }
+    if (!qok) return;
+    bf16 *dst = a.out + ((int64_t)my_q * a.batch + bi) * (3 * ht) + head * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = db * 32 + 8 * r + 4 * g;
+            *(u32x2 *)(dst + j) = u32x2{pack_bf2(acc[db][4 * r] * a.scale, acc[db][4 * r + 1] * a.scale),
+                                        pack_bf2(acc[db][4 * r + 2] * a.scale, acc[db][4 * r + 3] * a.scale)};
+        }
+}
+
+// delta[bh][p] = sum_j dO[p][j] O[p][j]: D/8 lanes per (query, head), 8
+// columns each, reduced by shuffles within the lane group.
+template <int D>
+__global__ __launch_bounds__(256) void attn_delta_bf16(int batch, int nt, int seq, int q0, int q1,
+                                                       const bf16 *__restrict__ o, const bf16 *__restrict__ dout,
+                                                       float *__restrict__ delta) {
+    constexpr int LPG = D / 8;
+    const int64_t n = (int64_t)(q1 - q0) * batch * nt;
+    const int64_t i = (blockIdx.x * 256LL + threadIdx.x) / LPG;
+    const int part = threadIdx.x % LPG;
+    float s = 0.f;
+    int64_t base = 0;
+    if (i < n) {
+        base = i * D + part * 8;  // token-major rows: (call row, head) pairs are contiguous D-blocks
+        base += (int64_t)q0 * batch * nt * D;
+        float x[8], y[8];
+        load8(o + base, x);
+        load8(dout + base, y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += x[j] * y[j];
+    }
+#pragma unroll
+    for (int m = LPG / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (i < n && part == 0) {
+        const int head = (int)(i % nt);
+        const int64_t r = i / nt;
+        const int bi = (int)(r % batch);
+        const int p = q0 + (int)(r / batch);
+        delta[((int64_t)bi * nt + head) * seq + p] = s;
+    }
+}
+
 }  // namespace
 
 // (query, key) pairs of the causal product for queries [q0, q1) of every
@@ -1007,8 +1331,14 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
     if (dt == DType::BF16) {
         {
             TraceScope ts(st, "attn_delta_bf16", 2.0 * x.d * nd, 2.0 * nd * x.d * es + 4.0 * nd);
-            hipLaunchKernelGGL(attn_delta_kernel<bf16>, dim3(dgrid), dim3(256), 0, st, x.batch, x.nt, x.seq, x.d,
-                               x.q0, x.q1, (const bf16 *)x.o, (const bf16 *)x.dout, x.delta);
+            const int64_t threads = nd * (x.d / 8);
+            const unsigned dg = (unsigned)((threads + 255) / 256);
+            if (x.d == 128)
+                hipLaunchKernelGGL(attn_delta_bf16<128>, dim3(dg), dim3(256), 0, st, x.batch, x.nt, x.seq, x.q0, x.q1,
+                                   (const bf16 *)x.o, (const bf16 *)x.dout, x.delta);
+            else
+                hipLaunchKernelGGL(attn_delta_bf16<64>, dim3(dg), dim3(256), 0, st, x.batch, x.nt, x.seq, x.q0, x.q1,
+                                   (const bf16 *)x.o, (const bf16 *)x.dout, x.delta);
         }
         AttnP p{};
         p.batch = x.batch; p.nt = x.nt; p.seq = x.seq; p.q0 = x.q0; p.q1 = x.q1; p.scale = x.scale;
@@ -1017,16 +1347,32 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
         p.dout = (const bf16 *)x.dout; p.out = (bf16 *)x.dqkv; p.lse = x.lse; p.delta = x.delta;
         p.dk_acc = x.dk_acc; p.dv_acc = x.dv_acc;
         p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
-        dim3 gk((x.q1 + 63) / 64, bh), gq((nq + 63) / 64, bh);
+        dim3 gk((x.q1 + kBwdBK - 1) / kBwdBK, bh), gq((nq + kBwdBQ - 1) / kBwdBQ, bh);
+        const int tile = 64 * x.d * 2;
+        const int lds_kv = 2 * (2 * tile + 1024), lds_q = 2 * 2 * tile;
         {
             TraceScope ts(st, "attn_bwd_dkdv_bf16", 8.0 * x.d * pairs, kv_bytes);
-            if (x.d == 128) hipLaunchKernelGGL(attn_bwd_dkdv_bf16<128>, gk, dim3(256), 0, st, p);
-            else hipLaunchKernelGGL(attn_bwd_dkdv_bf16<64>, gk, dim3(256), 0, st, p);
+            if (x.d == 128) {
+                hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<128>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+                hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<128>, gk, dim3(256), lds_kv, st, p);
+            } else {
+                hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<64>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+                hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<64>, gk, dim3(256), lds_kv, st, p);
+            }
         }
         {
             TraceScope ts(st, "attn_bwd_dq_bf16", 6.0 * x.d * pairs, q_bytes);
-            if (x.d == 128) hipLaunchKernelGGL(attn_bwd_dq_bf16<128>, gq, dim3(256), 0, st, p);
-            else hipLaunchKernelGGL(attn_bwd_dq_bf16<64>, gq, dim3(256), 0, st, p);
+            if (x.d == 128) {
+                hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    lds_q);
+                hipLaunchKernelGGL(attn_bwd_dq_mfma32<128>, gq, dim3(256), lds_q, st, p);
+            } else {
+                hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    lds_q);
+                hipLaunchKernelGGL(attn_bwd_dq_mfma32<64>, gq, dim3(256), lds_q, st, p);
+            }
         }
     } else {
         TraceScope ts(st, "attn_bwd_f32", 14.0 * x.d * pairs, kv_bytes + q_bytes);
