@@ -97,7 +97,7 @@ Saved saved_layout(const Dims &d) {
 }
 
 struct Scratch {
-    int64_t dz, dO, delta, dqkv, red, attn, total;
+    int64_t dz, dO, delta, dqkv, red, attn, split, total;
 };
 Scratch scratch_layout(const Dims &d) {
     Scratch L;
@@ -114,6 +114,7 @@ Scratch scratch_layout(const Dims &d) {
     int64_t cs = (int64_t)colsum_partials_floats((int)d.T, (int)widest);
     L.red = take((red > cs ? red : cs) * 4);
     L.attn = take((int64_t)attn_fwd_work_floats((int)d.b, (int)d.nt, (int)d.s, (int)d.d) * 4);
+    L.split = d.dt == DType::BF16 ? take((int64_t)gemm_split_workspace_floats() * 4) : off;
     L.total = off;
     return L;
 }
@@ -206,7 +207,14 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
     hipStream_t st = (hipStream_t)stream;
     const int es = d.es;
-    EpiArgs e;
+    // every product may split its reduction through the scratch workspace
+    auto fresh = [&]() {
+        EpiArgs x;
+        x.split_ws = at<float *>(scratch, S.split);
+        x.split_ws_floats = d.dt == DType::BF16 ? (int64_t)gemm_split_workspace_floats() : 0;
+        return x;
+    };
+    EpiArgs e = fresh();
     if (phase == TP_FWD_ATTN) {
         NEED(w->ln1_g, "w.ln1_g");
         NEED(w->ln1_b, "w.ln1_b");
@@ -223,7 +231,7 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln1_g,
                               w->ln1_b, u1, at<float *>(saved, L.mu1 + r0 * 4), at<float *>(saved, L.rs1 + r0 * 4), st),
                 "layernorm forward (LN1)");
-        e = EpiArgs{};
+        e = fresh();
         e.bias = w->b_qkv;
         e.q = at<char *>(saved, L.q);
         e.k = kv->k;
@@ -239,7 +247,7 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         a.o = at<char *>(saved, L.o); a.lse = at<float *>(saved, L.lse);
         a.work = at<float *>(scratch, S.attn);
         HIPCALL(attn_fwd(d.dt, a, st), "attention forward");
-        e = EpiArgs{};
+        e = fresh();
         e.c = partial_out + r0 * d.h;
         e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ht, Mat{at<char *>(saved, L.o + r0 * d.ht * es), d.ht, true},
@@ -259,11 +267,11 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
             "layernorm forward (LN2)");
     void *z = at<char *>(saved, L.z + r0 * d.ft * es);
     void *gg = at<char *>(saved, L.g + r0 * d.ft * es);
-    e = EpiArgs{};
+    e = fresh();
     e.c = z; e.ldc = d.ft; e.c2 = gg; e.ldc2 = d.ft; e.bias = w->b1;
     HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{u2, d.h, true}, Mat{w->w1, d.h, true}, Epi::BiasGelu, e, st),
             "FC1 product");
-    e = EpiArgs{};
+    e = fresh();
     e.c = partial_out + r0 * d.h;
     e.ldc = d.h;
     HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ft, Mat{gg, d.ft, true}, Mat{w->w2, d.ft, true}, Epi::StoreF32, e,
@@ -348,7 +356,13 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     const int es = d.es;
     float *red = at<float *>(scratch, S.red);
     const Epi wepi = acc ? Epi::AccumF32 : Epi::StoreF32;  // weight-gradient epilogue
-    EpiArgs e;
+    auto fresh = [&]() {
+        EpiArgs x;
+        x.split_ws = at<float *>(scratch, S.split);
+        x.split_ws_floats = d.dt == DType::BF16 ? (int64_t)gemm_split_workspace_floats() : 0;
+        return x;
+    };
+    EpiArgs e = fresh();
     // rows of the call in each per-row tensor
     const void *dyr = dy ? at<const char *>(dy, r0 * d.h * es) : nullptr;
     void *dz = at<char *>(scratch, S.dz + r0 * d.ft * es);
@@ -358,12 +372,12 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
 
     if (mlp) {
         // dZ = (dY W2) * GELU'(Z); dU2,r = dZ W1
-        e = EpiArgs{};
+        e = fresh();
         e.c = dz; e.ldc = d.ft; e.aux = at<const char *>(saved, L.z + r0 * d.ft * es); e.ldaux = d.ft;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{dyr, d.h, true}, Mat{w->w2, d.ft, false}, Epi::GeluGrad,
                      e, st),
                 "FC2 input-gradient product");
-        e = EpiArgs{};
+        e = fresh();
         e.c = partial_out + r0 * d.h; e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)d.ft, Mat{dz, d.ft, true}, Mat{w->w1, d.h, false}, Epi::StoreF32,
                      e, st),
@@ -371,12 +385,12 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     }
     if (mlp_w) {
         // dW2 = dY^T G, dW1 = dZ^T u2, db1 = sum dZ, db2 = sum dY
-        e = EpiArgs{};
+        e = fresh();
         e.c = g->w2; e.ldc = d.ft;
         HIPCALL(gemm(d.dt, (int)d.h, (int)d.ft, (int)nrows, Mat{dyr, d.h, false},
                      Mat{at<const char *>(saved, L.g + r0 * d.ft * es), d.ft, false}, wepi, e, st),
                 "FC2 weight-gradient product");
-        e = EpiArgs{};
+        e = fresh();
         e.c = g->w1; e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)d.ft, (int)d.h, (int)nrows, Mat{dz, d.ft, false},
                      Mat{at<const char *>(saved, L.u2 + r0 * d.h * es), d.h, false}, wepi, e, st),
@@ -390,7 +404,7 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
                               at<const char *>(ln_in, r0 * d.h * es), w->ln2_g, at<const float *>(saved, L.mu2 + r0 * 4),
                               at<const float *>(saved, L.rs2 + r0 * 4), dhr, g->ln2_g, g->ln2_b, acc, red, st),
                 "layernorm backward (LN2)");
-        e = EpiArgs{};
+        e = fresh();
         e.c = dO; e.ldc = d.ht;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.ht, (int)d.h, Mat{dhr, d.h, true}, Mat{w->w_o, d.ht, false}, Epi::Store, e,
                      st),
@@ -409,7 +423,7 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         a.acc_in = kvg->done_from != d.s;
         HIPCALL(attn_bwd(d.dt, a, st), "attention backward");
         // dU1,r = dQKV W_qkv
-        e = EpiArgs{};
+        e = fresh();
         e.c = partial_out + r0 * d.h; e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.h, (int)(3 * d.ht), Mat{dqkv, 3 * d.ht, true}, Mat{w->w_qkv, d.h, false},
                      Epi::StoreF32, e, st),
@@ -418,13 +432,13 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     }
     if (attn_w) {
         // dW_o = dH^T O, db_o = sum dH, dW_qkv = dQKV^T u1, db_qkv = sum dQKV
-        e = EpiArgs{};
+        e = fresh();
         e.c = g->w_o; e.ldc = d.ht;
         HIPCALL(gemm(d.dt, (int)d.h, (int)d.ht, (int)nrows, Mat{dhr, d.h, false},
                      Mat{at<const char *>(saved, L.o + r0 * d.ht * es), d.ht, false}, wepi, e, st),
                 "out-projection weight-gradient product");
         HIPCALL(colsum(d.dt, (int)nrows, (int)d.h, dhr, d.h, g->b_o, acc, red, st), "b_o gradient");
-        e = EpiArgs{};
+        e = fresh();
         e.c = g->w_qkv; e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)(3 * d.ht), (int)d.h, (int)nrows, Mat{dqkv, 3 * d.ht, false},
                      Mat{at<const char *>(saved, L.u1 + r0 * d.h * es), d.h, false}, wepi, e, st),

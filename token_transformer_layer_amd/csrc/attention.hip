@@ -10,18 +10,15 @@
 // the query; the softmax is taken online (running maximum and sum per query)
 // so K and V stream once per query tile from HBM through LDS.
 //
-// bf16 kernels use v_mfma_f32_16x16x32_bf16.  In the forward each wave owns
-// 16 queries and computes S^T = K Q^T, so one lane holds one query's scores
-// for 16 keys; those registers are, without any data movement, the B operand
-// of O^T += V^T P^T (the 32 keys of one MFMA step are taken as keys
-// 4g..4g+3 and 16+4g..16+4g+3 of lane group g, and V^T is read from LDS in
-// the same order).  The backward recomputes P from the saved log-sum-exp and
-// uses two kernels so that no floating-point atomics are needed and results
-// are deterministic: one per key tile (dK, dV, looping over the queries that
-// see those keys) and one per query tile (dQ, looping over the keys the
-// queries see).  dK and dV of keys before the call's first query are
-// accumulated in fp32 across calls, because the backward runs the slices in
-// reverse and later slices' queries also see earlier keys.
+// bf16 kernels use v_mfma_f32_32x32x16_bf16 with K/V (forward, dQ) or Q/dO
+// (dK, dV) tiles staged by direct-to-LDS loads; their layouts are described
+// with each kernel below.  The backward recomputes P from the saved
+// log-sum-exp and uses two kernels so that no floating-point atomics are
+// needed and results are deterministic: one per key block (dK, dV, looping
+// over the queries that see those keys) and one per query block (dQ, looping
+// over the keys the queries see).  dK and dV of keys before the call's first
+// query are accumulated in fp32 across calls, because the backward runs the
+// slices in reverse and later slices' queries also see earlier keys.
 //
 // fp32 kernels are plain one-wave-per-row loops (used for the fp32 storage
 // configuration only).
@@ -39,106 +36,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// LDS tile [64 rows][D] bf16 with 16-byte chunks swizzled by row.
-template <int D>
-__device__ __forceinline__ int rowtile_off(int row, int ch) {
-    constexpr int CH = D / 8;
-    return row * (D * 2) + ((ch ^ (row & (CH - 1))) << 4);
-}
-// LDS tile [D rows][64 keys] bf16 (transposed), 8-byte units swizzled by row.
-__device__ __forceinline__ int coltile_off(int row, int unit) { return row * 128 + ((unit ^ (row & 15)) << 3); }
-
-// Copies a 64 x D bf16 tile whose rows are `ld` elements apart, rows
-// [r0, r0+64) of which only rows < rend exist, into registers (16 bytes per
-// lane per vector, zeros past rend).
-template <int D>
-struct RowTile {
-    static constexpr int VEC = 64 * D / 8 / 256;
-    u32x4 r[VEC];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t base, int r0, int rend, int tid) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            int v = tid + i * 256;
-            int row = v / (D / 8), ch = v % (D / 8);
-            uint32_t off = (r0 + row < rend) ? (uint32_t)((base + (int64_t)(r0 + row) * D + ch * 8) * 2) : kOOB;
-            r[i] = buf_load16(rs, off);
-        }
-    }
-    // natural layout [row][D]
-    __device__ __forceinline__ void store_rows(char *lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            int v = tid + i * 256;
-            int row = v / (D / 8), ch = v % (D / 8);
-            *(u32x4 *)(lds + rowtile_off<D>(row, ch)) = r[i];
-        }
-    }
-};
-
-// Same tile, loaded so that each lane holds 4 consecutive rows of one
-// 8-column chunk, and stored transposed as [D][64].
-template <int D>
-struct ColTile {
-    static constexpr int NB = 16 * (D / 8);  // (4-row group, chunk) pairs
-    u32x4 r[4];
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t base, int r0, int rend, int tid) {
-        if (tid < NB) {
-            int ch = tid % (D / 8), kg = tid / (D / 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int row = r0 + kg * 4 + i;
-                uint32_t off = row < rend ? (uint32_t)((base + (int64_t)row * D + ch * 8) * 2) : kOOB;
-                r[i] = buf_load16(rs, off);
-            }
-        }
-    }
-    __device__ __forceinline__ void store_cols(char *lds, int tid) const {
-        if (tid < NB) {
-            int ch = tid % (D / 8), kg = tid / (D / 8);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                uint32_t lo0 = r[0][c >> 1], lo1 = r[1][c >> 1], lo2 = r[2][c >> 1], lo3 = r[3][c >> 1];
-                uint32_t w0, w1;
-                if (c & 1) {
-                    w0 = (lo0 >> 16) | (lo1 & 0xffff0000u);
-                    w1 = (lo2 >> 16) | (lo3 & 0xffff0000u);
-                } else {
-                    w0 = (lo0 & 0xffffu) | (lo1 << 16);
-                    w1 = (lo2 & 0xffffu) | (lo3 << 16);
-                }
-                *(u32x2 *)(lds + coltile_off(ch * 8 + c, kg)) = u32x2{w0, w1};
-            }
-        }
-    }
-};
-
-// A operand of an MFMA step over 32 keys (or queries) from a transposed tile:
-// row `row`, units (step*8 + g) and (step*8 + 4 + g).
-__device__ __forceinline__ bf16x8 read_cols(const char *lds, int row, int step, int g) {
-    u32x2 a = *(const u32x2 *)(lds + coltile_off(row, step * 8 + g));
-    u32x2 b = *(const u32x2 *)(lds + coltile_off(row, step * 8 + 4 + g));
-    u32x4 w{a[0], a[1], b[0], b[1]};
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x4 &lo, const f32x4 &hi) {
-    u32x4 w{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
-    return __builtin_bit_cast(bf16x8, w);
-}
-
-__device__ __forceinline__ float group_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    return fmaxf(v, __shfl_xor(v, 32, 64));
-}
-__device__ __forceinline__ float group_sum(float v) {
-    v += __shfl_xor(v, 16, 64);
-    return v + __shfl_xor(v, 32, 64);
-}
-
 struct AttnP {
     int batch, nt, seq, q0, q1, k_final0, acc_in;
     float scale;
@@ -147,118 +44,6 @@ struct AttnP {
     float *lse, *delta, *dk_acc, *dv_acc;
     uint32_t kv_bytes, q_bytes;
 };
-
-// ---------------------------------------------------------------------------
-// Forward
-// ---------------------------------------------------------------------------
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16(AttnP a) {
-    constexpr int KS = D / 32;  // MFMA steps over d
-    constexpr int DB = D / 16;  // 16-row blocks of d
-    __shared__ __attribute__((aligned(16))) char ks_lds[64 * D * 2];
-    __shared__ __attribute__((aligned(16))) char vt_lds[64 * D * 2];
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
-    const int qt0 = a.q0 + blockIdx.x * 64;
-    const int qw0 = qt0 + w * 16;
-    const int my_q = qw0 + li;
-    const int q_eff = min(my_q, a.q1 - 1);  // padding lanes act as the last query
-    const int kend = min(a.q1, qt0 + 64);
-    const int64_t slab = (int64_t)bh * a.seq * D;
-    const float sl2 = a.scale * kLog2e;
-
-    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
-    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
-    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
-
-    bf16x8 qreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        uint32_t off = my_q < a.q1 ? (uint32_t)((slab + (int64_t)my_q * D + s * 32 + g * 8) * 2) : kOOB;
-        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-    }
-
-    f32x4 acc_o[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) acc_o[i] = f32x4{};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    RowTile<D> kt_r;
-    ColTile<D> vt_r;
-    const int nkt = (kend + 63) / 64;
-    kt_r.load(rk, slab, 0, kend, tid);
-    vt_r.load(rv, slab, 0, kend, tid);
-    for (int kt = 0; kt < nkt; ++kt) {
-        kt_r.store_rows(ks_lds, tid);
-        vt_r.store_cols(vt_lds, tid);
-        __syncthreads();
-        if (kt + 1 < nkt) {
-            kt_r.load(rk, slab, (kt + 1) * 64, kend, tid);
-            vt_r.load(rv, slab, (kt + 1) * 64, kend, tid);
-        }
-        const int key0 = kt * 64;
-        if (key0 <= qw0 + 15) {  // some key of the tile is visible to this wave
-            f32x4 s[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                s[kb] = f32x4{};
-#pragma unroll
-                for (int st = 0; st < KS; ++st) {
-                    bf16x8 ka = *(const bf16x8 *)(ks_lds + rowtile_off<D>(kb * 16 + li, st * 4 + g));
-                    s[kb] = mfma16(ka, qreg[st], s[kb]);
-                }
-            }
-            // S^T[key = key0 + kb*16 + 4g + v][query = my_q]
-            float mt = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    int key = key0 + kb * 16 + 4 * g + v;
-                    float x = key <= q_eff ? s[kb][v] * sl2 : -INFINITY;
-                    s[kb][v] = x;
-                    mt = fmaxf(mt, x);
-                }
-            mt = group_max(mt);
-            const float m_new = fmaxf(m_run, mt);  // finite: key 0 is always visible
-            const float alpha = exp2f(m_run - m_new);
-            m_run = m_new;
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float p = exp2f(s[kb][v] - m_new);
-                    s[kb][v] = p;
-                    ls += p;
-                }
-            l_run = l_run * alpha + ls;
-#pragma unroll
-            for (int i = 0; i < DB; ++i) acc_o[i] *= alpha;
-            bf16x8 pb[2] = {pack8(s[0], s[1]), pack8(s[2], s[3])};
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    acc_o[db] = mfma16(read_cols(vt_lds, db * 16 + li, st, g), pb[st], acc_o[db]);
-        }
-        __syncthreads();
-    }
-    const float l_tot = group_sum(l_run);
-    if (my_q < a.q1) {
-        const float inv = 1.0f / l_tot;
-        const int ht = a.nt * D;
-        bf16 *orow = const_cast<bf16 *>(a.out) + ((int64_t)my_q * a.batch + bi) * ht + head * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            u32x2 w2{pack_bf2(acc_o[db][0] * inv, acc_o[db][1] * inv), pack_bf2(acc_o[db][2] * inv, acc_o[db][3] * inv)};
-            *(u32x2 *)(orow + db * 16 + 4 * g) = w2;
-        }
-        if (g == 0) a.lse[(int64_t)bh * a.seq + my_q] = (m_run + log2f(l_tot)) * kLn2;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Backward
@@ -280,246 +65,6 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(int batch, int nt, int 
     float s = 0.f;
     for (int j = 0; j < d; ++j) s += to_f32(o[base + j]) * to_f32(dout[base + j]);
     delta[((int64_t)bi * nt + head) * seq + p] = s;
-}
-
-// dK, dV for the keys of tile blockIdx.x (keys [0, q1)), over the call's
-// queries [q0, q1).
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16(AttnP a) {
-    constexpr int KS = D / 32, DB = D / 16;
-    __shared__ __attribute__((aligned(16))) char q_lds[64 * D * 2];
-    __shared__ __attribute__((aligned(16))) char qt_lds[64 * D * 2];
-    __shared__ __attribute__((aligned(16))) char do_lds[64 * D * 2];
-    __shared__ __attribute__((aligned(16))) char dot_lds[64 * D * 2];
-    __shared__ float lse_lds[64], del_lds[64];
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
-    const int kt0 = blockIdx.x * 64;
-    const int kw0 = kt0 + w * 16;
-    const int my_k = kw0 + li;
-    const int ht = a.nt * D;
-    const int64_t slab = (int64_t)bh * a.seq * D;
-    const float sl2 = a.scale * kLog2e;
-
-    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
-    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
-    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
-    // dO lives token-major [s, b, ht]: rows of one (bi, head) are batch*ht apart
-    const uint32_t do_bytes = (uint32_t)(((int64_t)a.seq * a.batch * ht) * 2);
-    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, do_bytes);
-
-    bf16x8 kreg[KS], vreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        uint32_t off = my_k < a.q1 ? (uint32_t)((slab + (int64_t)my_k * D + s * 32 + g * 8) * 2) : kOOB;
-        kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-        vreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
-    }
-    f32x4 acc_dk[DB], acc_dv[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x4{}; acc_dv[i] = f32x4{}; }
-
-    const int qstart = max(a.q0, kt0);
-    const int nqt = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
-    RowTile<D> qr, dor;
-    ColTile<D> qc, doc;
-    // dO rows for (bi, head): element (p, j) at (p*batch + bi)*ht + head*D + j.
-    // The tile loaders take rows `D` apart from `base`, so dO goes through a
-    // per-row address instead (below).
-    auto load_tile = [&](int p0) {
-        qr.load(rq, slab, p0, a.q1, tid);
-        qc.load(rq, slab, p0, a.q1, tid);
-#pragma unroll
-        for (int i = 0; i < RowTile<D>::VEC; ++i) {
-            int v = tid + i * 256;
-            int row = v / (D / 8), ch = v % (D / 8);
-            int p = p0 + row;
-            uint32_t off = p < a.q1 ? (uint32_t)((((int64_t)p * a.batch + bi) * ht + head * D + ch * 8) * 2) : kOOB;
-            dor.r[i] = buf_load16(rdo, off);
-        }
-        if (tid < ColTile<D>::NB) {
-            int ch = tid % (D / 8), kg = tid / (D / 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int p = p0 + kg * 4 + i;
-                uint32_t off = p < a.q1 ? (uint32_t)((((int64_t)p * a.batch + bi) * ht + head * D + ch * 8) * 2) : kOOB;
-                doc.r[i] = buf_load16(rdo, off);
-            }
-        }
-    };
-    if (nqt > 0) load_tile(qstart);
-    for (int qt = 0; qt < nqt; ++qt) {
-        const int p0 = qstart + qt * 64;
-        qr.store_rows(q_lds, tid);
-        qc.store_cols(qt_lds, tid);
-        dor.store_rows(do_lds, tid);
-        doc.store_cols(dot_lds, tid);
-        if (tid < 64) {
-            int p = p0 + tid;
-            bool ok = p < a.q1;
-            lse_lds[tid] = ok ? a.lse[(int64_t)bh * a.seq + p] * kLog2e : INFINITY;
-            del_lds[tid] = ok ? a.delta[(int64_t)bh * a.seq + p] : 0.f;
-        }
-        __syncthreads();
-        if (qt + 1 < nqt) load_tile(p0 + 64);
-        if (p0 + 63 >= kw0) {  // some query of the tile sees some key of this wave
-            f32x4 sp[4], dp[4];
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                sp[qb] = f32x4{};
-                dp[qb] = f32x4{};
-#pragma unroll
-                for (int st = 0; st < KS; ++st) {
-                    bf16x8 qa = *(const bf16x8 *)(q_lds + rowtile_off<D>(qb * 16 + li, st * 4 + g));
-                    bf16x8 da = *(const bf16x8 *)(do_lds + rowtile_off<D>(qb * 16 + li, st * 4 + g));
-                    sp[qb] = mfma16(qa, kreg[st], sp[qb]);
-                    dp[qb] = mfma16(da, vreg[st], dp[qb]);
-                }
-            }
-            // sp[qb][v]: S[query = p0 + qb*16 + 4g + v][key = my_k]
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    int qi = qb * 16 + 4 * g + v;
-                    int p = p0 + qi;
-                    float pr = (my_k <= p) ? exp2f(sp[qb][v] * sl2 - lse_lds[qi]) : 0.f;
-                    sp[qb][v] = pr;
-                    dp[qb][v] = pr * (dp[qb][v] - del_lds[qi]);
-                }
-            bf16x8 pb[2] = {pack8(sp[0], sp[1]), pack8(sp[2], sp[3])};
-            bf16x8 sb[2] = {pack8(dp[0], dp[1]), pack8(dp[2], dp[3])};
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    acc_dv[db] = mfma16(read_cols(dot_lds, db * 16 + li, st, g), pb[st], acc_dv[db]);
-                    acc_dk[db] = mfma16(read_cols(qt_lds, db * 16 + li, st, g), sb[st], acc_dk[db]);
-                }
-        }
-        __syncthreads();
-    }
-    if (my_k >= a.q1) return;
-    // acc_dk[db][v] = dK[key = my_k][d = db*16 + 4g + v] / scale (same for dV, unscaled)
-    const int64_t arow = slab + (int64_t)my_k * D;
-    const bool final_key = my_k >= a.k_final0;
-    bf16 *dst = a.out + ((int64_t)my_k * a.batch + bi) * (3 * ht) + head * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const int j = db * 16 + 4 * g;
-        f32x4 dk = acc_dk[db] * a.scale, dv = acc_dv[db];
-        if (a.acc_in) {
-            dk += *(const f32x4 *)(a.dk_acc + arow + j);
-            dv += *(const f32x4 *)(a.dv_acc + arow + j);
-        }
-        if (final_key) {
-            *(u32x2 *)(dst + ht + j) = u32x2{pack_bf2(dk[0], dk[1]), pack_bf2(dk[2], dk[3])};
-            *(u32x2 *)(dst + 2 * ht + j) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
-        } else {
-            *(f32x4 *)(a.dk_acc + arow + j) = dk;
-            *(f32x4 *)(a.dv_acc + arow + j) = dv;
-        }
-    }
-}
-
-// dQ for the query tile blockIdx.x of [q0, q1), over keys [0, q1).
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_bf16(AttnP a) {
-    constexpr int KS = D / 32, DB = D / 16;
-    __shared__ __attribute__((aligned(16))) char k_lds[64 * D * 2];
-    __shared__ __attribute__((aligned(16))) char kt_lds[64 * D * 2];
-    __shared__ __attribute__((aligned(16))) char v_lds[64 * D * 2];
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
-    const int qt0 = a.q0 + blockIdx.x * 64;
-    const int qw0 = qt0 + w * 16;
-    const int my_q = qw0 + li;
-    const int q_eff = min(my_q, a.q1 - 1);
-    const int kend = min(a.q1, qt0 + 64);
-    const int ht = a.nt * D;
-    const int64_t slab = (int64_t)bh * a.seq * D;
-    const float sl2 = a.scale * kLog2e;
-
-    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
-    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
-    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
-    const uint32_t do_bytes = (uint32_t)(((int64_t)a.seq * a.batch * ht) * 2);
-    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, do_bytes);
-
-    bf16x8 qreg[KS], doreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        bool ok = my_q < a.q1;
-        uint32_t off = ok ? (uint32_t)((slab + (int64_t)my_q * D + s * 32 + g * 8) * 2) : kOOB;
-        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-        uint32_t offd = ok ? (uint32_t)((((int64_t)my_q * a.batch + bi) * ht + head * D + s * 32 + g * 8) * 2) : kOOB;
-        doreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, offd));
-    }
-    const float lse2 = my_q < a.q1 ? a.lse[(int64_t)bh * a.seq + my_q] * kLog2e : INFINITY;
-    const float del = my_q < a.q1 ? a.delta[(int64_t)bh * a.seq + my_q] : 0.f;
-
-    f32x4 acc_dq[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) acc_dq[i] = f32x4{};
-
-    RowTile<D> kr, vr;
-    ColTile<D> kc;
-    const int nkt = (kend + 63) / 64;
-    kr.load(rk, slab, 0, kend, tid);
-    kc.load(rk, slab, 0, kend, tid);
-    vr.load(rv, slab, 0, kend, tid);
-    for (int kt = 0; kt < nkt; ++kt) {
-        kr.store_rows(k_lds, tid);
-        kc.store_cols(kt_lds, tid);
-        vr.store_rows(v_lds, tid);
-        __syncthreads();
-        if (kt + 1 < nkt) {
-            kr.load(rk, slab, (kt + 1) * 64, kend, tid);
-            kc.load(rk, slab, (kt + 1) * 64, kend, tid);
-            vr.load(rv, slab, (kt + 1) * 64, kend, tid);
-        }
-        const int key0 = kt * 64;
-        if (key0 <= qw0 + 15) {
-            f32x4 sp[4], dp[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                sp[kb] = f32x4{};
-                dp[kb] = f32x4{};
-#pragma unroll
-                for (int st = 0; st < KS; ++st) {
-                    bf16x8 ka = *(const bf16x8 *)(k_lds + rowtile_off<D>(kb * 16 + li, st * 4 + g));
-                    bf16x8 va = *(const bf16x8 *)(v_lds + rowtile_off<D>(kb * 16 + li, st * 4 + g));
-                    sp[kb] = mfma16(ka, qreg[st], sp[kb]);
-                    dp[kb] = mfma16(va, doreg[st], dp[kb]);
-                }
-            }
-            // sp[kb][v]: S^T[key = key0 + kb*16 + 4g + v][query = my_q]
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    int key = key0 + kb * 16 + 4 * g + v;
-                    float pr = key <= q_eff ? exp2f(sp[kb][v] * sl2 - lse2) : 0.f;
-                    dp[kb][v] = pr * (dp[kb][v] - del);
-                }
-            bf16x8 sb[2] = {pack8(dp[0], dp[1]), pack8(dp[2], dp[3])};
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    acc_dq[db] = mfma16(read_cols(kt_lds, db * 16 + li, st, g), sb[st], acc_dq[db]);
-        }
-        __syncthreads();
-    }
-    if (my_q >= a.q1) return;
-    bf16 *dst = a.out + ((int64_t)my_q * a.batch + bi) * (3 * ht) + head * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        f32x4 dq = acc_dq[db] * a.scale;
-        *(u32x2 *)(dst + db * 16 + 4 * g) = u32x2{pack_bf2(dq[0], dq[1]), pack_bf2(dq[2], dq[3])};
-    }
 }
 
 // ---------------------------------------------------------------------------

@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include <algorithm>
 #include <atomic>
 
 #include "trace.h"
@@ -146,8 +147,23 @@ struct EpiQkv {
     }
 };
 
+// Partial products of a split reduction: split blockIdx.y writes its fp32
+// tile to ws + blockIdx.y * stride (rows of ldc floats).
+struct EpiSplit {
+    float *ws;
+    int64_t ldc, stride;
+    __device__ __forceinline__ void operator()(int m, int n, float v) const {
+        ws[blockIdx.y * stride + m * ldc + n] = v;
+    }
+    __device__ __forceinline__ void row8(int m, int n, const float v[8]) const {
+        store8(ws + blockIdx.y * stride + m * ldc + n, v);
+    }
+};
+
 struct GemmArgs {
     int M, N, K;
+    int kc;      // reduction length per split: workgroup row blockIdx.y covers [y*kc, min(K, (y+1)*kc))
+    int nsplit;  // number of splits (gridDim.y)
     const void *a;
     int64_t lda;
     uint32_t a_bytes;
@@ -341,12 +357,13 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int nkt = (g.K + BK - 1) / BK;
+    const int kbase = blockIdx.y * g.kc, kend = min(g.K, kbase + g.kc);
+    const int nkt = kend > kbase ? (kend - kbase + BK - 1) / BK : 0;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
         if (s < nkt) {
-            OpA::issue(ra, smem + s * STAGE, m0, s * BK, g.M, g.K, g.lda, wid, lane);
-            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, s * BK, g.N, g.K, g.ldb, wid, lane);
+            OpA::issue(ra, smem + s * STAGE, m0, kbase + s * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, kbase + s * BK, g.N, kend, g.ldb, wid, lane);
         }
     }
     for (int kt = 0; kt < nkt; ++kt) {
@@ -367,8 +384,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // no LDS read moves above the barrier
         if (kt + S - 1 < nkt) {
             char *st = smem + ((kt + S - 1) % S) * STAGE;
-            OpA::issue(ra, st, m0, (kt + S - 1) * BK, g.M, g.K, g.lda, wid, lane);
-            OpB::issue(rb, st + OpA::kBytes, n0, (kt + S - 1) * BK, g.N, g.K, g.ldb, wid, lane);
+            OpA::issue(ra, st, m0, kbase + (kt + S - 1) * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, st + OpA::kBytes, n0, kbase + (kt + S - 1) * BK, g.N, kend, g.ldb, wid, lane);
         }
         const char *cur = smem + (kt % S) * STAGE;
 #pragma unroll
@@ -454,7 +471,8 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int nkt = (g.K + BK - 1) / BK;
+    const int kbase = blockIdx.y * g.kc, kend = min(g.K, kbase + g.kc);
+    const int nkt = kend > kbase ? (kend - kbase + BK - 1) / BK : 0;
     if (nkt > 0) {
         // Stages are always filled S tiles ahead: loads past the end of K
         // read as zeros (their stages are never consumed), so the number of
@@ -462,8 +480,8 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
         // has no branches for the scheduler to stop at.
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            OpA::issue(ra, smem + s * STAGE, m0, s * BK, g.M, g.K, g.lda, wid, lane);
-            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, s * BK, g.N, g.K, g.ldb, wid, lane);
+            OpA::issue(ra, smem + s * STAGE, m0, kbase + s * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, kbase + s * BK, g.N, kend, g.ldb, wid, lane);
         }
         wait_vmcnt<LPT * (S - 1)>();  // tile 0 has landed
         __builtin_amdgcn_s_barrier();
@@ -510,8 +528,8 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
             wait_vmcnt<LPT * (S - 2)>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            OpA::issue(ra, smem + stage * STAGE, m0, (kt + S) * BK, g.M, g.K, g.lda, wid, lane);
-            OpB::issue(rb, smem + stage * STAGE + OpA::kBytes, n0, (kt + S) * BK, g.N, g.K, g.ldb, wid, lane);
+            OpA::issue(ra, smem + stage * STAGE, m0, kbase + (kt + S) * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, smem + stage * STAGE + OpA::kBytes, n0, kbase + (kt + S) * BK, g.N, kend, g.ldb, wid, lane);
             stage = stage + 1 == S ? 0 : stage + 1;
             reads(smem + stage * STAGE, 0, 0);
             mfmas((KSTEPS - 1) & 1);
@@ -572,6 +590,27 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, Epi epi) {
         }
 }
 
+// Sums the nsplit partial products of each output element in split order and
+// applies the product's epilogue to 8 consecutive columns per thread.
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws, int nsplit, int M, int N,
+                                                            Epi epi) {
+    const int64_t i = blockIdx.x * 256LL + threadIdx.x;
+    const int n8 = N >> 3;
+    if (i >= (int64_t)M * n8) return;
+    const int m = (int)(i / n8), n = (int)(i % n8) * 8;
+    const int64_t stride = (int64_t)M * N;
+    float v[8];
+    load8(ws + (int64_t)m * N + n, v);
+    for (int sp = 1; sp < nsplit; ++sp) {
+        float x[8];
+        load8(ws + sp * stride + (int64_t)m * N + n, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] += x[j];
+    }
+    epi.row8(m, n, v);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -592,7 +631,8 @@ static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
         attr_set = true;
     }
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
-    hipLaunchKernelGGL((gemm_bf16_dl_kernel<C, AK, BK_, E>), dim3(tiles), dim3(C::kThreads), C::kLds, st, g, epi, 4);
+    hipLaunchKernelGGL((gemm_bf16_dl_kernel<C, AK, BK_, E>), dim3(tiles, g.nsplit), dim3(C::kThreads), C::kLds, st, g,
+                       epi, 4);
     return hipGetLastError();
 }
 
@@ -606,7 +646,8 @@ static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
         attr_set = true;
     }
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
-    hipLaunchKernelGGL((gemm_bf16_pp_kernel<C, AK, BK_, E>), dim3(tiles), dim3(C::kThreads), C::kLds, st, g, epi, 4);
+    hipLaunchKernelGGL((gemm_bf16_pp_kernel<C, AK, BK_, E>), dim3(tiles, g.nsplit), dim3(C::kThreads), C::kLds, st, g,
+                       epi, 4);
     return hipGetLastError();
 }
 
@@ -624,6 +665,8 @@ using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups pe
 enum class Tile { Dl128, Pp128, Pp256x128, Pp256 };
 
 static std::atomic<int> g_force_tile{-1};
+
+constexpr int64_t kSplitMaxFloats = 512LL * 128 * 128;  // 32 MB: about two rounds of 128x128 tiles
 
 void gemm_force_tile(int tile) { g_force_tile.store(tile); }
 
@@ -677,47 +720,63 @@ static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
     }
 }
 
-template <typename T, bool AK, bool BK_>
-static hipError_t dispatch_epi(const GemmArgs &g, Epi kind, const EpiArgs &e, hipStream_t st) {
+// Calls f with the epilogue functor of `kind`.
+template <typename T, class F>
+static hipError_t with_epi(Epi kind, const EpiArgs &e, F &&f) {
     switch (kind) {
-    case Epi::StoreF32:
-        return launch<T, AK, BK_>(g, EpiStoreF32<T>{(float *)e.c, e.ldc}, st);
-    case Epi::AccumF32:
-        return launch<T, AK, BK_>(g, EpiAccumF32<T>{(float *)e.c, e.ldc}, st);
-    case Epi::Store:
-        return launch<T, AK, BK_>(g, EpiStore<T>{(T *)e.c, e.ldc}, st);
-    case Epi::BiasGelu:
-        return launch<T, AK, BK_>(g, EpiBiasGelu<T>{(T *)e.c, e.ldc, (T *)e.c2, e.ldc2, (const T *)e.bias}, st);
-    case Epi::GeluGrad:
-        return launch<T, AK, BK_>(g, EpiGeluGrad<T>{(T *)e.c, e.ldc, (const T *)e.aux, e.ldaux}, st);
+    case Epi::StoreF32: return f(EpiStoreF32<T>{(float *)e.c, e.ldc});
+    case Epi::AccumF32: return f(EpiAccumF32<T>{(float *)e.c, e.ldc});
+    case Epi::Store: return f(EpiStore<T>{(T *)e.c, e.ldc});
+    case Epi::BiasGelu: return f(EpiBiasGelu<T>{(T *)e.c, e.ldc, (T *)e.c2, e.ldc2, (const T *)e.bias});
+    case Epi::GeluGrad: return f(EpiGeluGrad<T>{(T *)e.c, e.ldc, (const T *)e.aux, e.ldaux});
     case Epi::Qkv: {
         int dshift = 0;
         while ((1 << dshift) < e.d) ++dshift;
-        return launch<T, AK, BK_>(g,
-                                  EpiQkv<T>{(const T *)e.bias, (T *)e.q, (T *)e.k, (T *)e.v,
-                                            make_fastdiv((uint32_t)e.batch), e.nt, e.seq, dshift, e.ht,
-                                            e.row0},
-                                  st);
+        return f(EpiQkv<T>{(const T *)e.bias, (T *)e.q, (T *)e.k, (T *)e.v, make_fastdiv((uint32_t)e.batch), e.nt,
+                           e.seq, dshift, e.ht, e.row0});
     }
     }
     return hipErrorInvalidValue;
 }
 
+template <typename T, bool AK, bool BK_>
+static hipError_t dispatch_epi(const GemmArgs &g, Epi kind, const EpiArgs &e, float *split_ws, hipStream_t st) {
+    if (split_ws) return launch<T, AK, BK_>(g, EpiSplit{split_ws, g.N, (int64_t)g.M * g.N}, st);
+    return with_epi<T>(kind, e, [&](auto epi) { return launch<T, AK, BK_>(g, epi, st); });
+}
+
 template <typename T>
-static hipError_t dispatch_layout(const GemmArgs &g, bool ak, bool bk, Epi kind, const EpiArgs &e,
+static hipError_t dispatch_layout(const GemmArgs &g, bool ak, bool bk, Epi kind, const EpiArgs &e, float *split_ws,
                                   hipStream_t st) {
     // The layer uses three operand forms: forward (K, K), input gradient
     // (K, N-contiguous) and weight gradient (M-contiguous, N-contiguous).
-    if (ak && bk) return dispatch_epi<T, true, true>(g, kind, e, st);
-    if (ak && !bk) return dispatch_epi<T, true, false>(g, kind, e, st);
-    if (!ak && !bk) return dispatch_epi<T, false, false>(g, kind, e, st);
+    if (ak && bk) return dispatch_epi<T, true, true>(g, kind, e, split_ws, st);
+    if (ak && !bk) return dispatch_epi<T, true, false>(g, kind, e, split_ws, st);
+    if (!ak && !bk) return dispatch_epi<T, false, false>(g, kind, e, split_ws, st);
     return hipErrorInvalidValue;
 }
+
+// Number of reduction splits: a product whose 128x128 tiles do not fill the
+// compute units (short token ranges, narrow outputs) splits its reduction
+// so that about two workgroups per compute unit run, when the caller's
+// workspace holds the partial products (at most kSplitMaxFloats floats).
+static int pick_splits(int M, int N, int K, Tile t, int64_t ws_floats) {
+    if (t != Tile::Dl128 && t != Tile::Pp128) return 1;
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles >= 256) return 1;
+    int sp = (int)((512 + tiles / 2) / tiles);
+    sp = std::min(sp, 8);
+    sp = std::min(sp, K / 512);
+    while (sp > 1 && (int64_t)sp * M * N > ws_floats) --sp;
+    return std::max(sp, 1);
+}
+
+size_t gemm_split_workspace_floats() { return kSplitMaxFloats; }
 
 hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const EpiArgs &e, hipStream_t st) {
     if (M <= 0 || N <= 0) return hipSuccess;
     const int es = dt == DType::BF16 ? 2 : 4;
-    GemmArgs g;
+    GemmArgs g{};
     g.M = M;
     g.N = N;
     g.K = K;
@@ -731,14 +790,19 @@ hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const Epi
     }
     g.a_bytes = K > 0 ? extent_bytes(M, K, A, es) : 0;
     g.b_bytes = K > 0 ? extent_bytes(N, K, B, es) : 0;
+    const Tile tile = pick_tile(M, N, K, A.kcontig, B.kcontig);
+    const int nsplit = dt == DType::BF16 && e.split_ws ? pick_splits(M, N, g.K, tile, e.split_ws_floats) : 1;
+    g.nsplit = nsplit;
+    g.kc = nsplit > 1 ? ((g.K + nsplit - 1) / nsplit + 63) / 64 * 64 : g.K;
     // algorithmic work: 2MNK flops; A and B read once, C written once (read
     // too when accumulated), plus the epilogue's extra operand or output
     static const char *kEpiName[] = {"store_f32", "accum_f32", "store", "bias_gelu", "gelu_grad", "qkv"};
     const char *lay = A.kcontig ? (B.kcontig ? "nt" : "nn") : "tn";
     char name[64];
-    if (dt == DType::BF16)
-        snprintf(name, sizeof name, "gemm_bf16_%s_%s_%s", tile_name(pick_tile(M, N, K, A.kcontig, B.kcontig)), lay,
-                 kEpiName[(int)kind]);
+    if (dt == DType::BF16 && nsplit > 1)
+        snprintf(name, sizeof name, "gemm_bf16_%s_%s_%s_split", tile_name(tile), lay, kEpiName[(int)kind]);
+    else if (dt == DType::BF16)
+        snprintf(name, sizeof name, "gemm_bf16_%s_%s_%s", tile_name(tile), lay, kEpiName[(int)kind]);
     else
         snprintf(name, sizeof name, "gemm_f32_%s_%s", lay, kEpiName[(int)kind]);
     const double mn = (double)M * N;
@@ -748,8 +812,16 @@ hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const Epi
     if (kind == Epi::BiasGelu && e.c) out_b = 2 * mn * es;
     if (kind == Epi::GeluGrad) out_b = 2 * mn * es;
     TraceScope ts(st, name, 2.0 * mn * K, ((double)M * K + (double)N * K) * es + out_b);
-    if (dt == DType::BF16) return dispatch_layout<bf16>(g, A.kcontig, B.kcontig, kind, e, st);
-    return dispatch_layout<float>(g, A.kcontig, B.kcontig, kind, e, st);
+    if (dt != DType::BF16) return dispatch_layout<float>(g, A.kcontig, B.kcontig, kind, e, nullptr, st);
+    if (nsplit == 1) return dispatch_layout<bf16>(g, A.kcontig, B.kcontig, kind, e, nullptr, st);
+    hipError_t err = dispatch_layout<bf16>(g, A.kcontig, B.kcontig, kind, e, e.split_ws, st);
+    if (err != hipSuccess) return err;
+    const int64_t threads = (int64_t)M * (N / 8);
+    return with_epi<bf16>(kind, e, [&](auto epi) {
+        hipLaunchKernelGGL((splitk_reduce_kernel<decltype(epi)>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                           0, st, e.split_ws, nsplit, M, N, epi);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace tpk

@@ -38,12 +38,18 @@ struct EpiArgs {
     // Qkv scatter: token row m of the call is global row row0 + m = p*batch + bi
     void *q = nullptr, *k = nullptr, *v = nullptr;
     int batch = 1, seq = 1, nt = 1, d = 64, ht = 64, row0 = 0;
+    // workspace for split reductions (fp32, split_ws_floats floats); a
+    // product may split its reduction over workgroups when it is given
+    float *split_ws = nullptr;
+    int64_t split_ws_floats = 0;
 };
 
 hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const EpiArgs &e,
                 hipStream_t st);
 // -1: tile configuration chosen per shape; 0..3: forced (see tp_gemm_force_tile)
 void gemm_force_tile(int tile);
+// floats of split-reduction workspace that lets every product split
+size_t gemm_split_workspace_floats();
 
 // LayerNorm forward over rows [0, rows): u = LN(x) * g + b; mean/rstd fp32.
 hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, const void *g,
