@@ -50,6 +50,7 @@ __all__ = [
     "layer_norm", "layer_norm_backward",
     "heads_split", "heads_merge",
     "causal_attention", "causal_attention_backward",
+    "attention_block", "merge_partials",
     "layer_forward", "layer_backward",
     "shard_params", "new_kv_cache", "new_kv_grad",
     "shard_attn_forward", "shard_mlp_forward",
@@ -185,6 +186,67 @@ def causal_attention_backward(do, q, k, v, p, o):
     dq = (ds @ k) / math.sqrt(d)
     dk = (np.swapaxes(ds, -1, -2) @ q) / math.sqrt(d)
     return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# Attention over one block of keys and values, and the merge of two partial
+# results ([TT11], the passage on very long sequences: each device keeps its
+# own queries and receives every device's keys and values, passed round a
+# ring while it computes).  A device therefore sees the keys one block at a
+# time; the exact result over all keys follows from the per-block results by
+# the log-sum-exp identity (a reading: the pages do not spell out how blocks
+# are combined, and exact attention over the union is the plainest one).
+# ----------------------------------------------------------------------------
+
+def attention_block(q, k, v, q_pos0, k_pos0):
+    """Causal attention of queries at positions q_pos0 .. q_pos0+Lq-1 over
+    one block of keys at positions k_pos0 .. k_pos0+Lk-1.
+
+    q: [b, n, Lq, d]; k, v: [b, n, Lk, d].  Query at position p sees the
+    block's keys at positions j <= p.  Returns (o, lse): o_p = sum_j P_pj v_j
+    with P the softmax over the visible keys of the block, lse_p = log sum_j
+    exp(q_p . k_j / sqrt(d)) over the same keys; a query that sees none of
+    the block's keys gets o = 0 and lse = -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[-1]
+    lq, lk = q.shape[-2], k.shape[-2]
+    scores = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(d)
+    pos_q = q_pos0 + np.arange(lq)
+    pos_k = k_pos0 + np.arange(lk)
+    visible = pos_k[None, :] <= pos_q[:, None]
+    scores = np.where(visible, scores, -np.inf)
+    any_visible = visible.any(axis=-1)
+    row_max = np.where(any_visible, scores.max(axis=-1), 0.0)[..., None]
+    e = np.where(visible, np.exp(scores - row_max), 0.0)
+    denom = e.sum(axis=-1, keepdims=True)
+    safe = np.where(denom > 0, denom, 1.0)
+    o = (e / safe) @ v
+    lse = np.where(any_visible, (row_max + np.log(safe))[..., 0], -np.inf)
+    return o, lse
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets from the results
+    over each: with m = max(lse_a, lse_b), w_x = exp(lse_x - m),
+    o = (w_a o_a + w_b o_b) / (w_a + w_b) and lse = m + log(w_a + w_b).  A
+    side with lse = -inf (no visible key) has weight 0; if both are -inf the
+    result is o = 0, lse = -inf."""
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(lse_a, lse_b)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w_a = np.where(np.isneginf(lse_a), 0.0, np.exp(lse_a - m_safe))
+    w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))
+    tot = w_a + w_b
+    tot_safe = np.where(empty, 1.0, tot)
+    o = (w_a[..., None] * o_a + w_b[..., None] * o_b) / tot_safe[..., None]
+    lse = np.where(empty, -np.inf, m_safe + np.log(tot_safe))
+    return o, lse
 
 
 # ----------------------------------------------------------------------------

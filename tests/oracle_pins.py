@@ -253,3 +253,64 @@ def cube_error(orc, seed=4):
 
 def math_erf_ok():
     return abs(math.erf(1.0) - 0.8427007929497149) < 1e-15
+
+
+def brute_block_attention(q, k, v, q_pos0, k_pos0):
+    """Pure-Python loops: for each query, the softmax over the visible keys
+    of the block written out term by term (positions compared directly)."""
+    b, n, lq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    lk = len(k[0][0])
+    o = [[[[0.0] * d for _ in range(lq)] for _ in range(n)] for _ in range(b)]
+    lse = [[[float("-inf")] * lq for _ in range(n)] for _ in range(b)]
+    for bi in range(b):
+        for h in range(n):
+            for i in range(lq):
+                s = []
+                for j in range(lk):
+                    if k_pos0 + j <= q_pos0 + i:
+                        dot = sum(q[bi][h][i][x] * k[bi][h][j][x] for x in range(d))
+                        s.append((j, dot / math.sqrt(d)))
+                if not s:
+                    continue
+                z = sum(math.exp(val) for _, val in s)
+                lse[bi][h][i] = math.log(z)
+                for j, val in s:
+                    w = math.exp(val) / z
+                    for x in range(d):
+                        o[bi][h][i][x] += w * v[bi][h][j][x]
+    return o, lse
+
+
+def ring_error(orc, seed=5):
+    """Largest deviation of (a) attention_block against the brute force, for
+    blocks before, overlapping and after the queries, and (b) the merge of
+    per-block results over a partition of the keys against the brute force
+    over all keys."""
+    rng = np.random.default_rng(seed)
+    b, n, d = 2, 2, 4
+    q_pos0, lq = 5, 4
+    lk_total = q_pos0 + lq + 2  # two keys past the last query
+    q = rng.normal(size=(b, n, lq, d))
+    k = rng.normal(size=(b, n, lk_total, d))
+    v = rng.normal(size=(b, n, lk_total, d))
+    err = 0.0
+    blocks = [(0, 3), (3, 6), (6, 9), (9, lk_total)]
+    acc = None
+    for k0, k1 in blocks:
+        o, lse = orc.attention_block(q, k[:, :, k0:k1], v[:, :, k0:k1], q_pos0, k0)
+        bo, bl = brute_block_attention(q.tolist(), k[:, :, k0:k1].tolist(), v[:, :, k0:k1].tolist(), q_pos0, k0)
+        bo, bl = np.array(bo), np.array(bl)
+        fin = np.isfinite(bl)
+        if not np.array_equal(fin, np.isfinite(lse)):
+            return float("inf")
+        err = max(err, float(np.abs(o - bo).max()), float(np.abs(lse[fin] - bl[fin]).max()) if fin.any() else 0.0)
+        acc = (o, lse) if acc is None else orc.merge_partials(acc[0], acc[1], o, lse)
+    fo, fl = brute_block_attention(q.tolist(), k.tolist(), v.tolist(), q_pos0, 0)
+    err = max(err, float(np.abs(acc[0] - np.array(fo)).max()), float(np.abs(acc[1] - np.array(fl)).max()))
+    # merging in the other order gives the same result
+    rev = None
+    for k0, k1 in reversed(blocks):
+        o, lse = orc.attention_block(q, k[:, :, k0:k1], v[:, :, k0:k1], q_pos0, k0)
+        rev = (o, lse) if rev is None else orc.merge_partials(rev[0], rev[1], o, lse)
+    err = max(err, float(np.abs(rev[0] - acc[0]).max()), float(np.abs(rev[1] - acc[1]).max()))
+    return err

@@ -44,6 +44,14 @@ MUTANTS = [
     ("shard_mlp_backward", 'return _mm(dz, sp["w1"]), gr', 'return _mm(dg, sp["w1"]), gr'),
     ("ln1_backward", 'return np.asarray(dh_rows, dtype=np.float64) + dln1', 'return dln1'),
     ("cube_ffn_block", "return gelu(x @", "return (x @"),
+    ("attention_block", "visible = pos_k[None, :] <= pos_q[:, None]", "visible = pos_k[None, :] < pos_q[:, None]"),
+    ("attention_block", "pos_k = k_pos0 + np.arange(lk)", "pos_k = np.arange(lk)"),
+    ("attention_block", "e = np.where(visible, np.exp(scores - row_max), 0.0)", "e = np.where(visible, np.exp(scores), 0.0)"),
+    ("merge_partials", "o = (w_a[..., None] * o_a + w_b[..., None] * o_b) / tot_safe[..., None]",
+     "o = (w_a[..., None] * o_a + w_b[..., None] * o_b)"),
+    ("merge_partials", "lse = np.where(empty, -np.inf, m_safe + np.log(tot_safe))", "lse = np.where(empty, -np.inf, m_safe)"),
+    ("merge_partials", "w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))",
+     "w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_a - m_safe))"),
 ]
 
 
@@ -59,6 +67,7 @@ def _pin_failures(orc):
         ("tp-2-ranks", lambda: pins.tp_error(orc, 2, [6]) < 1e-12),
         ("slices", lambda: pins.tp_error(orc, 2, [2, 1, 3]) < 1e-12),
         ("cube", lambda: pins.cube_error(orc) < 1e-12),
+        ("ring", lambda: pins.ring_error(orc) < 1e-12),
     ]
     for name, ok in checks:
         with np.errstate(all="ignore"):

@@ -89,3 +89,30 @@ def test_shard_layer_step_single_rank():
     assert np.abs(r3["dx"] - gr["x"]).max() < 1e-12
     for k in ("ln1_g", "ln2_g", "b_o", "b2", "w1", "w2"):
         assert np.abs(r3["grads"][k] - gr[k]).max() < 1e-12
+
+
+def test_attention_block_and_merge_match_brute_force():
+    """Blocks before, across and after the queries, and the merge of all
+    blocks (in either order) equal to attention over every key, both
+    against pure-Python loops."""
+    assert pins.ring_error(oracle) < 1e-12
+
+
+def test_attention_block_special_cases():
+    rng = np.random.default_rng(11)
+    q = rng.normal(size=(1, 2, 3, 4))
+    k = rng.normal(size=(1, 2, 5, 4))
+    v = rng.normal(size=(1, 2, 5, 4))
+    # every key after every query: nothing visible
+    o, lse = oracle.attention_block(q, k, v, q_pos0=10, k_pos0=13)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # merging with an empty result changes nothing
+    o2, l2 = oracle.attention_block(q, k, v, q_pos0=10, k_pos0=8)
+    mo, ml = oracle.merge_partials(o2, l2, o, lse)
+    assert np.array_equal(mo, o2) and np.array_equal(ml, l2)
+    mo, ml = oracle.merge_partials(o, lse, o, lse)
+    assert np.all(mo == 0) and np.all(np.isneginf(ml))
+    # the first query sees exactly one key of a block starting at its position
+    o1, l1 = oracle.attention_block(q, k, v, q_pos0=4, k_pos0=4)
+    assert np.allclose(o1[..., 0, :], v[..., 0, :], atol=1e-15)
+    assert np.allclose(l1[..., 0], (q[..., 0, :] * k[..., 0, :]).sum(-1) / 2.0, atol=1e-15)
