@@ -254,6 +254,42 @@ tp_status tp_cube_ffn_block(int32_t rows, int32_t hidden, int32_t ffn, const voi
                             const void *w1, const void *b1, const void *w2, void *hbuf,
                             float *out, void *stream);
 
+/* Attention with the keys split into blocks ("Transformer Training 11:
+ * model parallelism", the passage on very long sequences: a device keeps its
+ * own queries and receives every device's keys and values, passed round a
+ * ring while it computes).  One call takes the device's queries against one
+ * block of keys and values; tp_attn_merge combines the results of two
+ * disjoint blocks into the result over their union (log-sum-exp rule), so
+ * merging the results of all blocks gives causal attention over all keys.
+ *
+ * Shapes (the heads are this device's heads): q [batch, heads, nq,
+ * head_dim], k and v [batch, heads, nk, head_dim], bf16; queries sit at
+ * positions q_pos0 .. q_pos0+nq-1 and keys at k_pos0 .. k_pos0+nk-1, and a
+ * query at position p sees the keys at positions <= p.  Scores are
+ * q.k / sqrt(head_dim).  head_dim is 64 or 128. */
+typedef struct {
+    int32_t batch, heads, head_dim;
+    int32_t nq, nk;
+    int32_t q_pos0, k_pos0;
+} tp_attn_block_shape;
+
+/* o fp32 [batch, heads, nq, head_dim]: softmax over the block's visible keys
+ * applied to v (normalised within the block); lse fp32 [batch, heads, nq]:
+ * natural log of the sum of exp(score) over those keys.  A query that sees
+ * none of the block's keys gets o = 0 and lse = -inf.  All pointers device,
+ * 16-byte aligned, each buffer below 2 GiB; nq or nk may be 0. */
+tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, const void *k,
+                            const void *v, float *o, float *lse, void *stream);
+
+/* (o, lse) over the union of two disjoint key sets from (o_a, lse_a) and
+ * (o_b, lse_b), each shaped as tp_attn_block_fwd's outputs for `shape`
+ * (nk, q_pos0 and k_pos0 are not used): with m = max(lse_a, lse_b) and
+ * w = exp(lse - m) per side (0 for -inf), o = (w_a o_a + w_b o_b) /
+ * (w_a + w_b) and lse = m + log(w_a + w_b); -inf and o = 0 if both sides
+ * are empty.  o may be o_a or o_b and lse may be lse_a or lse_b (in place). */
+tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, const float *lse_a,
+                        const float *o_b, const float *lse_b, float *o, float *lse, void *stream);
+
 /* Per-kernel timing.  tp_trace_enable(1) discards earlier records and makes
  * every later kernel launch of the library (from any thread) record two HIP
  * events on its launch stream, with the kernel's name and the algorithmic

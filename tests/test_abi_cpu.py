@@ -175,3 +175,18 @@ def test_force_tile_range():
         assert _status(lambda: abi.tp_gemm_force_tile(bad)) == abi.TP_EINVAL
     abi.tp_gemm_force_tile(3)
     abi.tp_gemm_force_tile(-1)
+
+
+def test_block_attention_checks():
+    good = abi.tp_attn_block_shape(1, 2, 128, 10, 10, 0, 0)
+    call = lambda s, q=FAKE, o=FAKE: abi.tp_attn_block_fwd(s, q, FAKE, FAKE, o, FAKE, None)
+    assert _status(lambda: call(abi.tp_attn_block_shape(1, 2, 96, 10, 10, 0, 0))) == abi.TP_EUNSUPPORTED
+    assert _status(lambda: call(abi.tp_attn_block_shape(0, 2, 128, 10, 10, 0, 0))) == abi.TP_ESHAPE
+    assert _status(lambda: call(abi.tp_attn_block_shape(1, 2, 128, -1, 10, 0, 0))) == abi.TP_ESHAPE
+    assert _status(lambda: call(abi.tp_attn_block_shape(1, 2, 128, 10, 10, -5, 0))) == abi.TP_ESHAPE
+    assert _status(lambda: call(good, q=None)) == abi.TP_EINVAL
+    assert _status(lambda: call(good, o=FAKE + 4)) == abi.TP_EALIGN
+    merge = lambda s, o=FAKE: abi.tp_attn_merge(s, FAKE, FAKE, FAKE, FAKE, o, FAKE, None)
+    assert _status(lambda: merge(good, o=None)) == abi.TP_EINVAL
+    assert _status(lambda: merge(good, o=FAKE + 8)) == abi.TP_EALIGN
+    assert _status(lambda: merge(abi.tp_attn_block_shape(1, 2, 32, 10, 0, 0, 0))) == abi.TP_EUNSUPPORTED

@@ -19,8 +19,8 @@ TP_FWD_ATTN, TP_FWD_MLP = 0, 1
 TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1, TP_BWD_MLP_DATA, TP_BWD_ATTN_DATA, TP_BWD_WGRAD = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
-            "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_trace_enable",
-            "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
+            "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_attn_block_fwd",
+            "tp_attn_merge", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
 
 
 class TPError(RuntimeError):
@@ -60,6 +60,10 @@ class tp_trace_record(ctypes.Structure):
                 ("ms", ctypes.c_float)]
 
 
+class tp_attn_block_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "heads", "head_dim", "nq", "nk", "q_pos0", "k_pos0")]
+
+
 class tp_kv_grad(ctypes.Structure):
     _fields_ = [("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("done_from", ctypes.c_int32)]
 
@@ -93,6 +97,10 @@ def lib():
     L.tp_residual_combine.restype = ctypes.c_int
     L.tp_cube_ffn_block.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.tp_cube_ffn_block.restype = ctypes.c_int
+    L.tp_attn_block_fwd.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp]
+    L.tp_attn_block_fwd.restype = ctypes.c_int
+    L.tp_attn_merge.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp, vp]
+    L.tp_attn_merge.restype = ctypes.c_int
     L.tp_trace_enable.argtypes = [i32]
     L.tp_trace_enable.restype = None
     L.tp_trace_read.argtypes = [P(tp_trace_record), i32]
@@ -152,6 +160,14 @@ def tp_residual_combine(cfg, rows, resid, reduced, bias, out, stream):
 
 def tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream):
     _check(lib().tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream))
+
+
+def tp_attn_block_fwd(shape, q, k, v, o, lse, stream):
+    _check(lib().tp_attn_block_fwd(ctypes.byref(shape), q, k, v, o, lse, stream))
+
+
+def tp_attn_merge(shape, o_a, lse_a, o_b, lse_b, o, lse, stream):
+    _check(lib().tp_attn_merge(ctypes.byref(shape), o_a, lse_a, o_b, lse_b, o, lse, stream))
 
 
 def tp_trace_enable(on):

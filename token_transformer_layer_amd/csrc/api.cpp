@@ -494,4 +494,56 @@ tp_status tp_cube_ffn_block(int32_t rows, int32_t hidden, int32_t ffn, const voi
     return TP_OK;
 }
 
+static tp_status check_block(const tp_attn_block_shape *b) {
+    if (!b) return fail(TP_EINVAL, "shape is NULL");
+    if (b->batch <= 0 || b->heads <= 0 || b->nq < 0 || b->nk < 0 || b->q_pos0 < 0 || b->k_pos0 < 0)
+        return fail(TP_ESHAPE, "batch and heads must be positive; nq, nk and the positions non-negative");
+    if (b->head_dim != 64 && b->head_dim != 128) return fail(TP_EUNSUPPORTED, "head_dim %d is not 64 or 128", b->head_dim);
+    if ((int64_t)b->q_pos0 + b->nq > INT32_MAX || (int64_t)b->k_pos0 + b->nk > INT32_MAX)
+        return fail(TP_ESHAPE, "positions exceed int32");
+    const int64_t bh = (int64_t)b->batch * b->heads;
+    if (bh * b->nq * b->head_dim * 4 >= kMaxBuffer || bh * b->nk * b->head_dim * 2 >= kMaxBuffer)
+        return fail(TP_ESHAPE, "a tensor of this block exceeds 2 GiB");
+    return TP_OK;
+}
+
+tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, const void *k, const void *v, float *o,
+                            float *lse, void *stream) {
+    tp_status s = check_block(shape);
+    if (s != TP_OK) return s;
+    NEED(q, "q");
+    NEED(k, "k");
+    NEED(v, "v");
+    NEED(o, "o");
+    NEED(lse, "lse");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return fail(TP_EALIGN, "q, k, v, o and lse must be 16-byte aligned");
+    AttnBlockArgs a;
+    a.bh = shape->batch * shape->heads;
+    a.nq = shape->nq;
+    a.nk = shape->nk;
+    a.d = shape->head_dim;
+    a.q_pos0 = shape->q_pos0;
+    a.k_pos0 = shape->k_pos0;
+    a.scale = 1.0f / std::sqrt((float)shape->head_dim);
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    return hip_status(attn_block_fwd(a, (hipStream_t)stream), "block attention");
+}
+
+tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, const float *lse_a, const float *o_b,
+                        const float *lse_b, float *o, float *lse, void *stream) {
+    tp_status s = check_block(shape);
+    if (s != TP_OK) return s;
+    NEED(o_a, "o_a");
+    NEED(lse_a, "lse_a");
+    NEED(o_b, "o_b");
+    NEED(lse_b, "lse_b");
+    NEED(o, "o");
+    NEED(lse, "lse");
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return fail(TP_EALIGN, "o_a, o_b and o must be 16-byte aligned");
+    const int64_t rows = (int64_t)shape->batch * shape->heads * shape->nq;
+    return hip_status(attn_merge(rows, shape->head_dim, o_a, lse_a, o_b, lse_b, o, lse, (hipStream_t)stream),
+                      "attention merge");
+}
+
 }  // extern "C"

@@ -271,6 +271,80 @@ __device__ __forceinline__ void kv_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst,
     }
 }
 
+// One 64-key tile of the online softmax of the forward: scores of the tile's
+// keys (LDS [64][D] at ks, positions key0 .. key0+63, only positions <= q_pos
+// and < kmax count) for this lane's query (Q in qreg as the B operand), the
+// running maximum and sum updated and O^T += V^T P^T accumulated (V at vs).
+template <int D>
+__device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const bf16x8 (&qreg)[D / 16],
+                                         f32x16 (&acc)[D / 32], float &m_run, float &l_run, int key0, int q_pos,
+                                         int kmax, float sl2, int lane) {
+    constexpr int KS = D / 16, DB = D / 32;
+    const int g = lane >> 5, li = lane & 31;
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        sc[kb] = f32x16{};
+        const int row = kb * 32 + li;
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+            sc[kb] = mfma32(*(const bf16x8 *)(ks + kv_chunk_off<D>(row, 2 * st + g)), qreg[st], sc[kb]);
+    }
+    // sc[kb][v]: score of key key0 + 32 kb + 8(v/4) + 4g + v%4 for the lane's query
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
+            const float x = (key <= q_pos && key < kmax) ? sc[kb][v] * sl2 : -INFINITY;
+            sc[kb][v] = x;
+            mt = fmaxf(mt, x);
+        }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    // a query may see no key yet when its key range is split (m = -inf):
+    // then every weight is 0 and nothing is rescaled
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __builtin_amdgcn_exp2f(sc[kb][v] - m_use);
+            sc[kb][v] = p;
+            ls += p;
+        }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+    // P^T for key step ks (16 keys): registers 8h..8h+7 of block ks/2, h = ks%2
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const f32x16 &src = sc[ks4 >> 1];
+        const int h = (ks4 & 1) * 8;
+        u32x4 wv{pack_bf2(src[h], src[h + 1]), pack_bf2(src[h + 2], src[h + 3]), pack_bf2(src[h + 4], src[h + 5]),
+                 pack_bf2(src[h + 6], src[h + 7])};
+        pb[ks4] = __builtin_bit_cast(bf16x8, wv);
+    }
+    const int G = lane >> 4, L = lane & 15;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int col = db * 32 + 16 * (G & 1) + 4 * (L & 3);
+        const int cc = col >> 3, within = (col & 7) * 2;
+#pragma unroll
+        for (int ks4 = 0; ks4 < 4; ++ks4) {
+            const int r0 = 16 * ks4 + 4 * g + (L >> 2);
+            u32x2 lo = lds_read_tr16(vs + kv_chunk_off<D>(r0, cc) + within);
+            u32x2 hi = lds_read_tr16(vs + kv_chunk_off<D>(r0 + 8, cc) + within);
+            acc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks4], acc[db]);
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_mfma32(AttnFwdP a) {
     constexpr int KS = D / 16;  // k-steps of S^T = K Q^T
@@ -324,68 +398,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         const int key0 = t * 64;
         if (key0 > qt0 + w * 32 + 31) continue;  // every key of the tile is after this wave's queries
-        f32x16 sc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sc[kb] = f32x16{};
-            const int row = kb * 32 + li;
-#pragma unroll
-            for (int st = 0; st < KS; ++st)
-                sc[kb] = mfma32(*(const bf16x8 *)(ks + kv_chunk_off<D>(row, 2 * st + g)), qreg[st], sc[kb]);
-        }
-        // sc[kb][v]: score of key key0 + 32 kb + 8(v/4) + 4g + v%4 for query my_q
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
-                const float x = key <= q_eff ? sc[kb][v] * a.sl2 : -INFINITY;
-                sc[kb][v] = x;
-                mt = fmaxf(mt, x);
-            }
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        // a query may see no key yet when its key range is split (m = -inf):
-        // then every weight is 0 and nothing is rescaled
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(sc[kb][v] - m_use);
-                sc[kb][v] = p;
-                ls += p;
-            }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-        // P^T for key step ks (16 keys): registers 8h..8h+7 of block ks/2, h = ks%2
-        bf16x8 pb[4];
-#pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) {
-            const f32x16 &src = sc[ks4 >> 1];
-            const int h = (ks4 & 1) * 8;
-            u32x4 wv{pack_bf2(src[h], src[h + 1]), pack_bf2(src[h + 2], src[h + 3]), pack_bf2(src[h + 4], src[h + 5]),
-                     pack_bf2(src[h + 6], src[h + 7])};
-            pb[ks4] = __builtin_bit_cast(bf16x8, wv);
-        }
-        const int G = lane >> 4, L = lane & 15;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int col = db * 32 + 16 * (G & 1) + 4 * (L & 3);
-            const int cc = col >> 3, within = (col & 7) * 2;
-#pragma unroll
-            for (int ks4 = 0; ks4 < 4; ++ks4) {
-                const int r0 = 16 * ks4 + 4 * g + (L >> 2);
-                u32x2 lo = lds_read_tr16(vs + kv_chunk_off<D>(r0, cc) + within);
-                u32x2 hi = lds_read_tr16(vs + kv_chunk_off<D>(r0 + 8, cc) + within);
-                acc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks4], acc[db]);
-            }
-        }
+        fwd_tile<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_eff, kend, a.sl2, lane);
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (my_q >= a.q1) return;
@@ -792,6 +805,117 @@ __global__ __launch_bounds__(256) void attn_delta_bf16(int batch, int nt, int se
     }
 }
 
+// ---------------------------------------------------------------------------
+// Attention of queries over one block of keys and values at given positions
+// (the per-block step of attention with the keys passed round a ring), and
+// the merge of two partial results.
+//
+// A workgroup owns 128 queries of one (batch row, head) and streams the
+// block's keys that its queries can see through LDS, with the forward's tile
+// step; the result is the block's normalised O in fp32 and its log-sum-exp
+// (-inf, with O = 0, for a query that sees none of the block's keys).
+// ---------------------------------------------------------------------------
+
+struct AttnBlockP {
+    int nq, nk, q_pos0, k_pos0;
+    float sl2;
+    const bf16 *q, *k, *v;
+    float *o, *lse;
+    uint32_t q_bytes, kv_bytes;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_block_fwd_mfma32(AttnBlockP a) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE = 64 * D * 2;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
+    const int bh = blockIdx.y;
+    const int lq0 = blockIdx.x * kFwdBQ;
+    const int my_lq = lq0 + w * 32 + li;  // query index within the block's queries
+    const bool qok = my_lq < a.nq;
+    const int q_pos = a.q_pos0 + min(my_lq, a.nq - 1);  // padding queries act as the last query
+    // keys past the workgroup's last query position are never seen
+    const int last_pos = a.q_pos0 + min(lq0 + kFwdBQ - 1, a.nq - 1);
+    const int kend = max(0, min(a.nk, last_pos - a.k_pos0 + 1));
+    const int ntiles = (kend + 63) / 64;
+    const int64_t qslab = (int64_t)bh * a.nq * D, kslab = (int64_t)bh * a.nk * D;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+    bf16x8 qreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint32_t off = qok ? (uint32_t)((qslab + (int64_t)my_lq * D + s * 16 + g * 8) * 2) : kOOB;
+        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    }
+    f32x16 acc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    if (ntiles > 0) {
+        kv_tile_dma<D>(rk, smem, kslab, 0, kend, w, lane);
+        kv_tile_dma<D>(rv, smem + TILE, kslab, 0, kend, w, lane);
+    }
+    const int wave_last_pos = a.q_pos0 + lq0 + w * 32 + 31;
+    for (int t = 0; t < ntiles; ++t) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        const char *ks = smem + (t & 1) * 2 * TILE;
+        const char *vs = ks + TILE;
+        if (t + 1 < ntiles) {
+            char *nx = smem + ((t + 1) & 1) * 2 * TILE;
+            kv_tile_dma<D>(rk, nx, kslab, (t + 1) * 64, kend, w, lane);
+            kv_tile_dma<D>(rv, nx + TILE, kslab, (t + 1) * 64, kend, w, lane);
+        }
+        const int key0 = a.k_pos0 + t * 64;
+        if (key0 > wave_last_pos) continue;  // every key of the tile is after this wave's queries
+        fwd_tile<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_pos, a.k_pos0 + kend, a.sl2, lane);
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!qok) return;
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? 1.0f / l_tot : 0.f;
+    float *orow = a.o + qslab + (int64_t)my_lq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *(f32x4 *)(orow + db * 32 + 8 * r + 4 * g) =
+                f32x4{acc[db][4 * r] * inv, acc[db][4 * r + 1] * inv, acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv};
+    if (g == 0) a.lse[(int64_t)bh * a.nq + my_lq] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+}
+
+// o = (w_a o_a + w_b o_b) / (w_a + w_b), lse = m + log(w_a + w_b) with
+// m = max(lse_a, lse_b) and w_x = exp(lse_x - m) (0 for lse_x = -inf); D/8
+// threads per row, each on 8 columns (a row's threads share one wave, so the
+// outputs may overwrite either input).
+__global__ __launch_bounds__(256) void attn_merge_kernel(int64_t rows, int d, const float *oa, const float *la,
+                                                         const float *ob, const float *lb, float *o, float *lse) {
+    const int per = d >> 3;
+    const int64_t i = blockIdx.x * 256LL + threadIdx.x;
+    const int64_t row = i / per;
+    const int part = (int)(i % per);
+    if (row >= rows) return;
+    const float lA = la[row], lB = lb[row];
+    const float m = fmaxf(lA, lB);
+    const bool empty = m == -INFINITY;
+    const float wa = lA == -INFINITY ? 0.f : expf(lA - m);
+    const float wb = lB == -INFINITY ? 0.f : expf(lB - m);
+    const float tot = wa + wb;
+    const float inv = empty ? 0.f : 1.0f / tot;
+    float x[8], y[8], r[8];
+    load8(oa + row * d + part * 8, x);
+    load8(ob + row * d + part * 8, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (wa * x[j] + wb * y[j]) * inv;
+    store8(o + row * d + part * 8, r);
+    if (part == 0) lse[row] = empty ? -INFINITY : m + logf(tot);
+}
+
 }  // namespace
 
 // (query, key) pairs of the causal product for queries [q0, q1) of every
@@ -932,6 +1056,51 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
         hipLaunchKernelGGL(attn_bwd_dkdv_f32, dim3(x.q1, bh), dim3(64), 0, st, p);
         hipLaunchKernelGGL(attn_bwd_dq_f32, dim3(nq, bh), dim3(64), 0, st, p);
     }
+    return hipGetLastError();
+}
+
+// Visible (query, key) pairs of a block: query at position p sees the keys
+// at positions k_pos0 .. min(p, k_pos0 + nk - 1).
+static double block_pairs(const AttnBlockArgs &x) {
+    double n = 0;
+    for (int i = 0; i < x.nq; ++i) {
+        const int64_t p = (int64_t)x.q_pos0 + i;
+        const int64_t c = std::min<int64_t>(x.nk, p - x.k_pos0 + 1);
+        if (c > 0) n += (double)c;
+    }
+    return n * x.bh;
+}
+
+hipError_t attn_block_fwd(const AttnBlockArgs &x, hipStream_t st) {
+    if (x.nq <= 0 || x.bh <= 0) return hipSuccess;
+    TraceScope ts(st, "attn_block_fwd_bf16", 4.0 * x.d * block_pairs(x),
+                  (double)x.bh * x.d * (2.0 * x.nq + 4.0 * x.nk + 4.0 * x.nq) + 4.0 * x.bh * x.nq);
+    AttnBlockP p{};
+    p.nq = x.nq; p.nk = x.nk; p.q_pos0 = x.q_pos0; p.k_pos0 = x.k_pos0;
+    p.sl2 = x.scale * kLog2e;
+    p.q = (const bf16 *)x.q; p.k = (const bf16 *)x.k; p.v = (const bf16 *)x.v;
+    p.o = x.o; p.lse = x.lse;
+    p.q_bytes = (uint32_t)((int64_t)x.bh * x.nq * x.d * 2);
+    p.kv_bytes = (uint32_t)((int64_t)x.bh * x.nk * x.d * 2);
+    const int lds = 2 * 2 * 64 * x.d * 2;
+    dim3 grid((x.nq + kFwdBQ - 1) / kFwdBQ, x.bh);
+    if (x.d == 128) {
+        hipFuncSetAttribute((const void *)attn_block_fwd_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipLaunchKernelGGL(attn_block_fwd_mfma32<128>, grid, dim3(256), lds, st, p);
+    } else {
+        hipFuncSetAttribute((const void *)attn_block_fwd_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        hipLaunchKernelGGL(attn_block_fwd_mfma32<64>, grid, dim3(256), lds, st, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t attn_merge(int64_t rows, int d, const float *oa, const float *la, const float *ob, const float *lb,
+                      float *o, float *lse, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    TraceScope ts(st, "attn_merge_f32", 3.0 * rows * d, (double)rows * (3.0 * d * 4 + 12));
+    const int64_t threads = rows * (d / 8);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rows, d, oa, la,
+                       ob, lb, o, lse);
     return hipGetLastError();
 }
 

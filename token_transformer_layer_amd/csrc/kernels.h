@@ -99,4 +99,19 @@ size_t attn_fwd_work_floats(int batch, int nt, int seq, int d);
 hipError_t attn_fwd(DType dt, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd(DType dt, const AttnArgs &a, hipStream_t st);
 
+// Attention of nq queries at positions q_pos0.. over one block of nk keys at
+// positions k_pos0.. (key position <= query position), per (batch row, head)
+// slab of bh: q [bh, nq, d], k, v [bh, nk, d] bf16 -> o [bh, nq, d] fp32
+// normalised, lse [bh, nq] (-inf, o = 0, where no key is visible).
+struct AttnBlockArgs {
+    int bh, nq, nk, d, q_pos0, k_pos0;
+    float scale;
+    const void *q, *k, *v;
+    float *o, *lse;
+};
+hipError_t attn_block_fwd(const AttnBlockArgs &a, hipStream_t st);
+// merge of two partial results over disjoint key sets (rows = bh * nq)
+hipError_t attn_merge(int64_t rows, int d, const float *oa, const float *la, const float *ob, const float *lb,
+                      float *o, float *lse, hipStream_t st);
+
 }  // namespace tpk
