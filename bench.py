@@ -181,6 +181,42 @@ def cube_block(torch, steps, warmup):
     return dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
 
 
+def ring_block(torch, steps, warmup):
+    """Attention over key/value blocks (long-context shape: 4096 queries of 12
+    heads of 128 against a 4096-key block of an earlier device, and against
+    their own diagonal block), and the merge of two partial results."""
+    from token_transformer_layer_amd import abi, synth
+    b, n, d, L = 1, 12, 128, 4096
+    g = torch.Generator(device="cpu").manual_seed(1006)
+    q, k, v = [torch.randn((b, n, L, d), generator=g).to("cuda", torch.bfloat16) for _ in range(3)]
+    o = torch.empty((b, n, L, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((b, n, L), dtype=torch.float32, device="cuda")
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    st = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, qp, kp, pairs in [("off_diagonal", L, 0, float(L) * L), ("diagonal", L, L, L * (L + 1) / 2.0)]:
+        shape = abi.tp_attn_block_shape(b, n, d, L, L, qp, kp)
+
+        def step():
+            abi.tp_attn_block_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), st)
+        ms, _, _ = time_steps(torch, step, steps, warmup)
+        tf = 4.0 * d * pairs * b * n / (ms * 1e-3) / 1e12
+        out[name] = dict(ms=round(ms, 4), tflops=round(tf, 1), frac=round(tf / PEAK_BF16_TFLOPS, 4))
+    shape = abi.tp_attn_block_shape(b, n, d, L, L, 0, 0)
+
+    def merge():
+        abi.tp_attn_merge(shape, o.data_ptr(), lse.data_ptr(), o2.data_ptr(), lse2.data_ptr(), o2.data_ptr(),
+                          lse2.data_ptr(), st)
+    o2.zero_()
+    lse2.fill_(float("-inf"))
+    ms, _, _ = time_steps(torch, merge, steps, warmup)
+    by = b * n * L * (3 * d * 4 + 12)
+    out["merge"] = dict(ms=round(ms, 4), gbs=round(by / (ms * 1e-3) / 1e9, 1),
+                        frac=round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    out["shape"] = "batch 1, 12 heads x 128, 4096 queries, 4096-key blocks, bf16 in, fp32 O"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +293,7 @@ def main():
         extra["per_slice_calls"] = dict(ms_per_step=round(ps_ms, 4),
                                         tflops=round(total / (ps_ms * 1e-3) / 1e12, 1))
         extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
+        extra["ring_attention_block"] = ring_block(torch, max(3, args.steps // 2), 2)
 
     out = {
         "metric": "shard-layer fwd+bwd TFLOP/s, GPT-3 175B t=8 shard, one MI355X",
