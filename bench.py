@@ -217,6 +217,20 @@ def ring_block(torch, steps, warmup):
     return out
 
 
+def terapipe_plan(layer, bufs, stages):
+    """The token-slicing plan of a `stages`-stage pipeline of this layer
+    shard, from slice latencies measured here (16-token granularity)."""
+    from token_transformer_layer_amd import terapipe
+    timer = terapipe.SliceTimer(layer, bufs)
+    L = layer.shape.seq
+    fit = [(l, o) for l in (16, 64, 256, 1024) for o in (128, 512, 1024) if l + o <= L]
+    check = [(32, 256), (128, 768), (512, 1024), (96, 1536), (768, 1280)]
+    check = [(l, o) for l, o in check if l + o <= L]
+    out = terapipe.plan(timer, L, 16, stages, fit, check)
+    layer.new_step()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +308,7 @@ def main():
                                         tflops=round(total / (ps_ms * 1e-3) / 1e12, 1))
         extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
         extra["ring_attention_block"] = ring_block(torch, max(3, args.steps // 2), 2)
+        extra["terapipe_slicing"] = terapipe_plan(layer, bufs, stages=8)
 
     out = {
         "metric": "shard-layer fwd+bwd TFLOP/s, GPT-3 175B t=8 shard, one MI355X",

@@ -290,6 +290,37 @@ tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, con
 tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, const float *lse_a,
                         const float *o_b, const float *lse_b, float *o, float *lse, void *stream);
 
+/* Token-slicing plan of a token-level pipeline ("TeraPipe: Token-Level
+ * Pipeline Parallelism ...", section 3, selecting the slicing scheme).
+ * Host functions: every pointer is host memory; nothing is enqueued.
+ *
+ * A sequence of units * g tokens is cut into slices of whole units.  Over K
+ * pipeline stages whose every stage takes t_i for slice i, the last slice
+ * finishes at sum_i t_i + (K - 1) max_i t_i; tp_slicing_plan returns a plan
+ * minimising that, given cost[a * (units + 1) + b] = latency of the slice
+ * covering units [a, b) (entries with a >= b are ignored; +inf forbids a
+ * slice).  ends (capacity units) receives the slice ends in units
+ * (increasing, last = units), num_slices their count and latency the plan's
+ * latency.  units in [1, 4096], stages >= 1; costs >= 0.  The search takes
+ * each distinct cost as a candidate largest slice latency and finds the least
+ * total under it by dynamic programming over prefixes. */
+tp_status tp_slicing_plan(int32_t units, const double *cost, int32_t stages, int32_t *num_slices,
+                          int32_t *ends, double *latency);
+
+/* Slice-latency model: the context overhead of a slice of l tokens after o
+ * tokens of context is modelled as ctx = coef[0] * l * o + coef[1] * o +
+ * coef[2], fitted by least squares to n >= 3 measured samples (len[i],
+ * offset[i], ctx[i]); at least one sample needs offset > 0. */
+tp_status tp_fit_context_model(int32_t n, const int32_t *len, const int32_t *offset, const double *ctx,
+                               double coef[3]);
+
+/* cost[a * (units + 1) + b] = fwd[b - a] + (a > 0 ? ctx((b - a) g, a g) : 0)
+ * for a < b (+inf otherwise), with fwd[k] the measured latency of a slice of
+ * k units without context (fwd has units + 1 entries; fwd[0] unused) and ctx
+ * the model above: the cost table of tp_slicing_plan. */
+tp_status tp_slice_cost_table(int32_t units, int32_t granularity, const double *fwd, const double coef[3],
+                              double *cost);
+
 /* Per-kernel timing.  tp_trace_enable(1) discards earlier records and makes
  * every later kernel launch of the library (from any thread) record two HIP
  * events on its launch stream, with the kernel's name and the algorithmic

@@ -20,7 +20,7 @@ TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1, TP_BWD_MLP_DATA, TP_BWD_ATTN_DATA, TP_BWD_W
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_attn_block_fwd",
-            "tp_attn_merge", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
+            "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
 
 
 class TPError(RuntimeError):
@@ -101,6 +101,14 @@ def lib():
     L.tp_attn_block_fwd.restype = ctypes.c_int
     L.tp_attn_merge.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp, vp]
     L.tp_attn_merge.restype = ctypes.c_int
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    L.tp_slicing_plan.argtypes = [i32, dp, i32, ip, ip, dp]
+    L.tp_slicing_plan.restype = ctypes.c_int
+    L.tp_fit_context_model.argtypes = [i32, ip, ip, dp, dp]
+    L.tp_fit_context_model.restype = ctypes.c_int
+    L.tp_slice_cost_table.argtypes = [i32, i32, dp, dp, dp]
+    L.tp_slice_cost_table.restype = ctypes.c_int
     L.tp_trace_enable.argtypes = [i32]
     L.tp_trace_enable.restype = None
     L.tp_trace_read.argtypes = [P(tp_trace_record), i32]
@@ -168,6 +176,52 @@ def tp_attn_block_fwd(shape, q, k, v, o, lse, stream):
 
 def tp_attn_merge(shape, o_a, lse_a, o_b, lse_b, o, lse, stream):
     _check(lib().tp_attn_merge(ctypes.byref(shape), o_a, lse_a, o_b, lse_b, o, lse, stream))
+
+
+def _dbl(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _i32(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def tp_slicing_plan(units, cost, stages):
+    """cost: (units+1, units+1) host array.  Returns (latency, ends)."""
+    import numpy as np
+    c, cp = _dbl(cost)
+    if c.shape != (units + 1, units + 1):
+        raise ValueError("cost must be (units+1, units+1)")
+    ends, ep = _i32(np.zeros(units))
+    n = ctypes.c_int32()
+    lat = ctypes.c_double()
+    _check(lib().tp_slicing_plan(units, cp, stages, ctypes.byref(n), ep, ctypes.byref(lat)))
+    return lat.value, [int(x) for x in ends[:n.value]]
+
+
+def tp_fit_context_model(lens, offsets, ctx):
+    import numpy as np
+    l, lp = _i32(lens)
+    o, op = _i32(offsets)
+    c, cp = _dbl(ctx)
+    coef, fp = _dbl(np.zeros(3))
+    _check(lib().tp_fit_context_model(len(l), lp, op, cp, fp))
+    return tuple(float(x) for x in coef)
+
+
+def tp_slice_cost_table(units, granularity, fwd, coef):
+    import numpy as np
+    f, fp = _dbl(fwd)
+    if f.shape != (units + 1,):
+        raise ValueError("fwd must have units+1 entries")
+    k, kp = _dbl(coef)
+    cost, cp = _dbl(np.zeros((units + 1, units + 1)))
+    _check(lib().tp_slice_cost_table(units, granularity, fp, kp, cp))
+    return cost
 
 
 def tp_trace_enable(on):

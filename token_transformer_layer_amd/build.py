@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtpshard.so")
-SOURCES = ["api.cpp", "trace.cpp", "gemm.hip", "norm.hip", "attention.hip"]
+SOURCES = ["api.cpp", "trace.cpp", "slicing.cpp", "gemm.hip", "norm.hip", "attention.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -181,6 +181,15 @@ size_t tp_shard_scratch_bytes(const tp_shard_cfg *cfg) {
 
 const char *tp_last_error(void) { return g_err.c_str(); }
 
+// error reporting for the library's other host sources (not exported)
+__attribute__((visibility("hidden"))) tp_status tp_internal_fail(tp_status s, const char *msg) {
+    if (s == TP_OK) {
+        g_err.clear();
+        return s;
+    }
+    return fail(s, "%s", msg);
+}
+
 tp_status tp_gemm_force_tile(int32_t tile) {
     if (tile < -1 || tile > 3) return fail(TP_EINVAL, "tile must be -1 (automatic) or 0..3");
     tpk::gemm_force_tile(tile);
