@@ -13,4 +13,4 @@ function docstrings name the passage each one follows.  No function here is
 "parity unpinned".
 """
 from .layer import *  # noqa: F401,F403
-from . import slicing  # noqa: E402,F401
+from . import cube, slicing  # noqa: E402,F401
