@@ -181,6 +181,43 @@ def cube_block(torch, steps, warmup):
     return dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
 
 
+def cube_backward(torch, steps, warmup):
+    """The cube-partition FFN block's backward at the same shapes (dH = dOut
+    W2, dZ = dH GELU'(Z) with the bias gradient, dW2 = dOut^T H,
+    dW1 = dZ^T X, dX = dZ W1): TFLOP/s of its four products."""
+    from token_transformer_layer_amd import abi, synth
+    c = synth.CUBE
+    g = torch.Generator(device="cpu").manual_seed(c.seed + 2)
+    bf = torch.bfloat16
+    x, dout = [torch.randn(s, generator=g).to("cuda", bf) for s in ((c.rows, c.hidden), (c.rows, c.hidden))]
+    w1 = (torch.randn((c.ffn, c.hidden), generator=g) * 0.02).to("cuda", bf)
+    w2 = (torch.randn((c.hidden, c.ffn), generator=g) * 0.02).to("cuda", bf)
+    z, h = [torch.randn((c.rows, c.ffn), generator=g).to("cuda", bf) for _ in range(2)]
+    dh = torch.empty((c.rows, c.ffn), dtype=torch.float32, device="cuda")
+    dz = torch.empty((c.rows, c.ffn), dtype=bf, device="cuda")
+    db1 = torch.empty((c.ffn,), dtype=torch.float32, device="cuda")
+    dw1 = torch.empty((c.ffn, c.hidden), dtype=torch.float32, device="cuda")
+    dw2 = torch.empty((c.hidden, c.ffn), dtype=torch.float32, device="cuda")
+    dx = torch.empty((c.rows, c.hidden), dtype=torch.float32, device="cuda")
+    work = torch.empty(abi.tp_cube_work_bytes(c.rows, c.ffn), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        abi.tp_cube_matmul(abi.TP_CUBE_AB, c.rows, c.ffn, c.hidden, dout.data_ptr(), w2.data_ptr(), dh.data_ptr(),
+                           False, st)
+        abi.tp_cube_gelu_backward(c.rows, c.ffn, dh.data_ptr(), z.data_ptr(), dz.data_ptr(), db1.data_ptr(), False,
+                                  work.data_ptr(), st)
+        abi.tp_cube_matmul(abi.TP_CUBE_ATB, c.hidden, c.ffn, c.rows, dout.data_ptr(), h.data_ptr(), dw2.data_ptr(),
+                           False, st)
+        abi.tp_cube_matmul(abi.TP_CUBE_ATB, c.ffn, c.hidden, c.rows, dz.data_ptr(), x.data_ptr(), dw1.data_ptr(),
+                           False, st)
+        abi.tp_cube_matmul(abi.TP_CUBE_AB, c.rows, c.hidden, c.ffn, dz.data_ptr(), w1.data_ptr(), dx.data_ptr(),
+                           False, st)
+    ms, _, _ = time_steps(torch, step, steps, warmup)
+    fl = 8.0 * c.rows * c.hidden * c.ffn
+    return dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
+
+
 def ring_block(torch, steps, warmup):
     """Attention over key/value blocks (long-context shape: 4096 queries of 12
     heads of 128 against a 4096-key block of an earlier device, and against
@@ -307,6 +344,7 @@ def main():
         extra["per_slice_calls"] = dict(ms_per_step=round(ps_ms, 4),
                                         tflops=round(total / (ps_ms * 1e-3) / 1e12, 1))
         extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
+        extra["cube_ffn_backward"] = cube_backward(torch, max(3, args.steps // 2), 2)
         extra["ring_attention_block"] = ring_block(torch, max(3, args.steps // 2), 2)
         extra["terapipe_slicing"] = terapipe_plan(layer, bufs, stages=8)
 

@@ -254,6 +254,37 @@ tp_status tp_cube_ffn_block(int32_t rows, int32_t hidden, int32_t ffn, const voi
                             const void *w1, const void *b1, const void *w2, void *hbuf,
                             float *out, void *stream);
 
+/* One device's operations of the 3-D (cube) partition of matrix products
+ * ("Maximizing Parallelism in Distributed Training for Huge Neural
+ * Networks", section 3.1.2: the forms C = AB, AB^T, A^T B and their
+ * gradients, dA and dB each a product of one of the three forms; every
+ * device multiplies its gathered sub-blocks and the partial products are
+ * reduce-scattered).  bf16 operands, row-major; fp32 result:
+ *   TP_CUBE_AB:  a [M, K], b [K, N]     c = a b
+ *   TP_CUBE_ABT: a [M, K], b [N, K]     c = a b^T
+ *   TP_CUBE_ATB: a [K, M], b [K, N]     c = a^T b
+ * c fp32 [M, N] is stored (accumulate = 0) or added to (accumulate = 1).
+ * M, N, K >= 1 and multiples of 8; device pointers, 16-byte aligned; each
+ * buffer below 2 GiB. */
+typedef enum { TP_CUBE_AB = 0, TP_CUBE_ABT = 1, TP_CUBE_ATB = 2 } tp_cube_form;
+tp_status tp_cube_matmul(int32_t form, int32_t M, int32_t N, int32_t K, const void *a, const void *b,
+                         float *c, int32_t accumulate, void *stream);
+
+/* After the reduction of the first FFN product's partial sums (the
+ * nonlinearity comes after it): z = z_sum + bias[col] and h = GELU(z) (exact
+ * erf form), z_sum fp32 [rows, n], bias bf16 [n], z and h bf16 [rows, n]. */
+tp_status tp_cube_bias_gelu(int32_t rows, int32_t n, const float *z_sum, const void *bias, void *z,
+                            void *h, void *stream);
+
+/* dz = dh * GELU'(z) (bf16 [rows, n]; dh fp32 is the reduced gradient of h,
+ * z the bf16 values tp_cube_bias_gelu stored) and the bias gradient
+ * dbias[col] = sum over rows of dz ("Maximizing Parallelism ...", section
+ * 3.1.3), fp32 [n], stored or (accumulate = 1) added.  work: device memory
+ * of tp_cube_work_bytes(rows, n) bytes for the deterministic column sums. */
+size_t tp_cube_work_bytes(int32_t rows, int32_t n);
+tp_status tp_cube_gelu_backward(int32_t rows, int32_t n, const float *dh, const void *z, void *dz,
+                                float *dbias, int32_t accumulate, void *work, void *stream);
+
 /* Attention with the keys split into blocks ("Transformer Training 11:
  * model parallelism", the passage on very long sequences: a device keeps its
  * own queries and receives every device's keys and values, passed round a

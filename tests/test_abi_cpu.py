@@ -190,3 +190,17 @@ def test_block_attention_checks():
     assert _status(lambda: merge(good, o=None)) == abi.TP_EINVAL
     assert _status(lambda: merge(good, o=FAKE + 8)) == abi.TP_EALIGN
     assert _status(lambda: merge(abi.tp_attn_block_shape(1, 2, 32, 10, 0, 0, 0))) == abi.TP_EUNSUPPORTED
+
+
+def test_cube_op_checks():
+    mm = lambda form=0, M=16, N=16, K=16, acc=0, c=FAKE: abi.lib().tp_cube_matmul(form, M, N, K, FAKE, FAKE, c, acc,
+                                                                                   None)
+    assert mm(form=3) == abi.TP_EINVAL
+    assert mm(M=12) == abi.TP_ESHAPE
+    assert mm(K=0) == abi.TP_ESHAPE
+    assert mm(acc=2) == abi.TP_EINVAL
+    assert mm(c=None) == abi.TP_EINVAL
+    assert mm(c=FAKE + 4) == abi.TP_EALIGN
+    assert abi.lib().tp_cube_bias_gelu(4, 12, FAKE, FAKE, FAKE, FAKE, None) == abi.TP_ESHAPE
+    assert abi.lib().tp_cube_gelu_backward(4, 16, FAKE, FAKE, FAKE, FAKE, 0, None, None) == abi.TP_EINVAL
+    assert abi.tp_cube_work_bytes(0, 16) == 0 and abi.tp_cube_work_bytes(4096, 24576) > 0

@@ -20,7 +20,8 @@ TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1, TP_BWD_MLP_DATA, TP_BWD_ATTN_DATA, TP_BWD_W
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_attn_block_fwd",
-            "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
+            "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table",
+            "tp_cube_matmul", "tp_cube_bias_gelu", "tp_cube_work_bytes", "tp_cube_gelu_backward", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
 
 
 class TPError(RuntimeError):
@@ -101,6 +102,14 @@ def lib():
     L.tp_attn_block_fwd.restype = ctypes.c_int
     L.tp_attn_merge.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp, vp]
     L.tp_attn_merge.restype = ctypes.c_int
+    L.tp_cube_matmul.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
+    L.tp_cube_matmul.restype = ctypes.c_int
+    L.tp_cube_bias_gelu.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+    L.tp_cube_bias_gelu.restype = ctypes.c_int
+    L.tp_cube_work_bytes.argtypes = [i32, i32]
+    L.tp_cube_work_bytes.restype = ctypes.c_size_t
+    L.tp_cube_gelu_backward.argtypes = [i32, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.tp_cube_gelu_backward.restype = ctypes.c_int
     dp = ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(ctypes.c_int32)
     L.tp_slicing_plan.argtypes = [i32, dp, i32, ip, ip, dp]
@@ -176,6 +185,25 @@ def tp_attn_block_fwd(shape, q, k, v, o, lse, stream):
 
 def tp_attn_merge(shape, o_a, lse_a, o_b, lse_b, o, lse, stream):
     _check(lib().tp_attn_merge(ctypes.byref(shape), o_a, lse_a, o_b, lse_b, o, lse, stream))
+
+
+TP_CUBE_AB, TP_CUBE_ABT, TP_CUBE_ATB = 0, 1, 2
+
+
+def tp_cube_matmul(form, M, N, K, a, b, c, accumulate, stream):
+    _check(lib().tp_cube_matmul(form, M, N, K, a, b, c, 1 if accumulate else 0, stream))
+
+
+def tp_cube_bias_gelu(rows, n, z_sum, bias, z, h, stream):
+    _check(lib().tp_cube_bias_gelu(rows, n, z_sum, bias, z, h, stream))
+
+
+def tp_cube_work_bytes(rows, n):
+    return lib().tp_cube_work_bytes(rows, n)
+
+
+def tp_cube_gelu_backward(rows, n, dh, z, dz, dbias, accumulate, work, stream):
+    _check(lib().tp_cube_gelu_backward(rows, n, dh, z, dz, dbias, 1 if accumulate else 0, work, stream))
 
 
 def _dbl(a):

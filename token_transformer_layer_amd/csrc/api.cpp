@@ -555,4 +555,71 @@ tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, cons
                       "attention merge");
 }
 
+tp_status tp_cube_matmul(int32_t form, int32_t M, int32_t N, int32_t K, const void *a, const void *b, float *c,
+                         int32_t accumulate, void *stream) {
+    if (form < TP_CUBE_AB || form > TP_CUBE_ATB) return fail(TP_EINVAL, "form %d is not a tp_cube_form", form);
+    if (M <= 0 || N <= 0 || K <= 0) return fail(TP_ESHAPE, "M, N and K must be positive");
+    if (M % 8 || N % 8 || K % 8) return fail(TP_ESHAPE, "M, N and K must be multiples of 8");
+    if ((int64_t)M * K * 2 >= kMaxBuffer || (int64_t)N * K * 2 >= kMaxBuffer || (int64_t)M * N * 4 >= kMaxBuffer)
+        return fail(TP_ESHAPE, "an operand exceeds 2 GiB");
+    if (accumulate != 0 && accumulate != 1) return fail(TP_EINVAL, "accumulate must be 0 or 1");
+    NEED(a, "a");
+    NEED(b, "b");
+    NEED(c, "c");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return fail(TP_EALIGN, "a, b and c must be 16-byte aligned");
+    EpiArgs e;
+    e.c = c;
+    e.ldc = N;
+    Mat A, B;
+    if (form == TP_CUBE_AB) {
+        A = Mat{a, K, true};
+        B = Mat{b, N, false};
+    } else if (form == TP_CUBE_ABT) {
+        A = Mat{a, K, true};
+        B = Mat{b, K, true};
+    } else {
+        A = Mat{a, M, false};
+        B = Mat{b, N, false};
+    }
+    return hip_status(gemm(DType::BF16, M, N, K, A, B, accumulate ? Epi::AccumF32 : Epi::StoreF32, e,
+                           (hipStream_t)stream),
+                      "cube product");
+}
+
+tp_status tp_cube_bias_gelu(int32_t rows, int32_t n, const float *z_sum, const void *bias, void *z, void *h,
+                            void *stream) {
+    if (rows <= 0 || n <= 0 || n % 8) return fail(TP_ESHAPE, "rows must be positive and n a positive multiple of 8");
+    if ((int64_t)rows * n * 4 >= kMaxBuffer) return fail(TP_ESHAPE, "a tensor exceeds 2 GiB");
+    NEED(z_sum, "z_sum");
+    NEED(bias, "bias");
+    NEED(z, "z");
+    NEED(h, "h");
+    if (!aligned16(z_sum) || !aligned16(bias) || !aligned16(z) || !aligned16(h))
+        return fail(TP_EALIGN, "z_sum, bias, z and h must be 16-byte aligned");
+    return hip_status(bias_gelu(rows, n, z_sum, bias, z, h, (hipStream_t)stream), "cube bias and GELU");
+}
+
+size_t tp_cube_work_bytes(int32_t rows, int32_t n) {
+    if (rows <= 0 || n <= 0) return 0;
+    return colsum_partials_floats(rows, n) * sizeof(float);
+}
+
+tp_status tp_cube_gelu_backward(int32_t rows, int32_t n, const float *dh, const void *z, void *dz, float *dbias,
+                                int32_t accumulate, void *work, void *stream) {
+    if (rows <= 0 || n <= 0 || n % 8) return fail(TP_ESHAPE, "rows must be positive and n a positive multiple of 8");
+    if ((int64_t)rows * n * 4 >= kMaxBuffer) return fail(TP_ESHAPE, "a tensor exceeds 2 GiB");
+    if (accumulate != 0 && accumulate != 1) return fail(TP_EINVAL, "accumulate must be 0 or 1");
+    NEED(dh, "dh");
+    NEED(z, "z");
+    NEED(dz, "dz");
+    NEED(dbias, "dbias");
+    NEED(work, "work");
+    if (!aligned16(dh) || !aligned16(z) || !aligned16(dz) || !aligned16(dbias) || !aligned16(work))
+        return fail(TP_EALIGN, "dh, z, dz, dbias and work must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    HIPCALL(gelu_backward(rows, n, dh, z, dz, st), "cube GELU backward");
+    HIPCALL(colsum(DType::BF16, rows, n, dz, n, dbias, accumulate != 0, (float *)work, st), "cube bias gradient");
+    return TP_OK;
+}
+
 }  // extern "C"

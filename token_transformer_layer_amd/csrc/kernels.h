@@ -99,6 +99,11 @@ size_t attn_fwd_work_floats(int batch, int nt, int seq, int d);
 hipError_t attn_fwd(DType dt, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd(DType dt, const AttnArgs &a, hipStream_t st);
 
+// Cube-partition FFN steps (bf16 outputs, n a multiple of 8): z = z_sum +
+// bias, h = GELU(z); dz = dh * GELU'(z).
+hipError_t bias_gelu(int64_t rows, int n, const float *z_sum, const void *bias, void *z, void *h, hipStream_t st);
+hipError_t gelu_backward(int64_t rows, int n, const float *dh, const void *z, void *dz, hipStream_t st);
+
 // Attention of nq queries at positions q_pos0.. over one block of nk keys at
 // positions k_pos0.. (key position <= query position), per (batch row, head)
 // slab of bh: q [bh, nq, d], k, v [bh, nk, d] bf16 -> o [bh, nq, d] fp32

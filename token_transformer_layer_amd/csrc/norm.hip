@@ -11,6 +11,8 @@
 // db = sum of dC * A over rows).  Parameter gradients are reduced in two
 // deterministic stages (per-block partials, then one pass over the blocks),
 // so repeated runs give identical bits.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "trace.h"
@@ -273,6 +275,41 @@ int colsum_chunks(int rows) {
     return c < 64 ? (c < 1 ? 1 : c) : 64;
 }
 
+// Cube-partition FFN elementwise steps, 8 columns per thread: Z = z_sum +
+// bias[c] stored bf16 and H = GELU(Z) (of the fp32 Z); dZ = dH * GELU'(Z)
+// with Z the stored bf16 values.
+__global__ __launch_bounds__(kThreads) void bias_gelu_kernel(int64_t n8, int n, const float *__restrict__ zs,
+                                                             const bf16 *__restrict__ bias, bf16 *__restrict__ z,
+                                                             bf16 *__restrict__ h) {
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t e = i * 8;
+        const int c = (int)(e % n);
+        float v[8], b[8], g[8];
+        load8(zs + e, v);
+        load8(bias + c, b);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            v[j] += b[j];
+            g[j] = gelu_f(v[j]);
+        }
+        store8(z + e, v);
+        store8(h + e, g);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void gelu_backward_kernel(int64_t n8, const float *__restrict__ dh,
+                                                                 const bf16 *__restrict__ z, bf16 *__restrict__ dz) {
+    for (int64_t i = blockIdx.x * (int64_t)kThreads + threadIdx.x; i < n8; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t e = i * 8;
+        float d[8], zz[8];
+        load8(dh + e, d);
+        load8(z + e, zz);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] *= gelu_grad_f(zz[j]);
+        store8(dz + e, d);
+    }
+}
+
 }  // namespace
 
 size_t layernorm_bwd_partials_floats(int rows, int h) { return (size_t)ln_bwd_blocks(rows) * 2 * h; }
@@ -387,6 +424,26 @@ hipError_t residual_combine(DType dt, int64_t rows, int h, const void *resid, co
     else
         hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)blocks), dim3(kThreads), 0, st, n8, h,
                            (const float *)resid, reduced, (const float *)bias, (float *)out);
+    return hipGetLastError();
+}
+
+hipError_t bias_gelu(int64_t rows, int n, const float *z_sum, const void *bias, void *z, void *h, hipStream_t st) {
+    const int64_t n8 = rows * n / 8;
+    if (n8 <= 0) return hipSuccess;
+    TraceScope ts(st, "cube_bias_gelu", 0.0, (double)rows * n * (4 + 2 + 2) + 2.0 * n);
+    const int64_t blocks = std::min<int64_t>((n8 + kThreads - 1) / kThreads, 8192);
+    hipLaunchKernelGGL(bias_gelu_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, n8, n, z_sum,
+                       (const bf16 *)bias, (bf16 *)z, (bf16 *)h);
+    return hipGetLastError();
+}
+
+hipError_t gelu_backward(int64_t rows, int n, const float *dh, const void *z, void *dz, hipStream_t st) {
+    const int64_t n8 = rows * n / 8;
+    if (n8 <= 0) return hipSuccess;
+    TraceScope ts(st, "cube_gelu_bwd", 0.0, (double)rows * n * (4 + 2 + 2));
+    const int64_t blocks = std::min<int64_t>((n8 + kThreads - 1) / kThreads, 8192);
+    hipLaunchKernelGGL(gelu_backward_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, n8, dh, (const bf16 *)z,
+                       (bf16 *)dz);
     return hipGetLastError();
 }
 

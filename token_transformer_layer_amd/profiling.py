@@ -35,6 +35,7 @@ _FAMILY_SOURCES = {
     "colsum": ["norm.hip"],
     "block": ["norm.hip"],
     "combine": ["norm.hip"],
+    "cube": ["norm.hip"],
 }
 _SHARED = ["common.h", "kernels.h"]
 
