@@ -181,6 +181,55 @@ def cube_block(torch, steps, warmup):
     return dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
 
 
+def sequence_parallel_step(torch, layer, bufs, steps, warmup):
+    """One rank's step in the sequence-parallel form: LayerNorm, its backward
+    and the residual combines on the rank's 1/t shard of the rows, the
+    products and attention over all rows (the all-gathers and
+    reduce-scatters between them belong to the caller and are not run on
+    one GPU).  Same algorithmic flops as the headline step."""
+    from token_transformer_layer_amd import abi
+    sh = layer.shape
+    b, h = sh.batch, sh.hidden
+    T = sh.seq * b
+    rows = T // sh.tp
+    st = torch.cuda.current_stream().cuda_stream
+    M = len(sh.slices)
+    x, dy, hm, y, dh, dx = (bufs[k] for k in ("x", "dy", "h_mid", "y", "dh", "dx"))
+    pa, pm, pu2, pu1 = (bufs[k] for k in ("p_attn", "p_mlp", "p_du2", "p_du1"))
+    u1, u2 = layer.act(), layer.act()
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32, device="cuda")  # noqa: E731
+    mu1, rs1, mu2, rs2 = f32(rows), f32(rows), f32(rows), f32(rows)
+    lg = [f32(h) for _ in range(4)]
+    work = torch.empty(abi.tp_layernorm_work_bytes(layer.cfg, rows), dtype=torch.uint8, device="cuda")
+    P = layer.p
+    cfg = layer.cfg
+
+    def step():
+        layer.kv.filled = 0
+        layer.kvg.done_from = sh.seq
+        abi.tp_layernorm_fwd(cfg, rows, x.data_ptr(), P["ln1_g"].data_ptr(), P["ln1_b"].data_ptr(), u1.data_ptr(),
+                             mu1.data_ptr(), rs1.data_ptr(), st)
+        layer.fwd(abi.TP_FWD_ATTN_SP, 0, M, u1, pa)
+        abi.tp_residual_combine(cfg, rows, x.data_ptr(), pa.data_ptr(), P["b_o"].data_ptr(), hm.data_ptr(), st)
+        abi.tp_layernorm_fwd(cfg, rows, hm.data_ptr(), P["ln2_g"].data_ptr(), P["ln2_b"].data_ptr(), u2.data_ptr(),
+                             mu2.data_ptr(), rs2.data_ptr(), st)
+        layer.fwd(abi.TP_FWD_MLP_SP, 0, M, u2, pm)
+        abi.tp_residual_combine(cfg, rows, hm.data_ptr(), pm.data_ptr(), P["b2"].data_ptr(), y.data_ptr(), st)
+        layer.bwd(abi.TP_BWD_MLP, 0, M, dy=dy, partial_out=pu2, accumulate=False)
+        abi.tp_layernorm_bwd(cfg, rows, pu2.data_ptr(), dy.data_ptr(), hm.data_ptr(), P["ln2_g"].data_ptr(),
+                             mu2.data_ptr(), rs2.data_ptr(), dh.data_ptr(), lg[0].data_ptr(), lg[1].data_ptr(), False,
+                             work.data_ptr(), st)
+        layer.bwd(abi.TP_BWD_ATTN_SP, 0, M, dy=dy, partial_out=pu1, dh=dh, accumulate=False)
+        abi.tp_layernorm_bwd(cfg, rows, pu1.data_ptr(), dh.data_ptr(), x.data_ptr(), P["ln1_g"].data_ptr(),
+                             mu1.data_ptr(), rs1.data_ptr(), dx.data_ptr(), lg[2].data_ptr(), lg[3].data_ptr(), False,
+                             work.data_ptr(), st)
+    ms, _, _ = time_steps(torch, step, steps, warmup)
+    g_fl, a_fl = step_flops(sh)
+    layer.new_step()
+    return dict(ms_per_step=round(ms, 4), tflops=round((g_fl + a_fl) / (ms * 1e-3) / 1e12, 1),
+                shard_rows=rows, collectives="not run (one GPU)")
+
+
 def cube_backward(torch, steps, warmup):
     """The cube-partition FFN block's backward at the same shapes (dH = dOut
     W2, dZ = dH GELU'(Z) with the bias gradient, dW2 = dOut^T H,
@@ -345,6 +394,7 @@ def main():
                                         tflops=round(total / (ps_ms * 1e-3) / 1e12, 1))
         extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
         extra["cube_ffn_backward"] = cube_backward(torch, max(3, args.steps // 2), 2)
+        extra["sequence_parallel_step"] = sequence_parallel_step(torch, layer, bufs, max(3, args.steps // 2), 2)
         extra["ring_attention_block"] = ring_block(torch, max(3, args.steps // 2), 2)
         extra["terapipe_slicing"] = terapipe_plan(layer, bufs, stages=8)
 

@@ -162,7 +162,15 @@ typedef struct {
     int32_t done_from;
 } tp_kv_grad;
 
-typedef enum { TP_FWD_ATTN = 0, TP_FWD_MLP = 1 } tp_fwd_phase;
+/* Forward phases.  The _SP phases are the sequence-parallel form
+ * ("Transformer Training 11: model parallelism", sequence-parallelism
+ * slide: LayerNorm and dropout split along the sequence, each all-reduce
+ * becoming a reduce-scatter and an all-gather): LayerNorm runs on the
+ * rank's sequence shard (tp_layernorm_fwd) and the caller all-gathers its
+ * output, which TP_FWD_ATTN_SP / TP_FWD_MLP_SP take as `in` (LN1(x) /
+ * LN2(h_mid) for the call's rows) instead of computing it; the partial sums
+ * are then reduce-scattered instead of all-reduced. */
+typedef enum { TP_FWD_ATTN = 0, TP_FWD_MLP = 1, TP_FWD_ATTN_SP = 2, TP_FWD_MLP_SP = 3 } tp_fwd_phase;
 /* Backward phases.  TP_BWD_MLP = TP_BWD_MLP_DATA + the MLP weight and bias
  * gradients of the call's rows; TP_BWD_ATTN = TP_BWD_ATTN_DATA + the
  * attention block's weight and bias gradients.  The _DATA phases produce
@@ -178,7 +186,12 @@ typedef enum {
     TP_BWD_LN1 = 2,
     TP_BWD_MLP_DATA = 3,
     TP_BWD_ATTN_DATA = 4,
-    TP_BWD_WGRAD = 5
+    TP_BWD_WGRAD = 5,
+    /* sequence-parallel form of TP_BWD_ATTN(_DATA): dh is an input, the
+     * all-gathered dH = dY + LN2^T(dU2) that the caller formed on its
+     * sequence shard with tp_layernorm_bwd; ln_in and reduced_in unused */
+    TP_BWD_ATTN_SP = 6,
+    TP_BWD_ATTN_DATA_SP = 7
 } tp_bwd_phase;
 
 /* Bytes of the opaque "saved" buffer: activations the forward keeps for the
@@ -351,6 +364,24 @@ tp_status tp_fit_context_model(int32_t n, const int32_t *len, const int32_t *off
  * the model above: the cost table of tp_slicing_plan. */
 tp_status tp_slice_cost_table(int32_t units, int32_t granularity, const double *fwd, const double coef[3],
                               double *cost);
+
+/* LayerNorm over `rows` rows of width cfg->hidden (a sequence shard in the
+ * sequence-parallel form; "Transformer Training 11", sequence-parallelism
+ * slide), element type cfg->dtype, statistics fp32, eps cfg->ln_eps:
+ *   tp_layernorm_fwd: u = (x - mean) * rstd * gamma + beta, biased variance;
+ *   tp_layernorm_bwd: dx = resid + LN^T(du) for the saved mean and rstd
+ *     (du fp32, the reduced gradient of u), dgamma = sum over the rows of
+ *     du * xhat and dbeta = sum of du (fp32 [hidden]; stored or, with
+ *     accumulate = 1, added: a shard's share, which the caller all-reduces).
+ * work: tp_layernorm_work_bytes(cfg, rows) bytes of device memory.  mean
+ * and rstd (fp32 [rows]) need 4-byte alignment, every other pointer 16. */
+size_t tp_layernorm_work_bytes(const tp_shard_cfg *cfg, int64_t rows);
+tp_status tp_layernorm_fwd(const tp_shard_cfg *cfg, int64_t rows, const void *x, const void *gamma,
+                           const void *beta, void *u, float *mean, float *rstd, void *stream);
+tp_status tp_layernorm_bwd(const tp_shard_cfg *cfg, int64_t rows, const float *du, const void *resid,
+                           const void *x, const void *gamma, const float *mean, const float *rstd,
+                           void *dx, float *dgamma, float *dbeta, int32_t accumulate, void *work,
+                           void *stream);
 
 /* Per-kernel timing.  tp_trace_enable(1) discards earlier records and makes
  * every later kernel launch of the library (from any thread) record two HIP

@@ -109,7 +109,7 @@ def test_pointer_checks():
     assert _status(lambda: _fwd(c, part, 0, 1, in_ptr=FAKE + 8)) == abi.TP_EALIGN
     assert _status(lambda: _fwd(c, part, 0, 1, saved=None)) == abi.TP_EINVAL
     assert _status(lambda: _fwd(c, part, 0, 1, w=_weights(FAKE + 2))) == abi.TP_EALIGN
-    assert _status(lambda: _fwd(c, part, 0, 1, phase=9)) == abi.TP_EINVAL
+    assert _status(lambda: _fwd(c, part, 0, 1, phase=4)) == abi.TP_EINVAL
 
 
 def test_forward_slice_order_is_enforced():
@@ -148,7 +148,7 @@ def test_backward_slice_order_is_enforced():
         abi.tp_shard_layer_bwd(c, _weights(), part, 3, 4, phase, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                g, kv, kvg, FAKE, FAKE, None)
 
-    assert _status(lambda: bwd_phase(6)) == abi.TP_EINVAL
+    assert _status(lambda: bwd_phase(8)) == abi.TP_EINVAL
     assert _status(lambda: bwd_phase(-1)) == abi.TP_EINVAL
     kvg.done_from = 32
     assert _status(lambda: bwd_phase(abi.TP_BWD_ATTN_DATA)) == abi.TP_EORDER
@@ -204,3 +204,31 @@ def test_cube_op_checks():
     assert abi.lib().tp_cube_bias_gelu(4, 12, FAKE, FAKE, FAKE, FAKE, None) == abi.TP_ESHAPE
     assert abi.lib().tp_cube_gelu_backward(4, 16, FAKE, FAKE, FAKE, FAKE, 0, None, None) == abi.TP_EINVAL
     assert abi.tp_cube_work_bytes(0, 16) == 0 and abi.tp_cube_work_bytes(4096, 24576) > 0
+
+
+def test_layernorm_checks():
+    c = cfg_of(synth.CONFIGS["tiny-fp32"])
+    L = abi.lib()
+    assert L.tp_layernorm_fwd(c, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == abi.TP_ESHAPE
+    assert L.tp_layernorm_fwd(c, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == abi.TP_EINVAL
+    assert L.tp_layernorm_fwd(c, 10, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == abi.TP_EALIGN
+    args = [FAKE] * 9
+    assert L.tp_layernorm_bwd(c, 10, *args, 2, FAKE, None) == abi.TP_EINVAL
+    assert L.tp_layernorm_bwd(c, 10, *args[:8], None, 0, FAKE, None) == abi.TP_EINVAL
+    assert abi.tp_layernorm_work_bytes(c, 0) == 0 and abi.tp_layernorm_work_bytes(c, 100) > 0
+
+
+def test_sequence_parallel_phases_need_their_inputs():
+    c = cfg_of(synth.CONFIGS["tiny-fp32"])
+    part = abi.make_partition([64, 64])
+    g = abi.tp_shard_grads(*[FAKE] * len(abi.GRAD_FIELDS), 1)
+    kv = abi.tp_kv_cache(FAKE, FAKE, 128)
+    kvg = abi.tp_kv_grad(FAKE, FAKE, 128)
+    # the SP attention backward needs dh (given) but not ln_in / reduced_in
+    st = abi.lib().tp_shard_layer_bwd(c, _weights(), part, 1, 2, abi.TP_BWD_ATTN_SP, FAKE, None, None, FAKE, None,
+                                      FAKE, g, kv, kvg, FAKE, FAKE, None)
+    assert st == abi.TP_EINVAL and b"dh" in abi.lib().tp_last_error()
+    # the SP forward does not need LayerNorm parameters
+    w = abi.tp_shard_weights(*[None if n.startswith("ln") else FAKE for n in abi.WEIGHT_FIELDS])
+    assert _status(lambda: _fwd(c, part, 0, 1, phase=abi.TP_FWD_ATTN_SP, w=w, in_ptr=None)) == abi.TP_EINVAL
+    assert b"in" in abi.lib().tp_last_error()

@@ -15,13 +15,15 @@ TP_OK, TP_EINVAL, TP_ESHAPE, TP_EALIGN, TP_EORDER, TP_EUNSUPPORTED, TP_EHIP = ra
 STATUS_NAMES = {0: "TP_OK", 1: "TP_EINVAL", 2: "TP_ESHAPE", 3: "TP_EALIGN", 4: "TP_EORDER",
                 5: "TP_EUNSUPPORTED", 6: "TP_EHIP"}
 TP_F32, TP_BF16 = 0, 1
-TP_FWD_ATTN, TP_FWD_MLP = 0, 1
+TP_FWD_ATTN, TP_FWD_MLP, TP_FWD_ATTN_SP, TP_FWD_MLP_SP = 0, 1, 2, 3
 TP_BWD_MLP, TP_BWD_ATTN, TP_BWD_LN1, TP_BWD_MLP_DATA, TP_BWD_ATTN_DATA, TP_BWD_WGRAD = 0, 1, 2, 3, 4, 5
+TP_BWD_ATTN_SP, TP_BWD_ATTN_DATA_SP = 6, 7
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_attn_block_fwd",
             "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table",
-            "tp_cube_matmul", "tp_cube_bias_gelu", "tp_cube_work_bytes", "tp_cube_gelu_backward", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
+            "tp_cube_matmul", "tp_cube_bias_gelu", "tp_cube_work_bytes", "tp_cube_gelu_backward",
+            "tp_layernorm_work_bytes", "tp_layernorm_fwd", "tp_layernorm_bwd", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
 
 
 class TPError(RuntimeError):
@@ -102,6 +104,12 @@ def lib():
     L.tp_attn_block_fwd.restype = ctypes.c_int
     L.tp_attn_merge.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp, vp]
     L.tp_attn_merge.restype = ctypes.c_int
+    L.tp_layernorm_work_bytes.argtypes = [P(tp_shard_cfg), i64]
+    L.tp_layernorm_work_bytes.restype = ctypes.c_size_t
+    L.tp_layernorm_fwd.argtypes = [P(tp_shard_cfg), i64, vp, vp, vp, vp, vp, vp, vp]
+    L.tp_layernorm_fwd.restype = ctypes.c_int
+    L.tp_layernorm_bwd.argtypes = [P(tp_shard_cfg), i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    L.tp_layernorm_bwd.restype = ctypes.c_int
     L.tp_cube_matmul.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, vp]
     L.tp_cube_matmul.restype = ctypes.c_int
     L.tp_cube_bias_gelu.argtypes = [i32, i32, vp, vp, vp, vp, vp]
@@ -188,6 +196,19 @@ def tp_attn_merge(shape, o_a, lse_a, o_b, lse_b, o, lse, stream):
 
 
 TP_CUBE_AB, TP_CUBE_ABT, TP_CUBE_ATB = 0, 1, 2
+
+
+def tp_layernorm_work_bytes(cfg, rows):
+    return lib().tp_layernorm_work_bytes(ctypes.byref(cfg), rows)
+
+
+def tp_layernorm_fwd(cfg, rows, x, gamma, beta, u, mean, rstd, stream):
+    _check(lib().tp_layernorm_fwd(ctypes.byref(cfg), rows, x, gamma, beta, u, mean, rstd, stream))
+
+
+def tp_layernorm_bwd(cfg, rows, du, resid, x, gamma, mean, rstd, dx, dgamma, dbeta, accumulate, work, stream):
+    _check(lib().tp_layernorm_bwd(ctypes.byref(cfg), rows, du, resid, x, gamma, mean, rstd, dx, dgamma, dbeta,
+                                  1 if accumulate else 0, work, stream))
 
 
 def tp_cube_matmul(form, M, N, K, a, b, c, accumulate, stream):

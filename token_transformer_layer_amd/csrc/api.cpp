@@ -127,6 +127,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
         if (!aligned16(ptr)) return fail(TP_EALIGN, "%s is not 16-byte aligned", name); \
     } while (0)
 
+// scalar fp32 arrays (LayerNorm statistics): 4-byte alignment
+#define NEED4(ptr, name)                                                                 \
+    do {                                                                                 \
+        if (!(ptr)) return fail(TP_EINVAL, "%s is NULL", name);                         \
+        if ((uintptr_t)(ptr) & 3) return fail(TP_EALIGN, "%s is not 4-byte aligned", name); \
+    } while (0)
+
 tp_status check_range(const Dims &d, const tp_partition *part, int32_t j0, int32_t j1, int64_t *o0, int64_t *o1) {
     if (!part || !part->len) return fail(TP_EINVAL, "partition is NULL");
     if (part->num_slices <= 0) return fail(TP_ESHAPE, "partition has no slices");
@@ -206,7 +213,9 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     if (!w) return fail(TP_EINVAL, "weights is NULL");
     int64_t o0, o1;
     if ((s = check_range(d, part, slice_begin, slice_end, &o0, &o1)) != TP_OK) return s;
-    if (phase != TP_FWD_ATTN && phase != TP_FWD_MLP) return fail(TP_EINVAL, "forward phase %d is not valid", phase);
+    if (phase < TP_FWD_ATTN || phase > TP_FWD_MLP_SP) return fail(TP_EINVAL, "forward phase %d is not valid", phase);
+    // sequence-parallel phases take the gathered LayerNorm output as `in`
+    const bool sp = phase == TP_FWD_ATTN_SP || phase == TP_FWD_MLP_SP;
     NEED(in, "in");
     NEED(partial_out, "partial_out");
     NEED(saved, "saved");
@@ -224,9 +233,11 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         return x;
     };
     EpiArgs e = fresh();
-    if (phase == TP_FWD_ATTN) {
-        NEED(w->ln1_g, "w.ln1_g");
-        NEED(w->ln1_b, "w.ln1_b");
+    if (phase == TP_FWD_ATTN || phase == TP_FWD_ATTN_SP) {
+        if (!sp) {
+            NEED(w->ln1_g, "w.ln1_g");
+            NEED(w->ln1_b, "w.ln1_b");
+        }
         NEED(w->w_qkv, "w.w_qkv");
         NEED(w->b_qkv, "w.b_qkv");
         NEED(w->w_o, "w.w_o");
@@ -237,9 +248,15 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
             return fail(TP_EORDER, "slices must run in order: cache holds %d positions, call starts at %lld", kv->filled,
                         (long long)o0);
         void *u1 = at<char *>(saved, L.u1 + r0 * d.h * es);
-        HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln1_g,
-                              w->ln1_b, u1, at<float *>(saved, L.mu1 + r0 * 4), at<float *>(saved, L.rs1 + r0 * 4), st),
-                "layernorm forward (LN1)");
+        if (sp)
+            HIPCALL(hipMemcpyAsync(u1, at<const char *>(in, r0 * d.h * es), nrows * d.h * es, hipMemcpyDeviceToDevice,
+                                   st),
+                    "copy of the gathered LN1 output");
+        else
+            HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es),
+                                  w->ln1_g, w->ln1_b, u1, at<float *>(saved, L.mu1 + r0 * 4),
+                                  at<float *>(saved, L.rs1 + r0 * 4), st),
+                    "layernorm forward (LN1)");
         e = fresh();
         e.bias = w->b_qkv;
         e.q = at<char *>(saved, L.q);
@@ -265,15 +282,21 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         kv->filled = (int32_t)o1;
         return TP_OK;
     }
-    NEED(w->ln2_g, "w.ln2_g");
-    NEED(w->ln2_b, "w.ln2_b");
+    if (!sp) {
+        NEED(w->ln2_g, "w.ln2_g");
+        NEED(w->ln2_b, "w.ln2_b");
+    }
     NEED(w->w1, "w.w1");
     NEED(w->b1, "w.b1");
     NEED(w->w2, "w.w2");
     void *u2 = at<char *>(saved, L.u2 + r0 * d.h * es);
-    HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln2_g,
-                          w->ln2_b, u2, at<float *>(saved, L.mu2 + r0 * 4), at<float *>(saved, L.rs2 + r0 * 4), st),
-            "layernorm forward (LN2)");
+    if (sp)
+        HIPCALL(hipMemcpyAsync(u2, at<const char *>(in, r0 * d.h * es), nrows * d.h * es, hipMemcpyDeviceToDevice, st),
+                "copy of the gathered LN2 output");
+    else
+        HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln2_g,
+                              w->ln2_b, u2, at<float *>(saved, L.mu2 + r0 * 4), at<float *>(saved, L.rs2 + r0 * 4), st),
+                "layernorm forward (LN2)");
     void *z = at<char *>(saved, L.z + r0 * d.ft * es);
     void *gg = at<char *>(saved, L.g + r0 * d.ft * es);
     e = fresh();
@@ -301,13 +324,17 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     if (g->accumulate != 0 && g->accumulate != 1) return fail(TP_EINVAL, "grads.accumulate must be 0 or 1");
     int64_t o0, o1;
     if ((s = check_range(d, part, slice_begin, slice_end, &o0, &o1)) != TP_OK) return s;
-    if (phase < TP_BWD_MLP || phase > TP_BWD_WGRAD) return fail(TP_EINVAL, "backward phase %d is not valid", phase);
+    if (phase < TP_BWD_MLP || phase > TP_BWD_ATTN_DATA_SP)
+        return fail(TP_EINVAL, "backward phase %d is not valid", phase);
     NEED(saved, "saved");
     NEED(scratch, "scratch");
+    // sequence-parallel attention phases: dH is given (gathered), LN2's
+    // backward ran on the caller's shard
+    const bool sp = phase == TP_BWD_ATTN_SP || phase == TP_BWD_ATTN_DATA_SP;
     const bool mlp = phase == TP_BWD_MLP || phase == TP_BWD_MLP_DATA;
-    const bool attn = phase == TP_BWD_ATTN || phase == TP_BWD_ATTN_DATA;
+    const bool attn = phase == TP_BWD_ATTN || phase == TP_BWD_ATTN_DATA || sp;
     const bool mlp_w = phase == TP_BWD_MLP || phase == TP_BWD_WGRAD;
-    const bool attn_w = phase == TP_BWD_ATTN || phase == TP_BWD_WGRAD;
+    const bool attn_w = phase == TP_BWD_ATTN || phase == TP_BWD_WGRAD || phase == TP_BWD_ATTN_SP;
     const bool acc = g->accumulate != 0;
     // every check runs before anything is enqueued
     if (mlp || attn || mlp_w || attn_w) NEED(dy, "dy");
@@ -322,16 +349,18 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         NEED(g->w2, "g.w2");
         NEED(g->b2, "g.b2");
     }
-    if (attn || phase == TP_BWD_LN1) {
+    if ((attn && !sp) || phase == TP_BWD_LN1) {
         NEED(ln_in, "ln_in");
         NEED(reduced_in, "reduced_in");
     }
     if (attn || attn_w || phase == TP_BWD_LN1) NEED(dh, "dh");
-    if (attn) {
+    if (attn && !sp) {
         NEED(w->ln2_g, "w.ln2_g");
-        NEED(w->w_o, "w.w_o");
         NEED(g->ln2_g, "g.ln2_g");
         NEED(g->ln2_b, "g.ln2_b");
+    }
+    if (attn) {
+        NEED(w->w_o, "w.w_o");
         if (!kv || !kvg) return fail(TP_EINVAL, "kv and kvg are required for the attention backward");
         NEED(kv->k, "kv.k");
         NEED(kv->v, "kv.v");
@@ -343,8 +372,7 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
             return fail(TP_EORDER, "backward slices must run in reverse: done_from is %d, call ends at %lld",
                         kvg->done_from, (long long)o1);
     }
-    if (phase == TP_BWD_ATTN) NEED(w->w_qkv, "w.w_qkv");
-    if (phase == TP_BWD_ATTN_DATA) NEED(w->w_qkv, "w.w_qkv");
+    if (attn) NEED(w->w_qkv, "w.w_qkv");
     if (attn_w) {
         NEED(g->w_o, "g.w_o");
         NEED(g->b_o, "g.b_o");
@@ -408,11 +436,14 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         HIPCALL(colsum(d.dt, (int)nrows, (int)d.h, dyr, d.h, g->b2, acc, red, st), "b2 gradient");
     }
     if (attn) {
-        // dH = dY + LN2^T(sum_r dU2,r); dO = dH W_o; attention backward
-        HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dyr,
-                              at<const char *>(ln_in, r0 * d.h * es), w->ln2_g, at<const float *>(saved, L.mu2 + r0 * 4),
-                              at<const float *>(saved, L.rs2 + r0 * 4), dhr, g->ln2_g, g->ln2_b, acc, red, st),
-                "layernorm backward (LN2)");
+        // dH = dY + LN2^T(sum_r dU2,r) (given in the sequence-parallel form);
+        // dO = dH W_o; attention backward
+        if (!sp)
+            HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dyr,
+                                  at<const char *>(ln_in, r0 * d.h * es), w->ln2_g,
+                                  at<const float *>(saved, L.mu2 + r0 * 4), at<const float *>(saved, L.rs2 + r0 * 4), dhr,
+                                  g->ln2_g, g->ln2_b, acc, red, st),
+                    "layernorm backward (LN2)");
         e = fresh();
         e.c = dO; e.ldc = d.ht;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.ht, (int)d.h, Mat{dhr, d.h, true}, Mat{w->w_o, d.ht, false}, Epi::Store, e,
@@ -620,6 +651,63 @@ tp_status tp_cube_gelu_backward(int32_t rows, int32_t n, const float *dh, const 
     HIPCALL(gelu_backward(rows, n, dh, z, dz, st), "cube GELU backward");
     HIPCALL(colsum(DType::BF16, rows, n, dz, n, dbias, accumulate != 0, (float *)work, st), "cube bias gradient");
     return TP_OK;
+}
+
+size_t tp_layernorm_work_bytes(const tp_shard_cfg *cfg, int64_t rows) {
+    Dims d;
+    if (check_cfg(cfg, &d) != TP_OK || rows <= 0 || rows > INT32_MAX) return 0;
+    return layernorm_bwd_partials_floats((int)rows, (int)d.h) * sizeof(float);
+}
+
+static tp_status check_ln_rows(const Dims &d, int64_t rows) {
+    if (rows < 0 || rows > INT32_MAX) return fail(TP_ESHAPE, "rows %lld out of range", (long long)rows);
+    if (rows * d.h * 4 >= kMaxBuffer) return fail(TP_ESHAPE, "a tensor of %lld rows exceeds 2 GiB", (long long)rows);
+    return TP_OK;
+}
+
+tp_status tp_layernorm_fwd(const tp_shard_cfg *cfg, int64_t rows, const void *x, const void *gamma, const void *beta,
+                           void *u, float *mean, float *rstd, void *stream) {
+    Dims d;
+    tp_status s = check_cfg(cfg, &d);
+    if (s != TP_OK) return s;
+    if ((s = check_ln_rows(d, rows)) != TP_OK) return s;
+    NEED(x, "x");
+    NEED(gamma, "gamma");
+    NEED(beta, "beta");
+    NEED(u, "u");
+    NEED4(mean, "mean");
+    NEED4(rstd, "rstd");
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(u))
+        return fail(TP_EALIGN, "x, gamma, beta and u must be 16-byte aligned");
+    return hip_status(layernorm_fwd(d.dt, (int)rows, (int)d.h, cfg->ln_eps, x, gamma, beta, u, mean, rstd,
+                                    (hipStream_t)stream),
+                      "layernorm forward");
+}
+
+tp_status tp_layernorm_bwd(const tp_shard_cfg *cfg, int64_t rows, const float *du, const void *resid, const void *x,
+                           const void *gamma, const float *mean, const float *rstd, void *dx, float *dgamma,
+                           float *dbeta, int32_t accumulate, void *work, void *stream) {
+    Dims d;
+    tp_status s = check_cfg(cfg, &d);
+    if (s != TP_OK) return s;
+    if ((s = check_ln_rows(d, rows)) != TP_OK) return s;
+    if (accumulate != 0 && accumulate != 1) return fail(TP_EINVAL, "accumulate must be 0 or 1");
+    NEED(du, "du");
+    NEED(resid, "resid");
+    NEED(x, "x");
+    NEED(gamma, "gamma");
+    NEED4(mean, "mean");
+    NEED4(rstd, "rstd");
+    NEED(dx, "dx");
+    NEED(dgamma, "dgamma");
+    NEED(dbeta, "dbeta");
+    NEED(work, "work");
+    if (!aligned16(du) || !aligned16(resid) || !aligned16(x) || !aligned16(gamma) || !aligned16(dx) ||
+        !aligned16(dgamma) || !aligned16(dbeta) || !aligned16(work))
+        return fail(TP_EALIGN, "du, resid, x, gamma, dx, dgamma, dbeta and work must be 16-byte aligned");
+    return hip_status(layernorm_bwd(d.dt, (int)rows, (int)d.h, du, resid, x, gamma, mean, rstd, dx, dgamma, dbeta,
+                                    accumulate != 0, (float *)work, (hipStream_t)stream),
+                      "layernorm backward");
 }
 
 }  // extern "C"
