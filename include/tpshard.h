@@ -196,7 +196,7 @@ typedef enum {
 
 /* Bytes of the opaque "saved" buffer: activations the forward keeps for the
  * backward, for the whole sequence (u1, LN statistics, Q, O, log-sum-exp,
- * u2, Z, GELU(Z)).  0 if cfg is invalid. */
+ * u2, GELU'(Z), GELU(Z)).  0 if cfg is invalid. */
 size_t tp_shard_saved_bytes(const tp_shard_cfg *cfg);
 
 /* Bytes of the "scratch" buffer (any call, any slice range).  The backward

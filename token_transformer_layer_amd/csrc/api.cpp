@@ -75,7 +75,7 @@ int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 // Regions of the saved buffer (full sequence, T = s*b token rows).
 struct Saved {
-    int64_t u1, mu1, rs1, q, o, lse, u2, mu2, rs2, z, g, total;
+    int64_t u1, mu1, rs1, q, o, lse, u2, mu2, rs2, gz, g, total;  // gz: GELU'(Z)
 };
 Saved saved_layout(const Dims &d) {
     Saved L;
@@ -90,7 +90,7 @@ Saved saved_layout(const Dims &d) {
     L.u2 = take(d.T * d.h * d.es);
     L.mu2 = take(d.T * 4);
     L.rs2 = take(d.T * 4);
-    L.z = take(d.T * d.ft * d.es);
+    L.gz = take(d.T * d.ft * d.es);
     L.g = take(d.T * d.ft * d.es);
     L.total = off;
     return L;
@@ -297,10 +297,10 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         HIPCALL(layernorm_fwd(d.dt, (int)nrows, (int)d.h, cfg->ln_eps, at<const char *>(in, r0 * d.h * es), w->ln2_g,
                               w->ln2_b, u2, at<float *>(saved, L.mu2 + r0 * 4), at<float *>(saved, L.rs2 + r0 * 4), st),
                 "layernorm forward (LN2)");
-    void *z = at<char *>(saved, L.z + r0 * d.ft * es);
+    void *gz = at<char *>(saved, L.gz + r0 * d.ft * es);
     void *gg = at<char *>(saved, L.g + r0 * d.ft * es);
     e = fresh();
-    e.c = z; e.ldc = d.ft; e.c2 = gg; e.ldc2 = d.ft; e.bias = w->b1;
+    e.c = gz; e.ldc = d.ft; e.c2 = gg; e.ldc2 = d.ft; e.bias = w->b1;
     HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{u2, d.h, true}, Mat{w->w1, d.h, true}, Epi::BiasGelu, e, st),
             "FC1 product");
     e = fresh();
@@ -410,7 +410,7 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     if (mlp) {
         // dZ = (dY W2) * GELU'(Z); dU2,r = dZ W1
         e = fresh();
-        e.c = dz; e.ldc = d.ft; e.aux = at<const char *>(saved, L.z + r0 * d.ft * es); e.ldaux = d.ft;
+        e.c = dz; e.ldc = d.ft; e.aux = at<const char *>(saved, L.gz + r0 * d.ft * es); e.ldaux = d.ft;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.ft, (int)d.h, Mat{dyr, d.h, true}, Mat{w->w2, d.ft, false}, Epi::GeluGrad,
                      e, st),
                 "FC2 input-gradient product");

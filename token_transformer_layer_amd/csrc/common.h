@@ -130,6 +130,14 @@ __device__ __forceinline__ float gelu_grad_f(float z) {
     return cdf + z * pdf;
 }
 
+// GELU and its derivative together (they share Phi(z)).
+__device__ __forceinline__ void gelu_and_grad(float z, float &g, float &gp) {
+    const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * __expf(-0.5f * z * z);
+    g = z * cdf;
+    gp = cdf + z * pdf;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -67,25 +67,28 @@ struct EpiStore {
 
 template <typename T>
 struct EpiBiasGelu {
-    T *z;  // may be null
-    int64_t ldz;
+    T *gz;  // GELU'(z), for the backward; may be null
+    int64_t ldgz;
     T *g;
     int64_t ldg;
     const T *bias;
     __device__ __forceinline__ void operator()(int m, int n, float v) const {
-        float zz = v + to_f32(bias[n]);
-        if (z) z[m * ldz + n] = from_f32<T>(zz);
-        g[m * ldg + n] = from_f32<T>(gelu_f(zz));
+        float gg, gp;
+        gelu_and_grad(v + to_f32(bias[n]), gg, gp);
+        if (gz) gz[m * ldgz + n] = from_f32<T>(gp);
+        g[m * ldg + n] = from_f32<T>(gg);
     }
     __device__ __forceinline__ void row8(int m, int n, const float v[8]) const {
-        float b[8], zz[8], gg[8];
+        float b[8], gp[8], gg[8];
         load8(bias + n, b);
+        if (gz) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            zz[i] = v[i] + b[i];
-            gg[i] = gelu_f(zz[i]);
+            for (int i = 0; i < 8; ++i) gelu_and_grad(v[i] + b[i], gg[i], gp[i]);
+            store8(gz + m * ldgz + n, gp);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) gg[i] = gelu_f(v[i] + b[i]);
         }
-        if (z) store8(z + m * ldz + n, zz);
         store8(g + m * ldg + n, gg);
     }
 };
@@ -94,16 +97,16 @@ template <typename T>
 struct EpiGeluGrad {
     T *c;
     int64_t ldc;
-    const T *z;
-    int64_t ldz;
+    const T *gz;  // GELU'(Z) saved by the forward's EpiBiasGelu
+    int64_t ldgz;
     __device__ __forceinline__ void operator()(int m, int n, float v) const {
-        c[m * ldc + n] = from_f32<T>(v * gelu_grad_f(to_f32(z[m * ldz + n])));
+        c[m * ldc + n] = from_f32<T>(v * to_f32(gz[m * ldgz + n]));
     }
     __device__ __forceinline__ void row8(int m, int n, const float v[8]) const {
-        float zz[8], o[8];
-        load8(z + m * ldz + n, zz);
+        float d[8], o[8];
+        load8(gz + m * ldgz + n, d);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = v[i] * gelu_grad_f(zz[i]);
+        for (int i = 0; i < 8; ++i) o[i] = v[i] * d[i];
         store8(c + m * ldc + n, o);
     }
 };
@@ -621,6 +624,11 @@ static uint32_t extent_bytes(int rows, int k, const Mat &m, int es) {
     return (uint32_t)(last * es);
 }
 
+// Tile rows per group of the XCD-aware tile order (see tile_of): 8 measured
+// best or within noise of it on every product of the layer (4 and 16 lose up
+// to 5% on the long-K products).
+static int g_group_rows = 8;
+
 template <class C, bool AK, bool BK_, class E>
 static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
     static bool attr_set = false;
@@ -632,7 +640,7 @@ static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
     }
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
     hipLaunchKernelGGL((gemm_bf16_dl_kernel<C, AK, BK_, E>), dim3(tiles, g.nsplit), dim3(C::kThreads), C::kLds, st, g,
-                       epi, 4);
+                       epi, g_group_rows);
     return hipGetLastError();
 }
 
@@ -647,7 +655,7 @@ static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
     }
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
     hipLaunchKernelGGL((gemm_bf16_pp_kernel<C, AK, BK_, E>), dim3(tiles, g.nsplit), dim3(C::kThreads), C::kLds, st, g,
-                       epi, 4);
+                       epi, g_group_rows);
     return hipGetLastError();
 }
 

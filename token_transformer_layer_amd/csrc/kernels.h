@@ -22,8 +22,8 @@ enum class Epi {
     StoreF32,  // c fp32 [M][ldc] = acc
     AccumF32,  // c fp32 [M][ldc] += acc
     Store,     // c T [M][ldc] = acc
-    BiasGelu,  // z = acc + bias[n]; c T = z (if c != null); c2 T = GELU(z)
-    GeluGrad,  // c T = acc * GELU'(aux[m][n])  (aux T [M][ldaux])
+    BiasGelu,  // z = acc + bias[n]; c T = GELU'(z) (if c != null); c2 T = GELU(z)
+    GeluGrad,  // c T = acc * aux[m][n]  (aux T [M][ldaux]: the GELU'(Z) BiasGelu stored)
     Qkv,       // acc + bias[n] scattered into q/k/v [b, n_t, s, d]
 };
 

@@ -215,22 +215,36 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(int rows, int h, int r
 // `stride` floats apart.  A workgroup owns 32 columns; its 8 row groups each
 // sum every 8th partial row, and the 8 sums are added in a fixed order.
 constexpr int kRedCols = 32, kRedGroups = kThreads / kRedCols;
-__global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n, int64_t stride,
+// Columns c < n0 go to out0[c], columns n0 <= c < n to out1[c - n0] (two
+// vectors reduced by one launch).
+__global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n, int n0, int64_t stride,
                                                                  const float *__restrict__ partials,
-                                                                 float *__restrict__ out, int accumulate) {
+                                                                 float *__restrict__ out0, float *__restrict__ out1,
+                                                                 int accumulate) {
     __shared__ float part[kRedGroups][kRedCols];
     const int cx = threadIdx.x % kRedCols, gy = threadIdx.x / kRedCols;
     const int c = blockIdx.x * kRedCols + cx;
     float s = 0.f;
-    if (c < n)
-        for (int k = gy; k < nblk; k += kRedGroups) s += partials[(size_t)k * stride + c];
+    if (c < n) {
+        int k = gy;
+        // four partial rows' loads in flight, added in row order
+        for (; k + 3 * kRedGroups < nblk; k += 4 * kRedGroups) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = partials[(size_t)(k + u * kRedGroups) * stride + c];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s += v[u];
+        }
+        for (; k < nblk; k += kRedGroups) s += partials[(size_t)k * stride + c];
+    }
     part[gy][cx] = s;
     __syncthreads();
     if (gy == 0 && c < n) {
         float t = 0.f;
 #pragma unroll
         for (int k = 0; k < kRedGroups; ++k) t += part[k][cx];
-        out[c] = accumulate ? out[c] + t : t;
+        float *o = c < n0 ? out0 + c : out1 + (c - n0);
+        *o = accumulate ? *o + t : t;
     }
 }
 
@@ -243,7 +257,18 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(int rows, int n, int64
     if (c8 >= n) return;
     const int r0 = blockIdx.y * rpc, r1 = min(rows, r0 + rpc);
     float s[8] = {};
-    for (int r = r0; r < r1; ++r) {
+    int r = r0;
+    // four rows' loads in flight, added in row order
+    for (; r + 4 <= r1; r += 4) {
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load8(a + (size_t)(r + u) * lda + c8, v[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s[j] += v[u][j];
+    }
+    for (; r < r1; ++r) {
         float v[8];
         load8(a + (size_t)r * lda + c8, v);
 #pragma unroll
@@ -371,17 +396,12 @@ hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int gb = (h + kRedCols - 1) / kRedCols;
-    {
-        TraceScope ts(st, "block_reduce", 0.0, (double)nblk * h * 4 + 8.0 * h);
-        hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
-                           (const float *)partials, dg, accumulate ? 1 : 0);
-    }
-    {
-        TraceScope ts(st, "block_reduce", 0.0, (double)nblk * h * 4 + 8.0 * h);
-        hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, h, (int64_t)2 * h,
-                           (const float *)(partials + h), db, accumulate ? 1 : 0);
-    }
+    // dgamma and dbeta: the partial rows are [2][h] per block, one launch
+    // reduces both halves
+    const int gb = (2 * h + kRedCols - 1) / kRedCols;
+    TraceScope ts(st, "block_reduce", 0.0, (double)nblk * 2 * h * 4 + 16.0 * h);
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, 2 * h, h, (int64_t)2 * h,
+                       (const float *)partials, dg, db, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -404,8 +424,8 @@ hipError_t colsum(DType dt, int rows, int n, const void *a, int64_t lda, float *
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     TraceScope ts(st, "block_reduce", 0.0, (double)nch * n * 4 + 8.0 * n);
-    hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kRedCols - 1) / kRedCols), dim3(kThreads), 0, st, nch, n,
-                       (int64_t)n, (const float *)partials, out, accumulate ? 1 : 0);
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kRedCols - 1) / kRedCols), dim3(kThreads), 0, st, nch, n, n,
+                       (int64_t)n, (const float *)partials, out, out, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
