@@ -496,14 +496,14 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[0][j] = OpB::frag(smem + OpA::kBytes, wn * WTN + j * 32, 0, lane);
 
-        auto mfmas = [&](int set) {
+        auto mfmas = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
         };
-        auto reads = [&](const char *stage, int kk, int set) {
+        auto reads = [&](const char *stage, int kk, int set) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[set][i] = OpA::frag(stage, wm * WTM + i * 32, kk, lane);
 #pragma unroll
@@ -511,7 +511,7 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
         };
         // k-steps 0 .. KSTEPS-2 of a tile: next k-step's fragments are read
         // while this one's MFMAs run
-        auto inner = [&](const char *cur) {
+        auto inner = [&](const char *cur) __attribute__((always_inline)) {
 #pragma unroll
             for (int kk = 0; kk + 1 < KSTEPS; ++kk) {
                 reads(cur, kk + 1, (kk + 1) & 1);
@@ -660,7 +660,8 @@ static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
 }
 
 using Dl128 = DlCfg<128, 128, 2, 2, 2>;              // 64 KB of LDS: two workgroups per compute unit
-using Pp256 = DlCfg<256, 256, 2, 2, 4, 32>;          // 128 KB, three K-tiles in flight, one workgroup
+using Pp256 = DlCfg<256, 256, 2, 2, 2, 64>;          // 128 KB, one workgroup per compute unit
+using Pp256x192 = DlCfg<256, 192, 2, 2, 2, 64>;      // 112 KB, one workgroup per compute unit
 using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups per compute unit
 
 // Tile configurations, chosen per product shape from measurements on MI355X
@@ -670,7 +671,7 @@ using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups pe
 // load path delivers, so larger tiles win wherever there are enough of them
 // to fill the 256 compute units; the plain (non-pipelined) 128x128 kernel
 // is the best fit for short reductions and narrow outputs.
-enum class Tile { Dl128, Pp128, Pp256x128, Pp256 };
+enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192 };
 
 static std::atomic<int> g_force_tile{-1};
 
@@ -683,11 +684,12 @@ static Tile pick_tile(int M, int N, int K, bool ak, bool bk) {
     if (forced >= 0) return (Tile)forced;
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);
+    const long t256x192 = (long)((M + 255) / 256) * ((N + 191) / 192);
     if (ak && bk) {
-        // forward form: long reductions with at least half a round of
-        // 256x256 tiles run best on them (QKV, FC1, large squares)
-        if (K >= 6144 && t256 >= 128 && (t256 >= 512 || t256 < 256)) return Tile::Pp256;
-        if (K >= 16384) return Tile::Pp128;
+        // forward form: long reductions run best on the large tiles, 256x256
+        // once there are two rounds of them, else 256x192 (QKV, FC1, FC2)
+        if (K >= 6144 && t256 >= 512) return Tile::Pp256;
+        if (K >= 6144 && t256x192 >= 128) return Tile::Pp256x192;
         return Tile::Dl128;
     }
     if (ak && !bk) {
@@ -707,6 +709,7 @@ static const char *tile_name(Tile t) {
     case Tile::Pp128: return "p128";
     case Tile::Pp256x128: return "256x128";
     case Tile::Pp256: return "256";
+    case Tile::Pp256x192: return "256x192";
     }
     return "?";
 }
@@ -716,6 +719,7 @@ static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
         switch (pick_tile(g.M, g.N, g.K, AK, BK_)) {
         case Tile::Pp256: return launch_pp<Pp256, AK, BK_>(g, epi, st);
+        case Tile::Pp256x192: return launch_pp<Pp256x192, AK, BK_>(g, epi, st);
         case Tile::Pp256x128: return launch_pp<Pp256x128, AK, BK_>(g, epi, st);
         case Tile::Pp128: return launch_pp<Dl128, AK, BK_>(g, epi, st);
         case Tile::Dl128: break;
