@@ -218,7 +218,21 @@ struct DlOperand {
         if constexpr (BK == 64) return lds_swz(r);
         else return (r >> 2) & 3;
     }
-    __device__ static __forceinline__ int swz_k(int k) { return (k & 3) * 4 & (kUnits - 1); }
+    // [BK][ROWS] layout: the 16-byte unit u of row k sits at position
+    // unit_pos(u, k), shifted by 4 (k % 4) units (64 bytes), so the four
+    // consecutive rows a transposing read touches together land on distinct
+    // banks; XOR for power-of-two widths, rotation otherwise (both bijective).
+    static constexpr bool kPow2Units = (kUnits & (kUnits - 1)) == 0;
+    __device__ static __forceinline__ int unit_pos(int u, int k) {
+        const int sh = (k & 3) * 4 % kUnits;
+        if constexpr (kPow2Units) return u ^ sh;
+        else return u + sh < kUnits ? u + sh : u + sh - kUnits;
+    }
+    __device__ static __forceinline__ int unit_src(int pos, int k) {
+        const int sh = (k & 3) * 4 % kUnits;
+        if constexpr (kPow2Units) return pos ^ sh;
+        else return pos >= sh ? pos - sh : pos - sh + kUnits;
+    }
 
     __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char *stage, int mn0, int k0, int MN,
                                                  int K, int64_t ld, int wave, int lane) {
@@ -234,7 +248,7 @@ struct DlOperand {
             } else {
                 const int byte = I * 1024 + lane * 16;
                 const int k = byte / kPitch;
-                const int u = ((byte % kPitch) >> 4) ^ swz_k(k);
+                const int u = unit_src((byte % kPitch) >> 4, k);
                 const int gk = k0 + k, gm = mn0 + u * 8;
                 off = (gm < MN && gk < K) ? (uint32_t)((gk * ld + gm) * 2) : kOOB;
             }
@@ -254,8 +268,8 @@ struct DlOperand {
             const int mn = base + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
             const int k = kk * 16 + 8 * (lane >> 5) + (L >> 2);
             const int u = mn >> 3, within = (mn & 7) * 2;
-            const char *p0 = stage + k * kPitch + ((u ^ swz_k(k)) << 4) + within;
-            const char *p1 = stage + (k + 4) * kPitch + ((u ^ swz_k(k + 4)) << 4) + within;
+            const char *p0 = stage + k * kPitch + (unit_pos(u, k) << 4) + within;
+            const char *p1 = stage + (k + 4) * kPitch + (unit_pos(u, k + 4) << 4) + within;
             u32x2 a = lds_read_tr16(p0), b = lds_read_tr16(p1);
             return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
         }
@@ -662,6 +676,7 @@ static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
 using Dl128 = DlCfg<128, 128, 2, 2, 2>;              // 64 KB of LDS: two workgroups per compute unit
 using Pp256 = DlCfg<256, 256, 2, 2, 2, 64>;          // 128 KB, one workgroup per compute unit
 using Pp256x192 = DlCfg<256, 192, 2, 2, 2, 64>;      // 112 KB, one workgroup per compute unit
+using Pp128x192 = DlCfg<128, 192, 2, 2, 2, 64, 2>;   // 80 KB, two workgroups per compute unit
 using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups per compute unit
 
 // Tile configurations, chosen per product shape from measurements on MI355X
@@ -671,11 +686,11 @@ using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups pe
 // load path delivers, so larger tiles win wherever there are enough of them
 // to fill the 256 compute units; the plain (non-pipelined) 128x128 kernel
 // is the best fit for short reductions and narrow outputs.
-enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192 };
+enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192 };
 
 static std::atomic<int> g_force_tile{-1};
 
-constexpr int64_t kSplitMaxFloats = 512LL * 128 * 128;  // 32 MB: about two rounds of 128x128 tiles
+constexpr int64_t kSplitMaxFloats = 512LL * 128 * 192;  // 48 MB: about two rounds of 128x192 tiles
 
 void gemm_force_tile(int tile) { g_force_tile.store(tile); }
 
@@ -683,23 +698,14 @@ static Tile pick_tile(int M, int N, int K, bool ak, bool bk) {
     const int forced = g_force_tile.load(std::memory_order_relaxed);
     if (forced >= 0) return (Tile)forced;
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-    const long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);
-    const long t256x192 = (long)((M + 255) / 256) * ((N + 191) / 192);
-    if (ak && bk) {
-        // forward form: long reductions run best on the large tiles, 256x256
-        // once there are two rounds of them, else 256x192 (QKV, FC1, FC2)
-        if (K >= 6144 && t256 >= 512) return Tile::Pp256;
-        if (K >= 6144 && t256x192 >= 128) return Tile::Pp256x192;
-        return Tile::Dl128;
-    }
-    if (ak && !bk) {
-        // input-gradient form
-        if (K >= 12288 && N >= 4096 && t256x128 >= 256) return Tile::Pp256x128;
-        if (K >= 6144 && N >= 8192) return Tile::Pp128;
-        return Tile::Dl128;
-    }
-    // weight-gradient form: wide outputs on both sides
-    if (M >= 4096 && N >= 4096 && t256x128 >= 512) return Tile::Pp256x128;
+    const long t128x192 = (long)((M + 127) / 128) * ((N + 191) / 192);
+    // Two 128x192 workgroups per compute unit (64-wide K-tiles: whole cache
+    // lines per row) are the best measured fit for every product of the
+    // layer shards; 256x256 tiles win once there are two rounds of them with
+    // a long reduction (large squares); products too small for a round of
+    // 128x192 tiles take 128x128 tiles and split their reduction.
+    if (ak && bk && K >= 6144 && t256 >= 512) return Tile::Pp256;
+    if (t128x192 >= 192 && K >= 512) return Tile::Pp128x192;
     return Tile::Dl128;
 }
 
@@ -710,6 +716,7 @@ static const char *tile_name(Tile t) {
     case Tile::Pp256x128: return "256x128";
     case Tile::Pp256: return "256";
     case Tile::Pp256x192: return "256x192";
+    case Tile::Pp128x192: return "128x192";
     }
     return "?";
 }
@@ -720,6 +727,7 @@ static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
         switch (pick_tile(g.M, g.N, g.K, AK, BK_)) {
         case Tile::Pp256: return launch_pp<Pp256, AK, BK_>(g, epi, st);
         case Tile::Pp256x192: return launch_pp<Pp256x192, AK, BK_>(g, epi, st);
+        case Tile::Pp128x192: return launch_pp<Pp128x192, AK, BK_>(g, epi, st);
         case Tile::Pp256x128: return launch_pp<Pp256x128, AK, BK_>(g, epi, st);
         case Tile::Pp128: return launch_pp<Dl128, AK, BK_>(g, epi, st);
         case Tile::Dl128: break;
@@ -768,15 +776,18 @@ static hipError_t dispatch_layout(const GemmArgs &g, bool ak, bool bk, Epi kind,
     return hipErrorInvalidValue;
 }
 
-// Number of reduction splits: a product whose 128x128 tiles do not fill the
+// Number of reduction splits: a product whose 128-row tiles do not fill the
 // compute units (short token ranges, narrow outputs) splits its reduction
-// so that about two workgroups per compute unit run, when the caller's
+// so that about 1.5 workgroups per compute unit run, when the caller's
 // workspace holds the partial products (at most kSplitMaxFloats floats).
 static int pick_splits(int M, int N, int K, Tile t, int64_t ws_floats) {
-    if (t != Tile::Dl128 && t != Tile::Pp128) return 1;
-    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (t != Tile::Dl128 && t != Tile::Pp128 && t != Tile::Pp128x192) return 1;
+    const int bn = t == Tile::Pp128x192 ? 192 : 128;
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + bn - 1) / bn);
     if (tiles >= 256) return 1;
-    int sp = (int)((512 + tiles / 2) / tiles);
+    // about 384 workgroups (1.5 per compute unit): measured better than two
+    // rounds, whose extra partial sums cost more than the fill they add
+    int sp = (int)((384 + tiles - 1) / tiles);
     sp = std::min(sp, 8);
     sp = std::min(sp, K / 512);
     while (sp > 1 && (int64_t)sp * M * N > ws_floats) --sp;
