@@ -461,6 +461,7 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         a.dk_acc = kvg->dk; a.dv_acc = kvg->dv;
         a.k_final0 = (int)o0;
         a.acc_in = kvg->done_from != d.s;
+        a.work = at<float *>(scratch, S.attn);
         HIPCALL(attn_bwd(d.dt, a, st), "attention backward");
         // dU1,r = dQKV W_qkv
         e = fresh();

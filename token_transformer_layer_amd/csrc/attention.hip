@@ -38,6 +38,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 struct AttnP {
     int batch, nt, seq, q0, q1, k_final0, acc_in;
+    int chunk_tiles, max_chunks, nblocks;  // work split of the backward (tiles per chunk)
+    float *part;                            // partial sums of split blocks
     float scale;
     const bf16 *q, *k, *v, *o, *dout;
     bf16 *out;  // forward: O; backward: dQKV
@@ -552,8 +554,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
-    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
-    const int kb0 = blockIdx.x * kBwdBK;
+    const int chunk = blockIdx.x, kb = blockIdx.y, bh = blockIdx.z, bi = bh / a.nt, head = bh % a.nt;
+    const int kb0 = kb * kBwdBK;
     const int kw0 = kb0 + w * 32;
     const int my_k = kw0 + li;
     const int ht = a.nt * D;
@@ -579,13 +581,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x16{}; acc_dv[i] = f32x16{}; }
 
     const int qstart = max(a.q0, kb0);
-    const int nqt = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
+    const int nqt_all = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
+    // this workgroup's chunk of the query tiles that see the key block
+    const int nch = max(1, (nqt_all + a.chunk_tiles - 1) / a.chunk_tiles);
+    if (chunk >= nch) return;  // whole workgroup
+    const int t_first = chunk * a.chunk_tiles;
+    const int nqt = max(0, min(nqt_all - t_first, a.chunk_tiles));
     const int64_t do_base = (int64_t)bi * ht + head * D;  // dO row p at do_base + p * batch * ht
     const int64_t do_ld = (int64_t)a.batch * ht;
     const int64_t stat0 = (int64_t)bh * a.seq;
 
     auto issue = [&](int t, char *st) {
-        const int p0 = qstart + t * 64;
+        const int p0 = qstart + (t_first + t) * 64;
         rows_tile_dma<D>(rq, st, slab, D, p0, a.q1, w, lane);
         rows_tile_dma<D>(rdo, st + TILE, do_base, do_ld, p0, a.q1, w, lane);
     };
@@ -593,7 +600,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     float stat = 0.f;
     auto load_stat = [&](int t) {
         if (tid < 128) {
-            const int p = qstart + t * 64 + (tid & 63);
+            const int p = qstart + (t_first + t) * 64 + (tid & 63);
             stat = p < a.q1 ? (tid < 64 ? a.lse[stat0 + p] * kLog2e : a.delta[stat0 + p]) : 0.f;
         }
     };
@@ -613,7 +620,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
             issue(t + 1, smem + ((t + 1) & 1) * STAGE);
             load_stat(t + 1);
         }
-        const int p0 = qstart + t * 64;
+        const int p0 = qstart + (t_first + t) * 64;
         const float *lse_s = (const float *)(st + 2 * TILE);
         const float *del_s = lse_s + 64;
 #pragma unroll
@@ -655,6 +662,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
         if (t + 1 < nqt) store_stat(smem + ((t + 1) & 1) * STAGE);
     }
     if (my_k >= a.q1) return;
+    if (nch > 1) {
+        // partial sums of this chunk (unscaled), [2][128 keys][D] per item
+        float *pk = a.part + (((int64_t)bh * a.nblocks + kb) * a.max_chunks + chunk) * (2 * kBwdBK * D) +
+                    (int64_t)(w * 32 + li) * D;
+        float *pv = pk + kBwdBK * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = db * 32 + 8 * r + 4 * g;
+                *(f32x4 *)(pk + j) = f32x4{acc_dk[db][4 * r], acc_dk[db][4 * r + 1], acc_dk[db][4 * r + 2],
+                                           acc_dk[db][4 * r + 3]};
+                *(f32x4 *)(pv + j) = f32x4{acc_dv[db][4 * r], acc_dv[db][4 * r + 1], acc_dv[db][4 * r + 2],
+                                           acc_dv[db][4 * r + 3]};
+            }
+        return;
+    }
     // acc[db] register v: d = db*32 + 8(v/4) + 4g + v%4 of key my_k
     const int64_t arow = slab + (int64_t)my_k * D;
     const bool final_key = my_k >= a.k_final0;
@@ -682,18 +706,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_mfma32(AttnP a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dq_mfma32(AttnP a) {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int TILE = 64 * D * 2;
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
-    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
-    const int qt0 = a.q0 + blockIdx.x * kBwdBQ;
+    const int chunk = blockIdx.x, qb = blockIdx.y, bh = blockIdx.z, bi = bh / a.nt, head = bh % a.nt;
+    const int qt0 = a.q0 + qb * kBwdBQ;
     const int my_q = qt0 + w * 32 + li;
     const int q_eff = min(my_q, a.q1 - 1);
     const int kend = min(a.q1, qt0 + kBwdBQ);
-    const int ntiles = (kend + 63) / 64;
+    const int ntiles_all = (kend + 63) / 64;
+    // this workgroup's chunk of the key tiles its queries see
+    const int nch = max(1, (ntiles_all + a.chunk_tiles - 1) / a.chunk_tiles);
+    if (chunk >= nch) return;  // whole workgroup
+    const int t0 = chunk * a.chunk_tiles, t1 = min(ntiles_all, t0 + a.chunk_tiles);
     const int ht = a.nt * D;
     const int64_t slab = (int64_t)bh * a.seq * D;
     const float sl2 = a.scale * kLog2e;
@@ -721,15 +749,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma32(AttnP a) {
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-    kv_tile_dma<D>(rk, smem, slab, 0, kend, w, lane);
-    kv_tile_dma<D>(rv, smem + TILE, slab, 0, kend, w, lane);
-    for (int t = 0; t < ntiles; ++t) {
+    kv_tile_dma<D>(rk, smem, slab, t0 * 64, kend, w, lane);
+    kv_tile_dma<D>(rv, smem + TILE, slab, t0 * 64, kend, w, lane);
+    for (int t = t0; t < t1; ++t) {
         wait_vmcnt<0>();
         __syncthreads();
-        const char *ks = smem + (t & 1) * 2 * TILE;
+        const char *ks = smem + ((t - t0) & 1) * 2 * TILE;
         const char *vs = ks + TILE;
-        if (t + 1 < ntiles) {
-            char *nx = smem + ((t + 1) & 1) * 2 * TILE;
+        if (t + 1 < t1) {
+            char *nx = smem + ((t + 1 - t0) & 1) * 2 * TILE;
             kv_tile_dma<D>(rk, nx, slab, (t + 1) * 64, kend, w, lane);
             kv_tile_dma<D>(rv, nx + TILE, slab, (t + 1) * 64, kend, w, lane);
         }
@@ -762,6 +790,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma32(AttnP a) {
             for (int k4 = 0; k4 < 4; ++k4) acc[db] = mfma32(tr_frag<D>(ks, 16 * k4, db, lane), sb[k4], acc[db]);
     }
     if (!qok) return;
+    if (nch > 1) {
+        // partial dQ of this chunk (unscaled), [128 queries][D] per item
+        float *pq = a.part + (((int64_t)bh * a.nblocks + qb) * a.max_chunks + chunk) * (kBwdBQ * D) +
+                    (int64_t)(w * 32 + li) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *(f32x4 *)(pq + db * 32 + 8 * r + 4 * g) =
+                    f32x4{acc[db][4 * r], acc[db][4 * r + 1], acc[db][4 * r + 2], acc[db][4 * r + 3]};
+        return;
+    }
     bf16 *dst = a.out + ((int64_t)my_q * a.batch + bi) * (3 * ht) + head * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -771,6 +811,82 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma32(AttnP a) {
             *(u32x2 *)(dst + j) = u32x2{pack_bf2(acc[db][4 * r] * a.scale, acc[db][4 * r + 1] * a.scale),
                                         pack_bf2(acc[db][4 * r + 2] * a.scale, acc[db][4 * r + 3] * a.scale)};
         }
+}
+
+// Split backward blocks: the partial sums of a block's chunks are added in
+// chunk order, then finished as the unsplit kernels finish them (dK scaled;
+// fp32 accumulators or final bf16 rows).  One workgroup per block, 8
+// consecutive columns per thread.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_combine(AttnP a) {
+    const int kb = blockIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int kb0 = kb * kBwdBK;
+    const int qstart = max(a.q0, kb0);
+    const int nqt_all = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
+    const int nch = max(1, (nqt_all + a.chunk_tiles - 1) / a.chunk_tiles);
+    if (nch == 1) return;
+    const int ht = a.nt * D;
+    const int64_t slab = (int64_t)bh * a.seq * D;
+    const float *base = a.part + ((int64_t)bh * a.nblocks + kb) * a.max_chunks * (2 * kBwdBK * D);
+    for (int i = threadIdx.x; i < kBwdBK * D / 8; i += 256) {
+        const int kl = i / (D / 8), j = (i % (D / 8)) * 8;
+        const int key = kb0 + kl;
+        if (key >= a.q1) continue;
+        float dk[8] = {}, dv[8] = {};
+        for (int c = 0; c < nch; ++c) {
+            float x[8], y[8];
+            const float *pk = base + (int64_t)c * (2 * kBwdBK * D) + kl * D + j;
+            load8(pk, x);
+            load8(pk + kBwdBK * D, y);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { dk[u] += x[u]; dv[u] += y[u]; }
+        }
+        const int64_t arow = slab + (int64_t)key * D + j;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dk[u] *= a.scale;
+        if (a.acc_in) {
+            float x[8], y[8];
+            load8(a.dk_acc + arow, x);
+            load8(a.dv_acc + arow, y);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { dk[u] += x[u]; dv[u] += y[u]; }
+        }
+        if (key >= a.k_final0) {
+            bf16 *dst = a.out + ((int64_t)key * a.batch + bi) * (3 * ht) + head * D + j;
+            store8(dst + ht, dk);
+            store8(dst + 2 * ht, dv);
+        } else {
+            store8(a.dk_acc + arow, dk);
+            store8(a.dv_acc + arow, dv);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_combine(AttnP a) {
+    const int qb = blockIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    const int qt0 = a.q0 + qb * kBwdBQ;
+    const int kend = min(a.q1, qt0 + kBwdBQ);
+    const int ntiles_all = (kend + 63) / 64;
+    const int nch = max(1, (ntiles_all + a.chunk_tiles - 1) / a.chunk_tiles);
+    if (nch == 1) return;
+    const int ht = a.nt * D;
+    const float *base = a.part + ((int64_t)bh * a.nblocks + qb) * a.max_chunks * (kBwdBQ * D);
+    for (int i = threadIdx.x; i < kBwdBQ * D / 8; i += 256) {
+        const int ql = i / (D / 8), j = (i % (D / 8)) * 8;
+        const int q = qt0 + ql;
+        if (q >= a.q1) continue;
+        float dq[8] = {};
+        for (int c = 0; c < nch; ++c) {
+            float x[8];
+            load8(base + (int64_t)c * (kBwdBQ * D) + ql * D + j, x);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dq[u] += x[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dq[u] *= a.scale;
+        store8(a.out + ((int64_t)q * a.batch + bi) * (3 * ht) + head * D + j, dq);
+    }
 }
 
 // delta[bh][p] = sum_j dO[p][j] O[p][j]: D/8 lanes per (query, head), 8
@@ -941,9 +1057,25 @@ static void fwd_split(const AttnArgs &x, AttnFwdP &p) {
     p.max_chunks = (max_tiles + p.chunk_tiles - 1) / p.chunk_tiles;
 }
 
+constexpr int kBwdMaxChunks = 8;
+
 size_t attn_fwd_work_floats(int batch, int nt, int seq, int d) {
     const int nqt = (seq + kFwdBQ - 1) / kFwdBQ;
-    return (size_t)batch * nt * nqt * kFwdMaxChunks * kFwdBQ * (d + 2);
+    const size_t fwd = (size_t)batch * nt * nqt * kFwdMaxChunks * kFwdBQ * (d + 2);
+    // the backward's partial sums of split blocks: dK and dV per 128 keys,
+    // or dQ per 128 queries, up to kBwdMaxChunks chunks per block
+    const int nb = (seq + kBwdBK - 1) / kBwdBK;
+    const size_t bwd = (size_t)batch * nt * nb * kBwdMaxChunks * 2 * kBwdBK * d;
+    return fwd > bwd ? fwd : bwd;
+}
+
+// Tiles per chunk of a split backward launch: enough work items for the
+// chip (`target`), at most kBwdMaxChunks chunks per block, at least two
+// tiles per chunk.
+static int bwd_chunk_tiles(double total_tiles, int max_tiles, int target) {
+    int ct = (int)std::ceil(total_tiles / target);
+    ct = std::max(ct, (max_tiles + kBwdMaxChunks - 1) / kBwdMaxChunks);
+    return std::max(ct, 2);
 }
 
 hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
@@ -1016,31 +1148,62 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
         p.dout = (const bf16 *)x.dout; p.out = (bf16 *)x.dqkv; p.lse = x.lse; p.delta = x.delta;
         p.dk_acc = x.dk_acc; p.dv_acc = x.dv_acc;
         p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
-        dim3 gk((x.q1 + kBwdBK - 1) / kBwdBK, bh), gq((nq + kBwdBQ - 1) / kBwdBQ, bh);
+        p.part = x.work;
         const int tile = 64 * x.d * 2;
         const int lds_kv = 2 * (2 * tile + 1024), lds_q = 2 * 2 * tile;
         {
+            // dK, dV: key block kb sees the query tiles from max(q0, 128 kb)
+            const int nkb = (x.q1 + kBwdBK - 1) / kBwdBK;
+            double total = 0;
+            int max_t = 1;
+            for (int kb = 0; kb < nkb; ++kb) {
+                const int qs = std::max(x.q0, kb * kBwdBK);
+                const int n = qs < x.q1 ? (x.q1 - qs + 63) / 64 : 0;
+                total += n;
+                max_t = std::max(max_t, n);
+            }
+            p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, 320);
+            p.max_chunks = (max_t + p.chunk_tiles - 1) / p.chunk_tiles;
+            p.nblocks = nkb;
+            dim3 gk(p.max_chunks, nkb, bh);
             TraceScope ts(st, "attn_bwd_dkdv_bf16", 8.0 * x.d * pairs, kv_bytes);
             if (x.d == 128) {
                 hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<128>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
                 hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<128>, gk, dim3(256), lds_kv, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<128>, dim3(nkb, bh), dim3(256), 0, st, p);
             } else {
                 hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<64>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
                 hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<64>, gk, dim3(256), lds_kv, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<64>, dim3(nkb, bh), dim3(256), 0, st, p);
             }
         }
         {
+            // dQ: query block qb sees the key tiles before min(q1, its end)
+            const int nqb = (nq + kBwdBQ - 1) / kBwdBQ;
+            double total = 0;
+            int max_t = 1;
+            for (int qb = 0; qb < nqb; ++qb) {
+                const int n = (std::min(x.q1, x.q0 + (qb + 1) * kBwdBQ) + 63) / 64;
+                total += n;
+                max_t = std::max(max_t, n);
+            }
+            p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, 512);
+            p.max_chunks = (max_t + p.chunk_tiles - 1) / p.chunk_tiles;
+            p.nblocks = nqb;
+            dim3 gq(p.max_chunks, nqb, bh);
             TraceScope ts(st, "attn_bwd_dq_bf16", 6.0 * x.d * pairs, q_bytes);
             if (x.d == 128) {
                 hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds_q);
                 hipLaunchKernelGGL(attn_bwd_dq_mfma32<128>, gq, dim3(256), lds_q, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<128>, dim3(nqb, bh), dim3(256), 0, st, p);
             } else {
                 hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds_q);
                 hipLaunchKernelGGL(attn_bwd_dq_mfma32<64>, gq, dim3(256), lds_q, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<64>, dim3(nqb, bh), dim3(256), 0, st, p);
             }
         }
     } else {

@@ -93,7 +93,7 @@ struct AttnArgs {
     float *dk_acc, *dv_acc;  // [b, nt, s, d] fp32 accumulators
     int k_final0;         // keys in [k_final0, q1) are complete after this call
     bool acc_in;          // accumulators hold earlier calls' contributions
-    float *work;          // forward: split-KV partials (attn_fwd_work_floats floats)
+    float *work;          // partial sums of split work (attn_fwd_work_floats floats; fwd and bwd)
 };
 size_t attn_fwd_work_floats(int batch, int nt, int seq, int d);
 hipError_t attn_fwd(DType dt, const AttnArgs &a, hipStream_t st);
