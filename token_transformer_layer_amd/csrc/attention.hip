@@ -36,9 +36,22 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Work items of a split launch: a 1-D grid of 8 * ceil(n_items / 8)
+// workgroups whose linear ids are dealt round-robin to the 8 XCDs; the items
+// of one XCD are made consecutive (id % 8 picks a range of n_items / 8 items)
+// so that the items of one (batch row, head), which share its K/V or Q/dO
+// tiles, stay in one XCD's L2.  Returns -1 for a padding workgroup.
+__device__ __forceinline__ int xcd_item(int n_items) {
+    const int id = blockIdx.x, per_xcd = gridDim.x >> 3;
+    const int item = (id & 7) * per_xcd + (id >> 3);
+    return item < n_items ? item : -1;
+}
+static inline unsigned xcd_grid(long n_items) { return (unsigned)(8 * ((n_items + 7) / 8)); }
+
 struct AttnP {
     int batch, nt, seq, q0, q1, k_final0, acc_in;
     int chunk_tiles, max_chunks, nblocks;  // work split of the backward (tiles per chunk)
+    int n_items, items_bh;                  // work items in all and per (batch row, head)
     float *part;                            // partial sums of split blocks
     float scale;
     const bf16 *q, *k, *v, *o, *dout;
@@ -239,6 +252,7 @@ constexpr int kFwdMaxChunks = 8;
 
 struct AttnFwdP {
     int batch, nt, seq, q0, q1, nqt, chunk_tiles, max_chunks;
+    int n_items, items_bh;  // work items in all and per (batch row, head)
     float sl2;  // scale * log2(e)
     const bf16 *q, *k, *v;
     bf16 *o;
@@ -251,9 +265,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16-byte chunk swizzle of a [rows][D] bf16 LDS tile: chunk c of row r sits
+// at chunk c ^ kv_swz<D>(r) of that row.  The two read patterns of the
+// kernels are then free of bank conflicts (64 banks of 4 bytes): one chunk of
+// 16 consecutive rows over 16 lanes (ds_read_b128), and four chunks of 4
+// consecutive rows over 32 lanes (ds_read_b64_tr_b16).  For D = 128 a row
+// spans all banks, so rows r..r+3 go to different 64-byte quarters (bits
+// 2-3 from r%4) and the 16 rows of a b128 read to different chunks; for
+// D = 64 two rows share the banks and the pattern is the solution of the same
+// two conditions.
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+
 template <int D>
 __device__ __forceinline__ int kv_chunk_off(int row, int c) {
-    return row * (D * 2) + ((c ^ (row & (D / 8 - 1))) << 4);
+    return row * (D * 2) + ((c ^ kv_swz<D>(row)) << 4);
 }
 
 // one 64-key tile of K or V (rows [key0, key0+64), rows >= kend zero) into LDS
@@ -266,7 +296,7 @@ __device__ __forceinline__ void kv_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst,
         const int I = wave * PER_WAVE + q;
         const int byte = I * 1024 + lane * 16;
         const int row = byte / (D * 2);
-        const int c = ((byte % (D * 2)) >> 4) ^ (row & (D / 8 - 1));
+        const int c = ((byte % (D * 2)) >> 4) ^ kv_swz<D>(row);
         const int key = key0 + row;
         const uint32_t off = key < kend ? (uint32_t)((slab + (int64_t)key * D + c * 8) * 2) : kOOB;
         lds_dma16(r, dst + I * 1024, off);
@@ -274,12 +304,22 @@ __device__ __forceinline__ void kv_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst,
 }
 
 // One 64-key tile of the online softmax of the forward: scores of the tile's
-// keys (LDS [64][D] at ks, positions key0 .. key0+63, only positions <= q_pos
-// and < kmax count) for this lane's query (Q in qreg as the B operand), the
-// running maximum and sum updated and O^T += V^T P^T accumulated (V at vs).
-template <int D>
+// keys (LDS [64][D] at ks, positions key0 .. key0+63) for this lane's query
+// (Q in qreg as the B operand), the running sum updated and O^T += V^T P^T
+// accumulated (V at vs).  MASK: some key of the tile is after a query of the
+// wave (position > q_pos) or at or past kmax, and those scores are dropped;
+// other tiles skip the test.
+//
+// The exponentials are taken against a reference maximum m_ref per query
+// (scaled, log2 units) that is raised only when a score exceeds it by more
+// than 2^8: weights stay below 256, which bf16 P and the fp32 sums hold
+// without loss, and the rescaling of O and the sum (alpha = 2^(m_old - m_new))
+// runs only on the tiles where some query of the wave needs it.  The result
+// O / l and the log-sum-exp m_ref + log2(l) do not depend on which reference
+// was used.
+template <int D, bool MASK>
 __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const bf16x8 (&qreg)[D / 16],
-                                         f32x16 (&acc)[D / 32], float &m_run, float &l_run, int key0, int q_pos,
+                                         f32x16 (&acc)[D / 32], float &m_ref, float &l_run, int key0, int q_pos,
                                          int kmax, float sl2, int lane) {
     constexpr int KS = D / 16, DB = D / 32;
     const int g = lane >> 5, li = lane & 31;
@@ -292,36 +332,39 @@ __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const b
         for (int st = 0; st < KS; ++st)
             sc[kb] = mfma32(*(const bf16x8 *)(ks + kv_chunk_off<D>(row, 2 * st + g)), qreg[st], sc[kb]);
     }
-    // sc[kb][v]: score of key key0 + 32 kb + 8(v/4) + 4g + v%4 for the lane's query
+    // sc[kb][v]: raw score of key key0 + 32 kb + 8(v/4) + 4g + v%4 for the lane's query
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
-            const float x = (key <= q_pos && key < kmax) ? sc[kb][v] * sl2 : -INFINITY;
-            sc[kb][v] = x;
-            mt = fmaxf(mt, x);
+            if constexpr (MASK) {
+                const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
+                if (!(key <= q_pos && key < kmax)) sc[kb][v] = -INFINITY;
+            }
+            mt = fmaxf(mt, sc[kb][v]);
         }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    // a query may see no key yet when its key range is split (m = -inf):
-    // then every weight is 0 and nothing is rescaled
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;  // sl2 > 0: the scaled maximum
+    if (__builtin_amdgcn_ballot_w64(mt > m_ref + 8.f)) {  // wave-uniform
+        const float m_new = fmaxf(m_ref, mt);
+        // a query that has seen no key yet keeps m = -inf (weights 0, nothing to rescale)
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+    }
+    const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const float p = __builtin_amdgcn_exp2f(sc[kb][v] - m_use);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][v], sl2, nm));
             sc[kb][v] = p;
             ls += p;
         }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+    l_run += ls;
     // P^T for key step ks (16 keys): registers 8h..8h+7 of block ks/2, h = ks%2
     bf16x8 pb[4];
 #pragma unroll
@@ -347,6 +390,19 @@ __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const b
     }
 }
 
+// One tile step with the mask test only where the tile needs it (a wave-
+// uniform choice): keys past the wave's first query position or at or past
+// kmax.
+template <int D>
+__device__ __forceinline__ void fwd_tile_step(const char *ks, const char *vs, const bf16x8 (&qreg)[D / 16],
+                                              f32x16 (&acc)[D / 32], float &m_ref, float &l_run, int key0,
+                                              int q_pos, int wave_first_pos, int kmax, float sl2, int lane) {
+    if (key0 + 63 > wave_first_pos || key0 + 64 > kmax)
+        fwd_tile<D, true>(ks, vs, qreg, acc, m_ref, l_run, key0, q_pos, kmax, sl2, lane);
+    else
+        fwd_tile<D, false>(ks, vs, qreg, acc, m_ref, l_run, key0, q_pos, kmax, sl2, lane);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_mfma32(AttnFwdP a) {
     constexpr int KS = D / 16;  // k-steps of S^T = K Q^T
@@ -355,16 +411,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
-    const int c = blockIdx.x, qi = blockIdx.y, bh = blockIdx.z;
+    // item -> (batch row and head, query tile, key chunk); a head's query
+    // tiles go longest first
+    const int item = xcd_item(a.n_items);
+    if (item < 0) return;  // whole workgroup
+    const int bh = item / a.items_bh;
+    int c = item - bh * a.items_bh, qi = a.nqt - 1;
+    for (; qi > 0; --qi) {
+        const int n = (min(a.q1, a.q0 + (qi + 1) * kFwdBQ) + 63) / 64;
+        const int nc = (n + a.chunk_tiles - 1) / a.chunk_tiles;
+        if (c < nc) break;
+        c -= nc;
+    }
     const int qt0 = a.q0 + qi * kFwdBQ;
     const int kend = min(a.q1, qt0 + kFwdBQ);
     const int ntiles = (kend + 63) / 64;
     const int nch = (ntiles + a.chunk_tiles - 1) / a.chunk_tiles;
-    if (c >= nch) return;  // whole workgroup
+    if (c >= nch) return;  // (not reached: the host counts the items the same way)
     const int t0 = c * a.chunk_tiles, t1 = min(ntiles, t0 + a.chunk_tiles);
     const int bi = bh / a.nt, head = bh % a.nt;
     const int my_q = qt0 + w * 32 + li;
     const int q_eff = min(my_q, a.q1 - 1);  // padding queries act as the last query
+    const int wave_first = min(qt0 + w * 32, a.q1 - 1);
     const int64_t slab = (int64_t)bh * a.seq * D;
 
     __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.kv_bytes);
@@ -400,7 +468,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         const int key0 = t * 64;
         if (key0 > qt0 + w * 32 + 31) continue;  // every key of the tile is after this wave's queries
-        fwd_tile<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_eff, kend, a.sl2, lane);
+        fwd_tile_step<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_eff, wave_first, kend, a.sl2, lane);
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (my_q >= a.q1) return;
@@ -516,7 +584,7 @@ __device__ __forceinline__ void rows_tile_dma(__amdgpu_buffer_rsrc_t r, char *ds
         const int I = wave * PER_WAVE + q;
         const int byte = I * 1024 + lane * 16;
         const int row = byte / (D * 2);
-        const int c = ((byte % (D * 2)) >> 4) ^ (row & (D / 8 - 1));
+        const int c = ((byte % (D * 2)) >> 4) ^ kv_swz<D>(row);
         const int gr = row0 + row;
         const uint32_t off = gr < rend ? (uint32_t)((base + (int64_t)gr * ld + c * 8) * 2) : kOOB;
         lds_dma16(r, dst + I * 1024, off);
@@ -554,7 +622,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
-    const int chunk = blockIdx.x, kb = blockIdx.y, bh = blockIdx.z, bi = bh / a.nt, head = bh % a.nt;
+    // item -> (batch row and head, key block, query chunk); a head's key
+    // blocks go longest first (the first block sees every query)
+    const int item = xcd_item(a.n_items);
+    if (item < 0) return;  // whole workgroup
+    const int bh = item / a.items_bh, bi = bh / a.nt, head = bh % a.nt;
+    int chunk = item - bh * a.items_bh, kb = 0;
+    for (; kb < a.nblocks - 1; ++kb) {
+        const int qs = max(a.q0, kb * kBwdBK);
+        const int nc = max(1, ((qs < a.q1 ? (a.q1 - qs + 63) / 64 : 0) + a.chunk_tiles - 1) / a.chunk_tiles);
+        if (chunk < nc) break;
+        chunk -= nc;
+    }
     const int kb0 = kb * kBwdBK;
     const int kw0 = kb0 + w * 32;
     const int my_k = kw0 + li;
@@ -584,7 +663,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     const int nqt_all = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
     // this workgroup's chunk of the query tiles that see the key block
     const int nch = max(1, (nqt_all + a.chunk_tiles - 1) / a.chunk_tiles);
-    if (chunk >= nch) return;  // whole workgroup
+    if (chunk >= nch) return;  // (not reached: the host counts the items the same way)
     const int t_first = chunk * a.chunk_tiles;
     const int nqt = max(0, min(nqt_all - t_first, a.chunk_tiles));
     const int64_t do_base = (int64_t)bi * ht + head * D;  // dO row p at do_base + p * batch * ht
@@ -712,7 +791,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
-    const int chunk = blockIdx.x, qb = blockIdx.y, bh = blockIdx.z, bi = bh / a.nt, head = bh % a.nt;
+    // item -> (batch row and head, query block, key chunk); a head's query
+    // blocks go longest first
+    const int item = xcd_item(a.n_items);
+    if (item < 0) return;  // whole workgroup
+    const int bh = item / a.items_bh, bi = bh / a.nt, head = bh % a.nt;
+    int chunk = item - bh * a.items_bh, qb = a.nblocks - 1;
+    for (; qb > 0; --qb) {
+        const int n = (min(a.q1, a.q0 + (qb + 1) * kBwdBQ) + 63) / 64;
+        const int nc = max(1, (n + a.chunk_tiles - 1) / a.chunk_tiles);
+        if (chunk < nc) break;
+        chunk -= nc;
+    }
     const int qt0 = a.q0 + qb * kBwdBQ;
     const int my_q = qt0 + w * 32 + li;
     const int q_eff = min(my_q, a.q1 - 1);
@@ -720,7 +810,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int ntiles_all = (kend + 63) / 64;
     // this workgroup's chunk of the key tiles its queries see
     const int nch = max(1, (ntiles_all + a.chunk_tiles - 1) / a.chunk_tiles);
-    if (chunk >= nch) return;  // whole workgroup
+    if (chunk >= nch) return;  // (not reached: the host counts the items the same way)
     const int t0 = chunk * a.chunk_tiles, t1 = min(ntiles_all, t0 + a.chunk_tiles);
     const int ht = a.nt * D;
     const int64_t slab = (int64_t)bh * a.seq * D;
@@ -977,6 +1067,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         kv_tile_dma<D>(rv, smem + TILE, kslab, 0, kend, w, lane);
     }
     const int wave_last_pos = a.q_pos0 + lq0 + w * 32 + 31;
+    const int wave_first_pos = a.q_pos0 + min(lq0 + w * 32, a.nq - 1);
     for (int t = 0; t < ntiles; ++t) {
         wait_vmcnt<0>();
         __syncthreads();
@@ -989,7 +1080,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         const int key0 = a.k_pos0 + t * 64;
         if (key0 > wave_last_pos) continue;  // every key of the tile is after this wave's queries
-        fwd_tile<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_pos, a.k_pos0 + kend, a.sl2, lane);
+        fwd_tile_step<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_pos, wave_first_pos, a.k_pos0 + kend, a.sl2, lane);
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (!qok) return;
@@ -1041,20 +1132,29 @@ static double causal_pairs(const AttnArgs &x) {
     return (q1 * (q1 + 1) - q0 * (q0 + 1)) / 2 * x.batch * x.nt;
 }
 
-// Key-chunk size of the split forward: enough work items to fill the chip
-// (about two per compute unit), at most kFwdMaxChunks chunks per query tile.
+// Key-chunk size of the split forward: the smallest chunk (at least two
+// tiles, at most kFwdMaxChunks chunks per query tile) whose work items all
+// fit in one round of the chip (two 64 KB workgroups on each of the 256
+// compute units); when even unsplit query tiles need more than one round,
+// the tiles are not split.
+constexpr int kFwdSlots = 2 * 256;
 static void fwd_split(const AttnArgs &x, AttnFwdP &p) {
     const int nq = x.q1 - x.q0;
     p.nqt = (nq + kFwdBQ - 1) / kFwdBQ;
     const int max_tiles = (x.q1 + 63) / 64;
-    double total = 0;
-    for (int i = 0; i < p.nqt; ++i) total += (std::min(x.q1, x.q0 + (i + 1) * kFwdBQ) + 63) / 64;
-    total *= (double)x.batch * x.nt;
-    int ch = (int)std::ceil(total / 512.0);
-    ch = std::max(ch, (max_tiles + kFwdMaxChunks - 1) / kFwdMaxChunks);
-    ch = std::max(ch, 2);
-    p.chunk_tiles = std::min(ch, max_tiles);
-    p.max_chunks = (max_tiles + p.chunk_tiles - 1) / p.chunk_tiles;
+    const int bh = x.batch * x.nt;
+    auto items = [&](int ct) {
+        long n = 0;
+        for (int i = 0; i < p.nqt; ++i) n += ((std::min(x.q1, x.q0 + (i + 1) * kFwdBQ) + 63) / 64 + ct - 1) / ct;
+        return n * bh;
+    };
+    int ct = std::min(max_tiles, std::max(2, (max_tiles + kFwdMaxChunks - 1) / kFwdMaxChunks));
+    while (ct < max_tiles && items(ct) > kFwdSlots) ++ct;
+    if (items(ct) > kFwdSlots) ct = max_tiles;
+    p.chunk_tiles = ct;
+    p.max_chunks = (max_tiles + ct - 1) / ct;
+    p.items_bh = (int)(items(ct) / bh);
+    p.n_items = p.items_bh * bh;
 }
 
 constexpr int kBwdMaxChunks = 8;
@@ -1096,7 +1196,7 @@ hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
         p.kv_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
         fwd_split(x, p);
         const int lds = 2 * 2 * 64 * x.d * 2;
-        dim3 grid(p.max_chunks, p.nqt, bh);
+        dim3 grid(xcd_grid(p.n_items));
         if (x.d == 128) {
             hipFuncSetAttribute((const void *)attn_fwd_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             hipLaunchKernelGGL(attn_fwd_mfma32<128>, grid, dim3(256), lds, st, p);
@@ -1165,7 +1265,14 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
             p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, 320);
             p.max_chunks = (max_t + p.chunk_tiles - 1) / p.chunk_tiles;
             p.nblocks = nkb;
-            dim3 gk(p.max_chunks, nkb, bh);
+            p.items_bh = 0;
+            for (int kb = 0; kb < nkb; ++kb) {
+                const int qs = std::max(x.q0, kb * kBwdBK);
+                const int n = qs < x.q1 ? (x.q1 - qs + 63) / 64 : 0;
+                p.items_bh += std::max(1, (n + p.chunk_tiles - 1) / p.chunk_tiles);
+            }
+            p.n_items = p.items_bh * bh;
+            dim3 gk(xcd_grid(p.n_items));
             TraceScope ts(st, "attn_bwd_dkdv_bf16", 8.0 * x.d * pairs, kv_bytes);
             if (x.d == 128) {
                 hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<128>,
@@ -1192,7 +1299,13 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
             p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, 512);
             p.max_chunks = (max_t + p.chunk_tiles - 1) / p.chunk_tiles;
             p.nblocks = nqb;
-            dim3 gq(p.max_chunks, nqb, bh);
+            p.items_bh = 0;
+            for (int qb = 0; qb < nqb; ++qb) {
+                const int n = (std::min(x.q1, x.q0 + (qb + 1) * kBwdBQ) + 63) / 64;
+                p.items_bh += std::max(1, (n + p.chunk_tiles - 1) / p.chunk_tiles);
+            }
+            p.n_items = p.items_bh * bh;
+            dim3 gq(xcd_grid(p.n_items));
             TraceScope ts(st, "attn_bwd_dq_bf16", 6.0 * x.d * pairs, q_bytes);
             if (x.d == 128) {
                 hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,

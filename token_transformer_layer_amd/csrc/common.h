@@ -71,9 +71,12 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 // bf16 halves of a 32-bit word
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// two values rounded to bf16 (nearest, ties to even) in one word: one
+// v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    bf16 a = (bf16)lo, b = (bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // 8 consecutive elements (16 bytes of bf16 or 32 bytes of fp32; the address
