@@ -505,50 +505,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // Merges the partial softmaxes of the key chunks of one query tile:
 // m = max_c m_c, l = sum_c 2^(m_c - m) l_c, O = sum_c 2^(m_c - m) O_c / l.
+// One thread per 8 columns of a query (D/8 threads per query), so a query
+// tile spans kFwdBQ * D / 2048 workgroups (grid.x = query tile * that +
+// part); every chunk's loads are issued before the sums.
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_combine(AttnFwdP a) {
-    const int qi = blockIdx.x, bh = blockIdx.y;
+    constexpr int TPQ = D / 8, QPW = 256 / TPQ, PARTS = kFwdBQ / QPW;
+    const int qi = blockIdx.x / PARTS, part = blockIdx.x % PARTS, bh = blockIdx.y;
     const int qt0 = a.q0 + qi * kFwdBQ;
     const int kend = min(a.q1, qt0 + kFwdBQ);
     const int ntiles = (kend + 63) / 64;
     const int nch = (ntiles + a.chunk_tiles - 1) / a.chunk_tiles;
     if (nch == 1) return;
     const int bi = bh / a.nt, head = bh % a.nt;
-    const int ql = threadIdx.x >> 1, half = threadIdx.x & 1;  // 2 threads per query, D/2 columns each
+    const int ql = part * QPW + threadIdx.x / TPQ, j = (threadIdx.x % TPQ) * 8;
     const int q = qt0 + ql;
     if (q >= a.q1) return;
     const int64_t item0 = ((int64_t)bh * a.nqt + qi) * a.max_chunks;
     const float *pml = a.part + (int64_t)a.batch * a.nt * a.nqt * a.max_chunks * kFwdBQ * D;
+    float mc[kFwdMaxChunks], lc[kFwdMaxChunks], x[kFwdMaxChunks][8];
+#pragma unroll
+    for (int cc = 0; cc < kFwdMaxChunks; ++cc) {
+        if (cc < nch) {
+            const float *e = pml + ((item0 + cc) * kFwdBQ + ql) * 2;
+            mc[cc] = e[0];
+            lc[cc] = e[1];
+            load8(a.part + ((item0 + cc) * kFwdBQ + ql) * D + j, x[cc]);
+        }
+    }
     float m = -INFINITY;
-    for (int cc = 0; cc < nch; ++cc) m = fmaxf(m, pml[((item0 + cc) * kFwdBQ + ql) * 2]);
-    float l = 0.f;
-    float o[D / 2];
 #pragma unroll
-    for (int j = 0; j < D / 2; ++j) o[j] = 0.f;
-    for (int cc = 0; cc < nch; ++cc) {
-        const float *e = pml + ((item0 + cc) * kFwdBQ + ql) * 2;
-        const float wgt = e[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(e[0] - m);
-        l += wgt * e[1];
-        const float *po = a.part + ((item0 + cc) * kFwdBQ + ql) * D + half * (D / 2);
+    for (int cc = 0; cc < kFwdMaxChunks; ++cc)
+        if (cc < nch) m = fmaxf(m, mc[cc]);
+    float l = 0.f, o[8] = {};
 #pragma unroll
-        for (int j = 0; j < D / 2; j += 4) {
-            const f32x4 x = *(const f32x4 *)(po + j);
-            o[j] += wgt * x[0];
-            o[j + 1] += wgt * x[1];
-            o[j + 2] += wgt * x[2];
-            o[j + 3] += wgt * x[3];
+    for (int cc = 0; cc < kFwdMaxChunks; ++cc) {
+        if (cc < nch) {
+            const float wgt = mc[cc] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc[cc] - m);
+            l += wgt * lc[cc];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] += wgt * x[cc][u];
         }
     }
     const float inv = 1.0f / l;
-    bf16 *orow = a.o + ((int64_t)q * a.batch + bi) * (a.nt * D) + head * D + half * (D / 2);
 #pragma unroll
-    for (int j = 0; j < D / 2; j += 8) {
-        float v8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v8[i] = o[j + i] * inv;
-        store8(orow + j, v8);
-    }
-    if (half == 0) a.lse[(int64_t)bh * a.seq + q] = (m + __log2f(l)) * kLn2;
+    for (int u = 0; u < 8; ++u) o[u] *= inv;
+    store8(a.o + ((int64_t)q * a.batch + bi) * (a.nt * D) + head * D + j, o);
+    if (j == 0) a.lse[(int64_t)bh * a.seq + q] = (m + __log2f(l)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -570,6 +573,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(AttnFwdP a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kBwdBK = 128;  // keys per dK/dV workgroup
+constexpr int kBwdMaxChunks = 8;  // chunks a split block may have
 constexpr int kBwdBQ = 128;  // queries per dQ workgroup
 
 // one 64-row tile of a [rows][D] bf16 matrix whose rows are `ld` elements
@@ -905,78 +909,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 // Split backward blocks: the partial sums of a block's chunks are added in
 // chunk order, then finished as the unsplit kernels finish them (dK scaled;
-// fp32 accumulators or final bf16 rows).  One workgroup per block, 8
-// consecutive columns per thread.
+// fp32 accumulators or final bf16 rows).  One thread per 8 columns of a row
+// (grid.x = block * rows-per-block * D / 2048 + part), every chunk's loads
+// issued before the sums.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_combine(AttnP a) {
-    const int kb = blockIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    constexpr int TPR = D / 8, RPW = 256 / TPR, PARTS = kBwdBK / RPW;
+    const int kb = blockIdx.x / PARTS, part = blockIdx.x % PARTS;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
     const int kb0 = kb * kBwdBK;
     const int qstart = max(a.q0, kb0);
     const int nqt_all = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
     const int nch = max(1, (nqt_all + a.chunk_tiles - 1) / a.chunk_tiles);
     if (nch == 1) return;
+    const int kl = part * RPW + threadIdx.x / TPR, j = (threadIdx.x % TPR) * 8;
+    const int key = kb0 + kl;
+    if (key >= a.q1) return;
     const int ht = a.nt * D;
     const int64_t slab = (int64_t)bh * a.seq * D;
-    const float *base = a.part + ((int64_t)bh * a.nblocks + kb) * a.max_chunks * (2 * kBwdBK * D);
-    for (int i = threadIdx.x; i < kBwdBK * D / 8; i += 256) {
-        const int kl = i / (D / 8), j = (i % (D / 8)) * 8;
-        const int key = kb0 + kl;
-        if (key >= a.q1) continue;
-        float dk[8] = {}, dv[8] = {};
-        for (int c = 0; c < nch; ++c) {
-            float x[8], y[8];
-            const float *pk = base + (int64_t)c * (2 * kBwdBK * D) + kl * D + j;
-            load8(pk, x);
-            load8(pk + kBwdBK * D, y);
+    const float *base = a.part + ((int64_t)bh * a.nblocks + kb) * a.max_chunks * (2 * kBwdBK * D) + kl * D + j;
+    float x[kBwdMaxChunks][8], y[kBwdMaxChunks][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) { dk[u] += x[u]; dv[u] += y[u]; }
+    for (int c = 0; c < kBwdMaxChunks; ++c) {
+        if (c < nch) {
+            load8(base + (int64_t)c * (2 * kBwdBK * D), x[c]);
+            load8(base + (int64_t)c * (2 * kBwdBK * D) + kBwdBK * D, y[c]);
         }
-        const int64_t arow = slab + (int64_t)key * D + j;
+    }
+    float dk[8] = {}, dv[8] = {};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dk[u] *= a.scale;
-        if (a.acc_in) {
-            float x[8], y[8];
-            load8(a.dk_acc + arow, x);
-            load8(a.dv_acc + arow, y);
+    for (int c = 0; c < kBwdMaxChunks; ++c) {
+        if (c < nch) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) { dk[u] += x[u]; dv[u] += y[u]; }
+            for (int u = 0; u < 8; ++u) { dk[u] += x[c][u]; dv[u] += y[c][u]; }
         }
-        if (key >= a.k_final0) {
-            bf16 *dst = a.out + ((int64_t)key * a.batch + bi) * (3 * ht) + head * D + j;
-            store8(dst + ht, dk);
-            store8(dst + 2 * ht, dv);
-        } else {
-            store8(a.dk_acc + arow, dk);
-            store8(a.dv_acc + arow, dv);
-        }
+    }
+    const int64_t arow = slab + (int64_t)key * D + j;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dk[u] *= a.scale;
+    if (a.acc_in) {
+        float xa[8], ya[8];
+        load8(a.dk_acc + arow, xa);
+        load8(a.dv_acc + arow, ya);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { dk[u] += xa[u]; dv[u] += ya[u]; }
+    }
+    if (key >= a.k_final0) {
+        bf16 *dst = a.out + ((int64_t)key * a.batch + bi) * (3 * ht) + head * D + j;
+        store8(dst + ht, dk);
+        store8(dst + 2 * ht, dv);
+    } else {
+        store8(a.dk_acc + arow, dk);
+        store8(a.dv_acc + arow, dv);
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_combine(AttnP a) {
-    const int qb = blockIdx.x, bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
+    constexpr int TPR = D / 8, RPW = 256 / TPR, PARTS = kBwdBQ / RPW;
+    const int qb = blockIdx.x / PARTS, part = blockIdx.x % PARTS;
+    const int bh = blockIdx.y, bi = bh / a.nt, head = bh % a.nt;
     const int qt0 = a.q0 + qb * kBwdBQ;
     const int kend = min(a.q1, qt0 + kBwdBQ);
     const int ntiles_all = (kend + 63) / 64;
     const int nch = max(1, (ntiles_all + a.chunk_tiles - 1) / a.chunk_tiles);
     if (nch == 1) return;
+    const int ql = part * RPW + threadIdx.x / TPR, j = (threadIdx.x % TPR) * 8;
+    const int q = qt0 + ql;
+    if (q >= a.q1) return;
     const int ht = a.nt * D;
-    const float *base = a.part + ((int64_t)bh * a.nblocks + qb) * a.max_chunks * (kBwdBQ * D);
-    for (int i = threadIdx.x; i < kBwdBQ * D / 8; i += 256) {
-        const int ql = i / (D / 8), j = (i % (D / 8)) * 8;
-        const int q = qt0 + ql;
-        if (q >= a.q1) continue;
-        float dq[8] = {};
-        for (int c = 0; c < nch; ++c) {
-            float x[8];
-            load8(base + (int64_t)c * (kBwdBQ * D) + ql * D + j, x);
+    const float *base = a.part + ((int64_t)bh * a.nblocks + qb) * a.max_chunks * (kBwdBQ * D) + ql * D + j;
+    float x[kBwdMaxChunks][8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) dq[u] += x[u];
+    for (int c = 0; c < kBwdMaxChunks; ++c)
+        if (c < nch) load8(base + (int64_t)c * (kBwdBQ * D), x[c]);
+    float dq[8] = {};
+#pragma unroll
+    for (int c = 0; c < kBwdMaxChunks; ++c) {
+        if (c < nch) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dq[u] += x[c][u];
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) dq[u] *= a.scale;
-        store8(a.out + ((int64_t)q * a.batch + bi) * (3 * ht) + head * D + j, dq);
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dq[u] *= a.scale;
+    store8(a.out + ((int64_t)q * a.batch + bi) * (3 * ht) + head * D + j, dq);
 }
 
 // delta[bh][p] = sum_j dO[p][j] O[p][j]: D/8 lanes per (query, head), 8
@@ -1157,8 +1174,6 @@ static void fwd_split(const AttnArgs &x, AttnFwdP &p) {
     p.n_items = p.items_bh * bh;
 }
 
-constexpr int kBwdMaxChunks = 8;
-
 size_t attn_fwd_work_floats(int batch, int nt, int seq, int d) {
     const int nqt = (seq + kFwdBQ - 1) / kFwdBQ;
     const size_t fwd = (size_t)batch * nt * nqt * kFwdMaxChunks * kFwdBQ * (d + 2);
@@ -1205,8 +1220,9 @@ hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
             hipLaunchKernelGGL(attn_fwd_mfma32<64>, grid, dim3(256), lds, st, p);
         }
         if (p.max_chunks > 1) {
-            if (x.d == 128) hipLaunchKernelGGL(attn_fwd_combine<128>, dim3(p.nqt, bh), dim3(256), 0, st, p);
-            else hipLaunchKernelGGL(attn_fwd_combine<64>, dim3(p.nqt, bh), dim3(256), 0, st, p);
+            const unsigned parts = (unsigned)(kFwdBQ * x.d / 2048);
+            if (x.d == 128) hipLaunchKernelGGL(attn_fwd_combine<128>, dim3(p.nqt * parts, bh), dim3(256), 0, st, p);
+            else hipLaunchKernelGGL(attn_fwd_combine<64>, dim3(p.nqt * parts, bh), dim3(256), 0, st, p);
         }
     } else {
         AttnF p{};
@@ -1278,12 +1294,12 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
                 hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<128>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
                 hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<128>, gk, dim3(256), lds_kv, st, p);
-                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<128>, dim3(nkb, bh), dim3(256), 0, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<128>, dim3(nkb * (kBwdBK * x.d / 2048), bh), dim3(256), 0, st, p);
             } else {
                 hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<64>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
                 hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<64>, gk, dim3(256), lds_kv, st, p);
-                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<64>, dim3(nkb, bh), dim3(256), 0, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<64>, dim3(nkb * (kBwdBK * x.d / 2048), bh), dim3(256), 0, st, p);
             }
         }
         {
@@ -1311,12 +1327,12 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
                 hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds_q);
                 hipLaunchKernelGGL(attn_bwd_dq_mfma32<128>, gq, dim3(256), lds_q, st, p);
-                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<128>, dim3(nqb, bh), dim3(256), 0, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<128>, dim3(nqb * (kBwdBQ * x.d / 2048), bh), dim3(256), 0, st, p);
             } else {
                 hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     lds_q);
                 hipLaunchKernelGGL(attn_bwd_dq_mfma32<64>, gq, dim3(256), lds_q, st, p);
-                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<64>, dim3(nqb, bh), dim3(256), 0, st, p);
+                if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<64>, dim3(nqb * (kBwdBQ * x.d / 2048), bh), dim3(256), 0, st, p);
             }
         }
     } else {
