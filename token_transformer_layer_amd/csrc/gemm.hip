@@ -796,7 +796,9 @@ static int pick_splits(int M, int N, int K, Tile t, int64_t ws_floats) {
     // to about 512 (two per compute unit)
     const int target = t == Tile::Pp128x192 && tiles < 192 ? 512 : 384;
     int sp = (int)((target + tiles - 1) / tiles);
-    sp = std::min(sp, 8);
+    // at most 8 splits, 16 when even 8 leave most compute units idle (a
+    // slice's narrow products: 12 tiles, 1.2 -> 1.5 TB/s of weights)
+    sp = std::min(sp, tiles * 8 < 128 ? 16 : 8);
     sp = std::min(sp, K / 512);
     while (sp > 1 && (int64_t)sp * M * N > ws_floats) --sp;
     return std::max(sp, 1);
