@@ -214,8 +214,7 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32(AttnF a) {
         }
         __syncthreads();
     }
-    dk0 *= a.scale;
-    dk1 *= a.scale;
+    // the accumulators hold dK unscaled; final keys are scaled on output
     const int64_t arow = slab + (int64_t)key * d;
     if (a.acc_in) {
         if (lane < d) { dk0 += a.dk_acc[arow + lane]; dv0 += a.dv_acc[arow + lane]; }
@@ -223,8 +222,8 @@ __global__ __launch_bounds__(64) void attn_bwd_dkdv_f32(AttnF a) {
     }
     if (key >= a.k_final0) {
         float *dst = a.out + ((int64_t)key * a.batch + bi) * (3 * ht) + head * d;
-        if (lane < d) { dst[ht + lane] = dk0; dst[2 * ht + lane] = dv0; }
-        if (lane + 64 < d) { dst[ht + lane + 64] = dk1; dst[2 * ht + lane + 64] = dv1; }
+        if (lane < d) { dst[ht + lane] = dk0 * a.scale; dst[2 * ht + lane] = dv0; }
+        if (lane + 64 < d) { dst[ht + lane + 64] = dk1 * a.scale; dst[2 * ht + lane + 64] = dv1; }
     } else {
         if (lane < d) { a.dk_acc[arow + lane] = dk0; a.dv_acc[arow + lane] = dv0; }
         if (lane + 64 < d) { a.dk_acc[arow + lane + 64] = dk1; a.dv_acc[arow + lane + 64] = dv1; }
@@ -574,6 +573,10 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(AttnFwdP a) {
 
 constexpr int kBwdBK = 128;  // keys per dK/dV workgroup
 constexpr int kBwdMaxChunks = 8;  // chunks a split block may have
+constexpr int kBwdKvStages = 3;   // LDS stages of the dK/dV kernel
+// vector-memory loads one wave issues per query tile of the dK/dV kernel
+// (the Q and dO DMAs, 1 KB per instruction over 4 waves)
+template <int D> constexpr int kBwdTileLoads = 2 * (64 * D * 2 / 1024) / 4;
 constexpr int kBwdBQ = 128;  // queries per dQ workgroup
 
 // one 64-row tile of a [rows][D] bf16 matrix whose rows are `ld` elements
@@ -623,6 +626,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int TILE = 64 * D * 2;
     constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, lse * log2(e) and delta (64 floats each), 1 KB aligned
+    constexpr int NST = kBwdKvStages;        // two query tiles in flight during a tile's work
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
@@ -659,15 +663,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
         kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
         vreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
     }
-    f32x16 acc_dk[DB], acc_dv[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x16{}; acc_dv[i] = f32x16{}; }
-
     const int qstart = max(a.q0, kb0);
     const int nqt_all = qstart < a.q1 ? (a.q1 - qstart + 63) / 64 : 0;
     // this workgroup's chunk of the query tiles that see the key block
     const int nch = max(1, (nqt_all + a.chunk_tiles - 1) / a.chunk_tiles);
     if (chunk >= nch) return;  // (not reached: the host counts the items the same way)
+    // acc[db] register v: d = db*32 + 8(v/4) + 4g + v%4 of key my_k.  An
+    // unsplit block starts from the earlier calls' contributions (the
+    // accumulators hold dK unscaled), loaded with the K/V fragments; split
+    // blocks add them in the combine.
+    const int64_t arow = slab + (int64_t)my_k * D;
+    f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x16{}; acc_dv[i] = f32x16{}; }
+    if (a.acc_in && nch == 1 && my_k < a.q1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = db * 32 + 8 * r + 4 * g;
+                const f32x4 pk = *(const f32x4 *)(a.dk_acc + arow + j);
+                const f32x4 pv = *(const f32x4 *)(a.dv_acc + arow + j);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc_dk[db][4 * r + u] = pk[u];
+                    acc_dv[db][4 * r + u] = pv[u];
+                }
+            }
+    }
     const int t_first = chunk * a.chunk_tiles;
     const int nqt = max(0, min(nqt_all - t_first, a.chunk_tiles));
     const int64_t do_base = (int64_t)bi * ht + head * D;  // dO row p at do_base + p * batch * ht
@@ -690,18 +713,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     auto store_stat = [&](char *st) {
         if (tid < 128) ((float *)(st + 2 * TILE))[tid] = stat;
     };
-    if (nqt > 0) {
-        issue(0, smem);
-        load_stat(0);
-        store_stat(smem);
+    // tile t sits in stage t % NST; tiles t + 1 and t + 2 are in flight while
+    // tile t is worked on (each tile's statistics load precedes its DMA, so
+    // waiting for the statistics leaves the DMA outstanding)
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) {
+        if (t < nqt) {
+            load_stat(t);
+            issue(t, smem + t * STAGE);
+            store_stat(smem + t * STAGE);
+        }
     }
     for (int t = 0; t < nqt; ++t) {
-        wait_vmcnt<0>();
+        // tile t has landed once at most tile t+1's loads are outstanding;
+        // the barrier then also frees the stage of tile t-1
+        if (t + 1 < nqt) wait_vmcnt<kBwdTileLoads<D>>();
+        else wait_vmcnt<0>();
         __syncthreads();
-        const char *st = smem + (t & 1) * STAGE;
-        if (t + 1 < nqt) {
-            issue(t + 1, smem + ((t + 1) & 1) * STAGE);
-            load_stat(t + 1);
+        const char *st = smem + (t % NST) * STAGE;
+        char *nx = smem + ((t + NST - 1) % NST) * STAGE;
+        if (t + NST - 1 < nqt) {
+            load_stat(t + NST - 1);
+            issue(t + NST - 1, nx);
         }
         const int p0 = qstart + (t_first + t) * 64;
         const float *lse_s = (const float *)(st + 2 * TILE);
@@ -742,7 +775,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
                 }
             }
         }
-        if (t + 1 < nqt) store_stat(smem + ((t + 1) & 1) * STAGE);
+        if (t + NST - 1 < nqt) store_stat(nx);
     }
     if (my_k >= a.q1) return;
     if (nch > 1) {
@@ -762,8 +795,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
             }
         return;
     }
-    // acc[db] register v: d = db*32 + 8(v/4) + 4g + v%4 of key my_k
-    const int64_t arow = slab + (int64_t)my_k * D;
+    // final keys: dK = scale * acc in bf16; others: the accumulators (dK unscaled)
     const bool final_key = my_k >= a.k_final0;
     bf16 *dst = a.out + ((int64_t)my_k * a.batch + bi) * (3 * ht) + head * D;
 #pragma unroll
@@ -773,12 +805,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
             const int j = db * 32 + 8 * r + 4 * g;
             f32x4 dk{acc_dk[db][4 * r], acc_dk[db][4 * r + 1], acc_dk[db][4 * r + 2], acc_dk[db][4 * r + 3]};
             f32x4 dv{acc_dv[db][4 * r], acc_dv[db][4 * r + 1], acc_dv[db][4 * r + 2], acc_dv[db][4 * r + 3]};
-            dk *= a.scale;
-            if (a.acc_in) {
-                dk += *(const f32x4 *)(a.dk_acc + arow + j);
-                dv += *(const f32x4 *)(a.dv_acc + arow + j);
-            }
             if (final_key) {
+                dk *= a.scale;
                 *(u32x2 *)(dst + ht + j) = u32x2{pack_bf2(dk[0], dk[1]), pack_bf2(dk[2], dk[3])};
                 *(u32x2 *)(dst + 2 * ht + j) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
             } else {
@@ -908,8 +936,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 // Split backward blocks: the partial sums of a block's chunks are added in
-// chunk order, then finished as the unsplit kernels finish them (dK scaled;
-// fp32 accumulators or final bf16 rows).  One thread per 8 columns of a row
+// chunk order, then finished as the unsplit kernels finish them (earlier
+// calls' contributions added; final rows in bf16 with dK scaled, others back
+// to the fp32 accumulators, which hold dK unscaled).  One thread per 8 columns of a row
 // (grid.x = block * rows-per-block * D / 2048 + part), every chunk's loads
 // issued before the sums.
 template <int D>
@@ -945,8 +974,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_combine(AttnP a) {
         }
     }
     const int64_t arow = slab + (int64_t)key * D + j;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) dk[u] *= a.scale;
     if (a.acc_in) {
         float xa[8], ya[8];
         load8(a.dk_acc + arow, xa);
@@ -954,8 +981,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_combine(AttnP a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) { dk[u] += xa[u]; dv[u] += ya[u]; }
     }
+    // the accumulators hold dK unscaled; final keys are scaled on output
     if (key >= a.k_final0) {
         bf16 *dst = a.out + ((int64_t)key * a.batch + bi) * (3 * ht) + head * D + j;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dk[u] *= a.scale;
         store8(dst + ht, dk);
         store8(dst + 2 * ht, dv);
     } else {
@@ -1266,7 +1296,7 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
         p.kv_bytes = p.q_bytes = (uint32_t)((int64_t)bh * x.seq * x.d * 2);
         p.part = x.work;
         const int tile = 64 * x.d * 2;
-        const int lds_kv = 2 * (2 * tile + 1024), lds_q = 2 * 2 * tile;
+        const int lds_kv = kBwdKvStages * (2 * tile + 1024), lds_q = 2 * 2 * tile;
         {
             // dK, dV: key block kb sees the query tiles from max(q0, 128 kb)
             const int nkb = (x.q1 + kBwdBK - 1) / kBwdBK;
