@@ -403,11 +403,12 @@ void tp_trace_enable(int32_t on);
 int32_t tp_trace_read(tp_trace_record *out, int32_t max);
 
 /* Tile configuration of the bf16 matrix products, for tests and tuning.
- * -1 (the default) lets the library choose per product shape; 0..5 force
+ * -1 (the default) lets the library choose per product shape; 0..6 force
  * one configuration for every later bf16 product of the process: 0 = 128x128
  * tiles, 1 = 128x128 tiles with software-pipelined fragment reads, 2 =
  * 256x128 tiles (two workgroups per compute unit), 3 = 256x256 tiles, 4 =
- * 256x192 tiles, 5 = 128x192 tiles (two workgroups per compute unit).  All
+ * 256x192 tiles, 5 = 128x192 tiles (two workgroups per compute unit), 6 =
+ * 256x256 tiles of 8 waves.  All
  * give identical results (each output element sums its products in the
  * same K order).  Returns TP_EINVAL for any other value. */
 tp_status tp_gemm_force_tile(int32_t tile);

@@ -75,7 +75,8 @@ def test_split_weight_gradients(shape):
     _check_shard(shape, "perturbed", "per-slice", rank=1, split_wgrad=True)
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5], ids=["t128", "p128", "t256x128", "t256", "t256x192", "t128x192"])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6],
+                         ids=["t128", "p128", "t256x128", "t256", "t256x192", "t128x192", "t256w8"])
 @pytest.mark.parametrize("shape", [RAGGED_D64, RAGGED_D128], ids=lambda s: s.name)
 def test_forced_gemm_tiles(shape, tile):
     """Every tile configuration of the bf16 products, forced on every product

@@ -14,6 +14,10 @@ def test_gemm_symbols_map_to_trace_names():
     assert profiling.trace_name(p) == "gemm_bf16_256x128_tn_store_f32"
     p = "_ZN3tpk19gemm_bf16_pp_kernelINS_5DlCfgILi128ELi128ELi2ELi2ELi2ELi64ELi1EEELb1ELb0ENS_11EpiStoreF32IDF16bEEEEvNS_8GemmArgsET2_i"
     assert profiling.trace_name(p) == "gemm_bf16_p128_nn_store_f32"
+    p = "_ZN3tpk19gemm_bf16_pp_kernelINS_5DlCfgILi256ELi192ELi4ELi2ELi2ELi64ELi1EEELb1ELb1ENS_11EpiBiasGeluIDF16bEEEEvNS_8GemmArgsET2_i"
+    assert profiling.trace_name(p) == "gemm_bf16_256x192w8_nt_bias_gelu"
+    d = "void tpk::gemm_bf16_pp_kernel<tpk::DlCfg<256, 256, 2, 4, 2, 64, 1>, false, false, tpk::EpiStoreF32<__bf16> >(tpk::GemmArgs)"
+    assert profiling.trace_name(d) == "gemm_bf16_256w8_tn_store_f32"
     assert profiling.trace_name("_ZN3tpk12_GLOBAL__N_113ln_bwd_kernelIDF16bEEviiiPKf") == "ln_bwd_kernel<bf16>"
 
 

@@ -144,7 +144,7 @@ def _check(status):
 
 
 def tp_gemm_force_tile(tile):
-    """-1: the library picks the bf16 product tiles per shape; 0..5 force one."""
+    """-1: the library picks the bf16 product tiles per shape; 0..6 force one."""
     _check(lib().tp_gemm_force_tile(int(tile)))
 
 

@@ -198,7 +198,7 @@ __attribute__((visibility("hidden"))) tp_status tp_internal_fail(tp_status s, co
 }
 
 tp_status tp_gemm_force_tile(int32_t tile) {
-    if (tile < -1 || tile > 5) return fail(TP_EINVAL, "tile must be -1 (automatic) or 0..5");
+    if (tile < -1 || tile > 6) return fail(TP_EINVAL, "tile must be -1 (automatic) or 0..6");
     tpk::gemm_force_tile(tile);
     g_err.clear();
     return TP_OK;

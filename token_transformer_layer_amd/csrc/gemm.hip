@@ -678,6 +678,9 @@ using Pp256 = DlCfg<256, 256, 2, 2, 2, 64>;          // 128 KB, one workgroup pe
 using Pp256x192 = DlCfg<256, 192, 2, 2, 2, 64>;      // 112 KB, one workgroup per compute unit
 using Pp128x192 = DlCfg<128, 192, 2, 2, 2, 64, 2>;   // 80 KB, two workgroups per compute unit
 using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups per compute unit
+// eight waves (two per SIMD) on one large tile: the latency hiding of two
+// workgroups per compute unit with the operand reuse of the large tile
+using Pp256w8 = DlCfg<256, 256, 2, 4, 2, 64>;        // 128 KB; waves 2x4 (128x64 each)
 
 // Tile configurations, chosen per product shape from measurements on MI355X
 // (TFLOP/s of each candidate on the GPT-3 175B t=8 shard's products and on
@@ -686,7 +689,7 @@ using Pp256x128 = DlCfg<256, 128, 2, 2, 3, 32, 2>;   // 72 KB, two workgroups pe
 // load path delivers, so larger tiles win wherever there are enough of them
 // to fill the 256 compute units; the plain (non-pipelined) 128x128 kernel
 // is the best fit for short reductions and narrow outputs.
-enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192 };
+enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192, Pp256w8 };
 
 static std::atomic<int> g_force_tile{-1};
 
@@ -694,17 +697,33 @@ constexpr int64_t kSplitMaxFloats = 512LL * 128 * 192;  // 48 MB: about two roun
 
 void gemm_force_tile(int tile) { g_force_tile.store(tile); }
 
+// Fraction of the last round of a launch that its tiles fill, with `slots`
+// workgroups resident on the chip at once.
+static double round_fill(long tiles, long slots) {
+    const long rounds = (tiles + slots - 1) / slots;
+    return rounds > 0 ? (double)tiles / (double)(rounds * slots) : 0.0;
+}
+
 static Tile pick_tile(int M, int N, int K, bool ak, bool bk) {
     const int forced = g_force_tile.load(std::memory_order_relaxed);
     if (forced >= 0) return (Tile)forced;
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128x192 = (long)((M + 127) / 128) * ((N + 191) / 192);
     // Two 128x192 workgroups per compute unit (64-wide K-tiles: whole cache
-    // lines per row) are the best measured fit for every product of the
-    // layer shards; 256x256 tiles win once there are two rounds of them with
-    // a long reduction (large squares); products too small for a round of
-    // 128x192 tiles take 128x128 tiles and split their reduction.
-    if (ak && bk && K >= 6144 && t256 >= 512) return Tile::Pp256;
+    // lines per row) are the best measured fit for the layer shards'
+    // forward and input-gradient products.  An 8-wave 256x256 workgroup
+    // per compute unit (one workgroup of two waves per SIMD) wins where its
+    // tiles fill the last round of 256: the weight gradients (K = tokens;
+    // 3% in the 175B step), large squares and the cube block's products
+    // (8-10% in isolation).  (An 8-wave 256x192 tile measured 10-15% ahead
+    // on the 175B forward products in isolation, with the operands resident
+    // in the MALL, but not in the step, where the weights come from HBM;
+    // it is not used.)  Products too small for a round of 128x192 tiles take
+    // 128x128 tiles and split their reduction.
+    const double f256 = round_fill(t256, 256), f128x192 = round_fill(t128x192, 512);
+    if (ak && bk && K >= 4096 && f256 >= 0.97) return Tile::Pp256w8;
+    if (ak && !bk && K >= 4096 && t128x192 >= 192 && f256 >= f128x192 - 0.02) return Tile::Pp256w8;
+    if (!ak && !bk && K >= 1024 && f256 >= 0.75 && t256 >= 128) return Tile::Pp256w8;
     if (t128x192 >= 192 && K >= 512) return Tile::Pp128x192;
     // narrow outputs of a long reduction over many rows (the attention
     // output projection's input gradient): 128x192 tiles with the reduction
@@ -722,6 +741,7 @@ static const char *tile_name(Tile t) {
     case Tile::Pp256: return "256";
     case Tile::Pp256x192: return "256x192";
     case Tile::Pp128x192: return "128x192";
+    case Tile::Pp256w8: return "256w8";
     }
     return "?";
 }
@@ -733,6 +753,7 @@ static hipError_t launch(const GemmArgs &g, const E &epi, hipStream_t st) {
         case Tile::Pp256: return launch_pp<Pp256, AK, BK_>(g, epi, st);
         case Tile::Pp256x192: return launch_pp<Pp256x192, AK, BK_>(g, epi, st);
         case Tile::Pp128x192: return launch_pp<Pp128x192, AK, BK_>(g, epi, st);
+        case Tile::Pp256w8: return launch_pp<Pp256w8, AK, BK_>(g, epi, st);
         case Tile::Pp256x128: return launch_pp<Pp256x128, AK, BK_>(g, epi, st);
         case Tile::Pp128: return launch_pp<Dl128, AK, BK_>(g, epi, st);
         case Tile::Dl128: break;

@@ -46,7 +46,7 @@ struct EpiArgs {
 
 hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const EpiArgs &e,
                 hipStream_t st);
-// -1: tile configuration chosen per shape; 0..5: forced (see tp_gemm_force_tile)
+// -1: tile configuration chosen per shape; 0..6: forced (see tp_gemm_force_tile)
 void gemm_force_tile(int tile);
 // floats of split-reduction workspace that lets every product split
 size_t gemm_split_workspace_floats();

@@ -58,11 +58,12 @@ def source_hash(trace_name):
     return h.hexdigest()
 
 
-def _tile_tag(pp, bm, bn):
+def _tile_tag(pp, bm, bn, waves=4):
     """The library's name for a tile configuration (see pick_tile in gemm.hip)."""
     if bm == bn == "128":
         return "p128" if pp else "128"
-    return bm if bm == bn else "%sx%s" % (bm, bn)
+    tag = bm if bm == bn else "%sx%s" % (bm, bn)
+    return tag + ("w%d" % waves if waves != 4 else "")
 
 
 def trace_name(symbol):
@@ -71,16 +72,18 @@ def trace_name(symbol):
     s = symbol.strip()
     if "gemm_bf16_dl_kernel" in s or "gemm_bf16_pp_kernel" in s:
         pp = "gemm_bf16_pp_kernel" in s
-        mm = re.search(r"DlCfgILi(\d+)ELi(\d+)E.*?EEELb(\d)ELb(\d)ENS_\d+(\w+?)I", s)
+        mm = re.search(r"DlCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E.*?EEELb(\d)ELb(\d)ENS_\d+(\w+?)I", s)
         if mm:
-            bm, bn, key, epi = mm.group(1), mm.group(2), (mm.group(3), mm.group(4)), mm.group(5)
+            bm, bn, waves = mm.group(1), mm.group(2), int(mm.group(3)) * int(mm.group(4))
+            key, epi = (mm.group(5), mm.group(6)), mm.group(7)
         else:
-            mm = re.search(r"DlCfg<(\d+), (\d+),.*?>, (true|false), (true|false), tpk::(?:\(anonymous namespace\)::)?(\w+)<", s)
-        if mm and not mm.group(3).isdigit():
-            bm, bn, epi = mm.group(1), mm.group(2), mm.group(5)
-            key = ("1" if mm.group(3) == "true" else "0", "1" if mm.group(4) == "true" else "0")
+            mm = re.search(r"DlCfg<(\d+), (\d+), (\d+), (\d+),.*?>, (true|false), (true|false), "
+                           r"tpk::(?:\(anonymous namespace\)::)?(\w+)<", s)
+            if mm:
+                bm, bn, waves, epi = mm.group(1), mm.group(2), int(mm.group(3)) * int(mm.group(4)), mm.group(7)
+                key = ("1" if mm.group(5) == "true" else "0", "1" if mm.group(6) == "true" else "0")
         if mm:
-            return "gemm_bf16_%s_%s_%s" % (_tile_tag(pp, bm, bn), _LAYOUT[key], _EPI.get(epi, epi))
+            return "gemm_bf16_%s_%s_%s" % (_tile_tag(pp, bm, bn, waves), _LAYOUT[key], _EPI.get(epi, epi))
     mm = re.match(r"_ZN3tpk(?:12_GLOBAL__N_1)?(\d+)", s)
     if mm:  # mangled name in the library's namespace: the kernel's own name
         n = int(mm.group(1))
