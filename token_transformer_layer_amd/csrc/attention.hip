@@ -1216,7 +1216,10 @@ size_t attn_fwd_work_floats(int batch, int nt, int seq, int d) {
 
 // Tiles per chunk of a split backward launch: enough work items for the
 // chip (`target`), at most kBwdMaxChunks chunks per block, at least two
-// tiles per chunk.
+// tiles per chunk.  Both backward kernels take about 448 items: on the 175B
+// shard (3264 tile pairs over 12 heads) chunks of 8 tiles, measured best
+// against targets of 256-768 (backward 120 us against 122-144).
+constexpr int kBwdItemTarget = 448;
 static int bwd_chunk_tiles(double total_tiles, int max_tiles, int target) {
     int ct = (int)std::ceil(total_tiles / target);
     ct = std::max(ct, (max_tiles + kBwdMaxChunks - 1) / kBwdMaxChunks);
@@ -1308,7 +1311,7 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
                 total += n;
                 max_t = std::max(max_t, n);
             }
-            p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, 320);
+            p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, kBwdItemTarget);
             p.max_chunks = (max_t + p.chunk_tiles - 1) / p.chunk_tiles;
             p.nblocks = nkb;
             p.items_bh = 0;
@@ -1342,7 +1345,7 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
                 total += n;
                 max_t = std::max(max_t, n);
             }
-            p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, 512);
+            p.chunk_tiles = bwd_chunk_tiles(total * bh, max_t, kBwdItemTarget);
             p.max_chunks = (max_t + p.chunk_tiles - 1) / p.chunk_tiles;
             p.nblocks = nqb;
             p.items_bh = 0;
