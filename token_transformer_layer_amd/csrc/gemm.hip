@@ -643,15 +643,28 @@ static uint32_t extent_bytes(int rows, int k, const Mat &m, int es) {
 // to 5% on the long-K products).
 static int g_group_rows = 8;
 
+// The dynamic-LDS limit of one kernel, raised once per device (a function
+// attribute is per device; the flags are atomic so concurrent first calls
+// only repeat an idempotent call).
+struct AttrOnce {
+    static constexpr int kMaxDev = 64;
+    std::atomic<bool> done[kMaxDev] = {};
+    hipError_t set(const void *fn, int lds) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < kMaxDev && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e == hipSuccess && dev >= 0 && dev < kMaxDev) done[dev].store(true, std::memory_order_release);
+        return e;
+    }
+};
+
 template <class C, bool AK, bool BK_, class E>
 static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_dl_kernel<C, AK, BK_, E>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static AttrOnce once;
+    hipError_t e = once.set((const void *)gemm_bf16_dl_kernel<C, AK, BK_, E>, C::kLds);
+    if (e != hipSuccess) return e;
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
     hipLaunchKernelGGL((gemm_bf16_dl_kernel<C, AK, BK_, E>), dim3(tiles, g.nsplit), dim3(C::kThreads), C::kLds, st, g,
                        epi, g_group_rows);
@@ -660,13 +673,9 @@ static hipError_t launch_dl(const GemmArgs &g, const E &epi, hipStream_t st) {
 
 template <class C, bool AK, bool BK_, class E>
 static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_bf16_pp_kernel<C, AK, BK_, E>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static AttrOnce once;
+    hipError_t e = once.set((const void *)gemm_bf16_pp_kernel<C, AK, BK_, E>, C::kLds);
+    if (e != hipSuccess) return e;
     const int tiles = ((g.M + C::kBM - 1) / C::kBM) * ((g.N + C::kBN - 1) / C::kBN);
     hipLaunchKernelGGL((gemm_bf16_pp_kernel<C, AK, BK_, E>), dim3(tiles, g.nsplit), dim3(C::kThreads), C::kLds, st, g,
                        epi, g_group_rows);
