@@ -156,7 +156,9 @@ typedef struct {
  * [b, n_t, s, d] each).  Backward attention calls run the slices in reverse:
  * a call over [j0, j1) requires done_from == o_{j1} (else TP_EORDER) and sets
  * done_from = o_{j0}.  Start a step with done_from = seq_len; the first call
- * does not read the accumulators, so they need no zeroing. */
+ * does not read the accumulators, so they need no zeroing.  Their contents
+ * are the library's working values (dK is held without the 1/sqrt(d)
+ * factor); the final dK and dV of a slice's keys are written to dqkv. */
 typedef struct {
     float *dk, *dv;
     int32_t done_from;
