@@ -819,13 +819,18 @@ static int pick_splits(int M, int N, int K, Tile t, int64_t ws_floats) {
     if (t != Tile::Dl128 && t != Tile::Pp128 && t != Tile::Pp128x192) return 1;
     const int bn = t == Tile::Pp128x192 ? 192 : 128;
     const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + bn - 1) / bn);
-    if (tiles >= 256) return 1;
-    // about 384 workgroups (1.5 per compute unit): measured better than two
-    // rounds, whose extra partial sums cost more than the fill they add;
-    // 128x192 tiles of a long reduction that fill less than one round split
-    // to about 512 (two per compute unit)
-    const int target = t == Tile::Pp128x192 && tiles < 192 ? 512 : 384;
-    int sp = (int)((target + tiles - 1) / tiles);
+    int sp;
+    if (t == Tile::Pp128x192) {
+        // two workgroups per compute unit: the largest split that keeps the
+        // launch within one round of 512 (tiles filling at most half a round)
+        if (tiles > 256) return 1;
+        sp = (int)(512 / tiles);
+    } else {
+        if (tiles >= 256) return 1;
+        // about 384 workgroups (1.5 per compute unit): measured better than
+        // two rounds, whose extra partial sums cost more than the fill they add
+        sp = (int)((384 + tiles - 1) / tiles);
+    }
     // at most 8 splits, 16 when even 8 leave most compute units idle (a
     // slice's narrow products: 12 tiles, 1.2 -> 1.5 TB/s of weights)
     sp = std::min(sp, tiles * 8 < 128 ? 16 : 8);
