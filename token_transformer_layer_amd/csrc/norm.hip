@@ -295,9 +295,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t n8, int h, co
 }
 
 int ln_bwd_blocks(int rows) { return rows < 256 ? rows : 256; }
+// chunks of 32 rows, at most 256 (long token ranges keep short serial sums)
 int colsum_chunks(int rows) {
     int c = (rows + 31) / 32;
-    return c < 64 ? (c < 1 ? 1 : c) : 64;
+    return c < 256 ? (c < 1 ? 1 : c) : 256;
 }
 
 // Cube-partition FFN elementwise steps, 8 columns per thread: Z = z_sum +
