@@ -22,7 +22,11 @@ gradient in one call over all slices afterwards.
 
 Prints ONE JSON line.  value = algorithmic fwd+bwd TFLOP/s of the step:
 GEMMs 3 x 2 T h (4 h_t + 2 f_t) plus causal attention 3 x 2 b h_t s (s+1)
-flops, over the measured time per step.
+flops, over the measured time per step (K timed steps after W warm-up steps,
+HIP events on the launch stream).  Per-kernel durations (the `kernels` table
+and the roofline of the dominant kernel) come from a second pass of K steps
+with the library's event trace on, whose step time is reported as
+`traced_step_ms` (the events between launches cost the step about 6%).
 """
 import argparse
 import json
@@ -355,7 +359,7 @@ def main():
     total = g_fl + a_fl
 
     step = make_step(layer, bufs, "whole")
-    ms, wall_ms, recs = time_steps(torch, step, args.steps, args.warmup, trace=not args.profile_only)
+    ms, wall_ms, _ = time_steps(torch, step, args.steps, args.warmup, trace=False)
     if args.profile_only:
         if args.copy_mib > 0:
             n = args.copy_mib * (1 << 20) // 4
@@ -367,6 +371,10 @@ def main():
             del src, dst
         print(json.dumps(dict(config=shape.name, ms_per_step=ms)))
         return
+    # per-kernel durations: the same K steps again with the library's event
+    # trace on the launch stream (the events recorded around every launch
+    # add about 6% to a step, so the headline comes from the untraced steps)
+    traced_step_ms, _, recs = time_steps(torch, step, args.steps, 1, trace=True)
     kt = kernel_table(recs, args.steps)
     # the dominant kernel: the largest share of the step's time
     dom_name = next(iter(kt))
@@ -419,6 +427,7 @@ def main():
         "gemm": dict(ms_per_step=round(gemm_ms, 4), tflops=round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
                      frac=round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
         "traced_kernel_ms_per_step": round(traced_ms, 4),
+        "traced_step_ms": round(traced_step_ms, 4),
         "wall_ms_per_step": round(wall_ms, 4),
         "roofline": roofline,
         "kernels": kt,
