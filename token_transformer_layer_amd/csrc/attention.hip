@@ -559,7 +559,8 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(AttnFwdP a) {
 // dK, dV: a workgroup owns 128 keys of one (batch row, head), 32 per wave,
 // held in registers; the query tiles that see them (64 queries each: Q and
 // dO rows, and the tile's log-sum-exp and rowsum(dO * O)) stream through LDS
-// by direct-to-LDS loads, two stages deep.  Per query tile a wave forms
+// by direct-to-LDS loads, three stages deep (two tiles in flight while one
+// is worked on).  Per query tile a wave forms
 // S = Q K^T and dP = dO V^T with keys along the lanes and queries along the
 // registers, which is already the B operand (keys as columns, queries as the
 // reduction) of dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T fragments

@@ -9,12 +9,15 @@
 // M/N-contiguous).
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16.  A workgroup of 4 waves computes a
-// 128x128 (or 256x256) tile, each wave a quarter of it as a grid of 32x32
-// MFMA blocks.  K-tiles of 64 travel from HBM straight into LDS (buffer
-// loads that write LDS, two stages, the next K-tile in flight while the
-// current one feeds the MFMAs); fragments are read from LDS with
-// ds_read_b128 (K-contiguous operands) or ds_read_b64_tr_b16 (M/N-contiguous
-// operands, read transposed).  Tiles are mapped to workgroups XCD-aware.
+// 128x192 tile (two workgroups per compute unit; also 128x128 and, with 4
+// or 8 waves, 256-row tiles), each wave its share as a grid of 32x32 MFMA
+// blocks.  K-tiles of 64 travel from HBM straight into LDS (buffer loads
+// that write LDS, two stages, the next K-tile in flight while the current
+// one feeds the MFMAs); fragments are read from LDS with ds_read_b128
+// (K-contiguous operands) or ds_read_b64_tr_b16 (M/N-contiguous operands,
+// read transposed).  Tiles are mapped to workgroups XCD-aware; products too
+// small to fill the chip split their reduction into fp32 partial sums that a
+// second kernel adds in split order.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (64 x 64 tiles, 4 x 4 per thread).
 #include <cmath>
