@@ -93,7 +93,8 @@ def test_forced_gemm_tiles(shape, tile):
 
 WIDE = [
     # hidden widths that give the LayerNorm kernels 4, 7 and 8 vectors of 8
-    # columns per thread, with and without the next-row prefetch
+    # columns per thread (the bf16 backward at 8192: 512 threads of 2), with
+    # and without the next-row prefetch
     LayerShape("wide-8192-bf16", 8192, 64, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2011),
     LayerShape("wide-14336-bf16", 14336, 112, 128, 1792, 16, 1, 24, (10, 14), "bf16", seed=2012),
     LayerShape("wide-16384-bf16", 16384, 128, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2013),

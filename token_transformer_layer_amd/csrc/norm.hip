@@ -88,122 +88,176 @@ __global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, cons
 // with gg = du * gamma; the block's sums of du * xhat and du over its rows go
 // to partials[block][0][:] and partials[block][1][:].  Each thread owns NV
 // vectors of 8 columns (column vector c = threadIdx.x + i * 256) and keeps
-// its gamma, its parameter-gradient sums and the next row's inputs in
+// its gamma, its parameter-gradient sums and up to two rows' inputs in
 // registers: the loads of row r + 1 are in flight while row r is reduced and
 // written.
+// Every row access goes through a buffer descriptor of that row, so vectors
+// past the row (offset kOOB) and rows past the block's range (a descriptor
+// of length zero) read zeros and drop stores without a branch: the loads are
+// unconditional, and the compiler's wait before a row's arithmetic covers
+// only that row's loads, not the next row's.
 // 8 consecutive elements as loaded: packed bf16, or fp32.
 template <typename T> struct Raw8;
 template <> struct Raw8<bf16> {
     u32x4 w;
-    __device__ __forceinline__ void load(const bf16 *p) { w = *(const u32x4 *)p; }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) { w = buf_load16(r, off); }
     __device__ __forceinline__ float operator[](int j) const { return j & 1 ? bf_hi(w[j >> 1]) : bf_lo(w[j >> 1]); }
 };
 template <> struct Raw8<float> {
-    float v[8];
-    __device__ __forceinline__ void load(const float *p) { load8(p, v); }
-    __device__ __forceinline__ float operator[](int j) const { return v[j]; }
+    u32x4 a, b;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        a = buf_load16(r, off);
+        b = buf_load16(r, off + 16);  // kOOB + 16 is still past every row
+    }
+    __device__ __forceinline__ float operator[](int j) const { return __uint_as_float(j < 4 ? a[j] : b[j - 4]); }
 };
+
+__device__ __forceinline__ void store8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[8], float *) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                                 __float_as_uint(v[3])}, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                                                 __float_as_uint(v[7])}, r, off + 16, 0, 0);
+}
+__device__ __forceinline__ void store8_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[8], bf16 *) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf2(v[2 * i], v[2 * i + 1]);
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+}
 
 template <typename T>
 struct LnRow {
     // one thread's share of a row: du fp32, x and resid as stored
-    float du[8];
+    Raw8<float> du;
     Raw8<T> x, res;
 };
 
-template <typename T, int NV>
-__global__ __launch_bounds__(kThreads) void ln_bwd_kernel(int rows, int h, int rpb, const float *__restrict__ du,
+template <typename T, int NV, int TPB>
+__global__ __launch_bounds__(TPB) void ln_bwd_kernel(int rows, int h, int rpb, const float *__restrict__ du,
                                                           const T *__restrict__ resid, const T *__restrict__ x,
                                                           const T *__restrict__ g, const float *__restrict__ mean,
                                                           const float *__restrict__ rstd, T *__restrict__ dx,
                                                           float *__restrict__ partials) {
-    __shared__ float red[2][2][4];
+    constexpr int NWV = TPB / 64;
+    __shared__ float red[2][2][NWV];
     const int nv = h >> 3;
     const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
+    const uint32_t row_f32 = (uint32_t)h * 4, row_t = (uint32_t)h * sizeof(T);
+    // byte offsets of this thread's vectors in an fp32 row and a T row
+    uint32_t o4[NV], ot[NV];
     float gg[NV][8], adg[NV][8], adb[NV][8];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) adg[i][j] = adb[i][j] = 0.f;
-        if (c < nv) load8(g + c * 8, gg[i]);
-        else
-#pragma unroll
-            for (int j = 0; j < 8; ++j) gg[i][j] = 0.f;
-    }
-    LnRow<T> cur[NV], nxt[NV];
-    auto load_row = [&](int row, LnRow<T> (&d)[NV]) {
+    {
+        const __amdgpu_buffer_rsrc_t pg = make_rsrc(g, row_t);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            if (c < nv) {
-                load8(du + (size_t)row * h + c * 8, d[i].du);
-                d[i].x.load(x + (size_t)row * h + c * 8);
-                d[i].res.load(resid + (size_t)row * h + c * 8);
+            const int c = threadIdx.x + i * TPB;
+            o4[i] = c < nv ? (uint32_t)c * 32 : kOOB;
+            ot[i] = c < nv ? (uint32_t)c * (8 * sizeof(T)) : kOOB;
+            Raw8<T> gr;
+            gr.load(pg, ot[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                gg[i][j] = gr[j];
+                adg[i][j] = adb[i][j] = 0.f;
             }
+        }
+    }
+    // a row's statistics are loaded with its data (before the next row's
+    // loads), so waiting for them does not wait for the next row
+    auto load_row = [&](int row, LnRow<T> (&d)[NV], float &mu, float &rs) __attribute__((always_inline)) {
+        const bool valid = row < r1;
+        const int rr = valid ? row : r0;
+        mu = mean[rr];
+        rs = rstd[rr];
+        const size_t base = (size_t)rr * h;
+        const __amdgpu_buffer_rsrc_t pdu = make_rsrc(du + base, valid ? row_f32 : 0u);
+        const __amdgpu_buffer_rsrc_t px = make_rsrc(x + base, valid ? row_t : 0u);
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(resid + base, valid ? row_t : 0u);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            d[i].du.load(pdu, o4[i]);
+            d[i].x.load(px, ot[i]);
+            d[i].res.load(pr, ot[i]);
         }
     };
-    // the next row is prefetched while the register budget allows (h up to
-    // 14336 in bf16, 10240 in fp32, at one wave per SIMD)
-    constexpr bool kPrefetch = NV * (sizeof(T) == 2 ? 1 : 5) <= (sizeof(T) == 2 ? 7 : 25);
-    if (kPrefetch && r0 < r1) load_row(r0, cur);
-    for (int row = r0; row < r1; ++row) {
-        if constexpr (kPrefetch) {
-            if (row + 1 < r1) load_row(row + 1, nxt);
-        } else {
-            load_row(row, cur);
-        }
-        const float mu = mean[row], rs = rstd[row];
+    auto process = [&](int row, const LnRow<T> (&cur)[NV], float mu, float rs) __attribute__((always_inline)) {
+        // vectors past the row hold zeros: they add nothing to the sums
         float s1 = 0.f, s2 = 0.f;
-        float xh[NV][8];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            if (c < nv) {
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    xh[i][j] = (cur[i].x[j] - mu) * rs;
-                    const float gd = cur[i].du[j] * gg[i][j];
-                    s1 += gd;
-                    s2 += gd * xh[i][j];
-                    adg[i][j] += cur[i].du[j] * xh[i][j];
-                    adb[i][j] += cur[i].du[j];
-                }
+            for (int j = 0; j < 8; ++j) {
+                const float xh = (cur[i].x[j] - mu) * rs;
+                const float gd = cur[i].du[j] * gg[i][j];
+                s1 += gd;
+                s2 += gd * xh;
+                adg[i][j] += cur[i].du[j] * xh;
+                adb[i][j] += cur[i].du[j];
             }
-        }
         // both row sums in one exchange; the two LDS buffers alternate by
         // row, so a buffer is rewritten only after every thread has passed
         // the next row's barrier
         s1 = wave_sum(s1);
         s2 = wave_sum(s2);
-        float(*rb)[4] = red[row & 1];
+        float(*rb)[NWV] = red[row & 1];
         if ((threadIdx.x & 63) == 0) {
             rb[0][threadIdx.x >> 6] = s1;
             rb[1][threadIdx.x >> 6] = s2;
         }
         __syncthreads();
-        const float m1 = (rb[0][0] + rb[0][1] + rb[0][2] + rb[0][3]) / (float)h;
-        const float m2 = (rb[1][0] + rb[1][1] + rb[1][2] + rb[1][3]) / (float)h;
+        float m1 = rb[0][0], m2 = rb[1][0];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) {
+            m1 += rb[0][w];
+            m2 += rb[1][w];
+        }
+        m1 /= (float)h;
+        m2 /= (float)h;
+        const __amdgpu_buffer_rsrc_t pdx = make_rsrc(dx + (size_t)row * h, row_t);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int c = threadIdx.x + i * kThreads;
-            if (c < nv) {
-                float o[8];
+            float o[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    o[j] = cur[i].res[j] + rs * (cur[i].du[j] * gg[i][j] - m1 - xh[i][j] * m2);
-                store8(dx + (size_t)row * h + c * 8, o);
+            for (int j = 0; j < 8; ++j) {
+                const float xh = (cur[i].x[j] - mu) * rs;
+                o[j] = cur[i].res[j] + rs * (cur[i].du[j] * gg[i][j] - m1 - xh * m2);
             }
+            store8_buf(pdx, ot[i], o, (T *)nullptr);
         }
-        if constexpr (kPrefetch) {
-#pragma unroll
-            for (int i = 0; i < NV; ++i) cur[i] = nxt[i];
+    };
+    // two register sets alternate by row while the register budget allows
+    // (6 vectors per thread in bf16, 5 in fp32 at one wave per SIMD; half as
+    // many at two); every load is issued, so the number in flight is the
+    // same on every path through the loop
+    constexpr bool kPrefetch = NV * (TPB / 256) <= (sizeof(T) == 2 ? 6 : 5);
+    if constexpr (kPrefetch) {
+        LnRow<T> ra[NV], rb[NV];
+        float mua, rsa, mub, rsb;
+        load_row(r0, ra, mua, rsa);
+        // the scheduling barriers keep each row's loads ahead of the
+        // previous row's arithmetic (the scheduler would otherwise sink them
+        // to shorten their registers' live ranges)
+        for (int row = r0; row < r1; row += 2) {
+            load_row(row + 1, rb, mub, rsb);
+            __builtin_amdgcn_sched_barrier(0);
+            process(row, ra, mua, rsa);
+            if (row + 1 >= r1) break;
+            load_row(row + 2, ra, mua, rsa);
+            __builtin_amdgcn_sched_barrier(0);
+            process(row + 1, rb, mub, rsb);
+        }
+    } else {
+        LnRow<T> ra[NV];
+        for (int row = r0; row < r1; ++row) {
+            float mu, rs;
+            load_row(row, ra, mu, rs);
+            process(row, ra, mu, rs);
         }
     }
     float *pb = partials + (size_t)blockIdx.x * 2 * h;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int c = threadIdx.x + i * kThreads;
+        const int c = threadIdx.x + i * TPB;
         if (c < nv) {
             store8(pb + c * 8, adg[i]);
             store8(pb + h + c * 8, adb[i]);
@@ -356,11 +410,11 @@ hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, co
     return hipGetLastError();
 }
 
-template <typename T, int NV>
+template <typename T, int NV, int TPB>
 static void launch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du, const void *resid, const void *x,
                           const void *g, const float *mean, const float *rstd, void *dx, float *partials,
                           hipStream_t st) {
-    hipLaunchKernelGGL((ln_bwd_kernel<T, NV>), dim3(nblk), dim3(kThreads), 0, st, rows, h, rpb, du,
+    hipLaunchKernelGGL((ln_bwd_kernel<T, NV, TPB>), dim3(nblk), dim3(TPB), 0, st, rows, h, rpb, du,
                        (const T *)resid, (const T *)x, (const T *)g, mean, rstd, (T *)dx, partials);
 }
 
@@ -368,16 +422,29 @@ template <typename T>
 static void dispatch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du, const void *resid, const void *x,
                             const void *g, const float *mean, const float *rstd, void *dx, float *partials,
                             hipStream_t st) {
-    const int nvt = ((h >> 3) + kThreads - 1) / kThreads;  // vectors per thread, 1..kMaxVec
+    const int nv = h >> 3;
+    // bf16 rows of 6145..12288 columns: 512 threads of 2 or 3 vectors each,
+    // two waves per SIMD with the next row prefetched
+    if constexpr (sizeof(T) == 2) {
+        if (nv > 3 * kThreads && nv <= 2 * 512) {
+            launch_ln_bwd<T, 2, 512>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
+            return;
+        }
+        if (nv > 2 * 512 && nv <= 3 * 512) {
+            launch_ln_bwd<T, 3, 512>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
+            return;
+        }
+    }
+    const int nvt = (nv + kThreads - 1) / kThreads;  // vectors per thread, 1..kMaxVec
     switch (nvt) {
-    case 1: launch_ln_bwd<T, 1>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    case 2: launch_ln_bwd<T, 2>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    case 3: launch_ln_bwd<T, 3>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    case 4: launch_ln_bwd<T, 4>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    case 5: launch_ln_bwd<T, 5>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    case 6: launch_ln_bwd<T, 6>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    case 7: launch_ln_bwd<T, 7>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
-    default: launch_ln_bwd<T, 8>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 1: launch_ln_bwd<T, 1, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 2: launch_ln_bwd<T, 2, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 3: launch_ln_bwd<T, 3, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 4: launch_ln_bwd<T, 4, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 5: launch_ln_bwd<T, 5, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 6: launch_ln_bwd<T, 6, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    case 7: launch_ln_bwd<T, 7, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
+    default: launch_ln_bwd<T, 8, kThreads>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); break;
     }
 }
 
