@@ -626,7 +626,7 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     constexpr int KS = D / 16, DB = D / 32;
     constexpr int TILE = 64 * D * 2;
-    constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, lse and delta (64 floats each), 1 KB aligned
+    constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, lse * log2(e) and delta (64 floats each), 1 KB aligned
     constexpr int NST = kBwdKvStages;        // two query tiles in flight during a tile's work
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -698,33 +698,45 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     const int64_t do_ld = (int64_t)a.batch * ht;
     const int64_t stat0 = (int64_t)bh * a.seq;
 
-    // the tile's log-sum-exps and deltas (64 each) go straight into LDS
-    // after it, loaded by the first two waves (a stage is two tiles and 512
-    // bytes)
-    const __amdgpu_buffer_rsrc_t rstat =
-        make_rsrc(__builtin_amdgcn_readfirstlane(w) == 0 ? a.lse + stat0 : a.delta + stat0, (uint32_t)a.seq * 4);
     auto issue = [&](int t, char *st) {
         const int p0 = qstart + (t_first + t) * 64;
         rows_tile_dma<D>(rq, st, slab, D, p0, a.q1, w, lane);
         rows_tile_dma<D>(rdo, st + TILE, do_base, do_ld, p0, a.q1, w, lane);
-        if (w < 2) lds_dma4(rstat, st + 2 * TILE + w * 256, p0 + lane < a.q1 ? (uint32_t)(p0 + lane) * 4 : kOOB);
+    };
+    // the tile's statistics go through registers of the first two waves
+    float stat = 0.f;
+    auto load_stat = [&](int t) {
+        if (tid < 128) {
+            const int p = qstart + (t_first + t) * 64 + (tid & 63);
+            stat = p < a.q1 ? (tid < 64 ? a.lse[stat0 + p] * kLog2e : a.delta[stat0 + p]) : 0.f;
+        }
+    };
+    auto store_stat = [&](char *st) {
+        if (tid < 128) ((float *)(st + 2 * TILE))[tid] = stat;
     };
     // tile t sits in stage t % NST; tiles t + 1 and t + 2 are in flight while
-    // tile t is worked on
+    // tile t is worked on (each tile's statistics load precedes its DMA, so
+    // waiting for the statistics leaves the DMA outstanding)
 #pragma unroll
-    for (int t = 0; t < NST - 1; ++t)
-        if (t < nqt) issue(t, smem + t * STAGE);
+    for (int t = 0; t < NST - 1; ++t) {
+        if (t < nqt) {
+            load_stat(t);
+            issue(t, smem + t * STAGE);
+            store_stat(smem + t * STAGE);
+        }
+    }
     for (int t = 0; t < nqt; ++t) {
-        // tile t has landed once at most tile t+1's loads are outstanding
-        // (waves 0 and 1 issue one more per tile, its statistics, and so
-        // wait for that one as well); the barrier then also frees the stage
-        // of tile t-1
+        // tile t has landed once at most tile t+1's loads are outstanding;
+        // the barrier then also frees the stage of tile t-1
         if (t + 1 < nqt) wait_vmcnt<kBwdTileLoads<D>>();
         else wait_vmcnt<0>();
         __syncthreads();
         const char *st = smem + (t % NST) * STAGE;
         char *nx = smem + ((t + NST - 1) % NST) * STAGE;
-        if (t + NST - 1 < nqt) issue(t + NST - 1, nx);
+        if (t + NST - 1 < nqt) {
+            load_stat(t + NST - 1);
+            issue(t + NST - 1, nx);
+        }
         const int p0 = qstart + (t_first + t) * 64;
         const float *lse_s = (const float *)(st + 2 * TILE);
         const float *del_s = lse_s + 64;
@@ -748,9 +760,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int q = p0 + ql + u;
-                    const float pr = (my_k <= q && q < a.q1)
-                                         ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * r + u], sl2, -(l4[u] * kLog2e)))
-                                         : 0.f;
+                    const float pr =
+                        (my_k <= q && q < a.q1) ? __builtin_amdgcn_exp2f(sc[4 * r + u] * sl2 - l4[u]) : 0.f;
                     sc[4 * r + u] = pr;
                     dp[4 * r + u] = pr * (dp[4 * r + u] - d4[u]);
                 }
@@ -765,6 +776,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
                 }
             }
         }
+        if (t + NST - 1 < nqt) store_stat(nx);
     }
     if (my_k >= a.q1) return;
     if (nch > 1) {

@@ -30,36 +30,39 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
-// Direct-to-LDS buffer loads: each lane's 16 (lds_dma16) or 4 (lds_dma4)
-// bytes land at lds_base + 16 * lane (4 * lane); lds_base must be the same
-// for the whole wave (it goes to M0); an out-of-bounds offset writes zeros.
+// Direct-to-LDS buffer load: each lane's 16 bytes land at lds_base + 16 *
+// lane (lds_base must be the same for the whole wave: it goes to M0); an
+// out-of-bounds offset writes zeros.
 //
-// They are issued as inline assembly, out of sight of the compiler's wait
-// insertion.  That pass treats every LDS read after a direct-to-LDS load it
-// can see as possibly reading what the load writes (it cannot tell two
-// stages of one LDS buffer apart) and waits for all such loads in flight
-// (s_waitcnt vmcnt(0)) before the read, so a pipeline that reads stage s
-// while stage s + 1 loads would wait for stage s + 1 every time.  Hidden
-// from it, the loads are waited for where the kernels say: every caller
-// waits on vmcnt for its own loads and then synchronises the workgroup
-// before any wave reads what they wrote, and drains them before it ends.
-// (The compiler's own waits for other vector-memory loads only become
-// more conservative: it does not count these, so it waits for more.)
+// UNTRACKED issues it as inline assembly, out of sight of the compiler's
+// wait insertion.  That pass treats every LDS read after a direct-to-LDS
+// load it can see as possibly reading what the load writes (it cannot tell
+// two stages of one LDS buffer apart) and waits for all such loads in
+// flight (s_waitcnt vmcnt(0)) before the read, so a pipeline that reads
+// stage s while stage s + 1 loads waits for stage s + 1 at every step.
+// Hidden from it, the loads are waited for only where the kernel says: a
+// caller of the untracked form waits on vmcnt for its own loads and then
+// synchronises the workgroup before any wave reads what they wrote, and
+// drains them before it ends.  (The compiler's own waits for other loads
+// only become more conservative, as it does not count these.)  The price:
+// a volatile asm statement also fences the scheduler, which cannot move LDS
+// reads or other memory operations across it.  Measured in the layer step,
+// the untracked form is faster for the GEMM kernels that read an M/N-
+// contiguous operand (transposing LDS reads, 3-13%) and slower for those
+// whose operands are both K-contiguous and for attention (1-7%), which
+// therefore keep the tracked builtin.
 typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ uint32_t lds_m0(char *lds_base) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
-}
+template <bool UNTRACKED = false>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_m0(lds_base)), "v"(voff), "s"(r)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_m0(lds_base)), "v"(voff), "s"(r)
-                 : "memory", "m0");
+    if constexpr (UNTRACKED) {
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m0), "v"(voff), "s"(r)
+                     : "memory", "m0");
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_base, 16, voff, 0, 0, 0);
+    }
 }
 
 // s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
