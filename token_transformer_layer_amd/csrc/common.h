@@ -46,11 +46,11 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // drains them before it ends.  (The compiler's own waits for other loads
 // only become more conservative, as it does not count these.)  The price:
 // a volatile asm statement also fences the scheduler, which cannot move LDS
-// reads or other memory operations across it.  Measured in the layer step,
-// the untracked form is faster for the GEMM kernels that read an M/N-
-// contiguous operand (transposing LDS reads, 3-13%) and slower for those
-// whose operands are both K-contiguous and for attention (1-7%), which
-// therefore keep the tracked builtin.
+// reads or other memory operations across it, so the GEMM hand-over reads
+// the next tile's first fragments before it issues the refill.  Measured in
+// the layer step, the GEMM kernels take the untracked form (weight
+// gradients 7% faster, input-gradient products 3-16%), and the attention
+// kernels, 1-3% slower with it, keep the tracked builtin.
 typedef __attribute__((address_space(3))) void lds_void;
 template <bool UNTRACKED = false>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {

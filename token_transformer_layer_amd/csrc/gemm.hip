@@ -237,7 +237,6 @@ struct DlOperand {
         else return pos >= sh ? pos - sh : pos - sh + kUnits;
     }
 
-    template <bool UNTRACKED>
     __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char *stage, int mn0, int k0, int MN,
                                                  int K, int64_t ld, int wave, int lane) {
 #pragma unroll
@@ -256,7 +255,7 @@ struct DlOperand {
                 const int gk = k0 + k, gm = mn0 + u * 8;
                 off = (gm < MN && gk < K) ? (uint32_t)((gk * ld + gm) * 2) : kOOB;
             }
-            lds_dma16<UNTRACKED>(r, stage + I * 1024, off);
+            lds_dma16<true>(r, stage + I * 1024, off);
         }
     }
 
@@ -351,9 +350,6 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[FM][FN], char *smem, Ep
 template <class C, bool AK, bool BK_, class Epi>
 __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, Epi epi, int gm_rows) {
     constexpr int BM = C::kBM, BN = C::kBN, BK = C::kBK, S = C::kStages;
-    // direct-to-LDS loads hidden from the compiler's wait insertion where an
-    // operand is M/N-contiguous (see lds_dma16)
-    constexpr bool kUntracked = !(AK && BK_);
     constexpr int NW = C::kWM * C::kWN;
     constexpr int WTM = BM / C::kWM, WTN = BN / C::kWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -386,10 +382,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
 #pragma unroll
     for (int s = 0; s < S - 1; ++s) {
         if (s < nkt) {
-            OpA::template issue<kUntracked>(ra, smem + s * STAGE, m0, kbase + s * BK, g.M, kend, g.lda, wid,
-                                            lane);
-            OpB::template issue<kUntracked>(rb, smem + s * STAGE + OpA::kBytes, n0, kbase + s * BK, g.N, kend, g.ldb,
-                                            wid, lane);
+            OpA::issue(ra, smem + s * STAGE, m0, kbase + s * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, kbase + s * BK, g.N, kend, g.ldb, wid, lane);
         }
     }
     for (int kt = 0; kt < nkt; ++kt) {
@@ -410,10 +404,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_bf16_dl_kernel(GemmArgs g, E
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // no LDS read moves above the barrier
         if (kt + S - 1 < nkt) {
             char *st = smem + ((kt + S - 1) % S) * STAGE;
-            OpA::template issue<kUntracked>(ra, st, m0, kbase + (kt + S - 1) * BK, g.M, kend, g.lda, wid,
-                                            lane);
-            OpB::template issue<kUntracked>(rb, st + OpA::kBytes, n0, kbase + (kt + S - 1) * BK, g.N, kend, g.ldb,
-                                            wid, lane);
+            OpA::issue(ra, st, m0, kbase + (kt + S - 1) * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, st + OpA::kBytes, n0, kbase + (kt + S - 1) * BK, g.N, kend, g.ldb, wid, lane);
         }
         const char *cur = smem + (kt % S) * STAGE;
 #pragma unroll
@@ -470,7 +462,6 @@ template <class C, bool AK, bool BK_, class Epi>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kOcc * C::kThreads / 256)))
 void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
     constexpr int BM = C::kBM, BN = C::kBN, BK = C::kBK, S = C::kStages;
-    constexpr bool kUntracked = !(AK && BK_);  // see lds_dma16
     constexpr int NW = C::kWM * C::kWN;
     constexpr int WTM = BM / C::kWM, WTN = BN / C::kWN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -509,10 +500,8 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
         // has no branches for the scheduler to stop at.
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            OpA::template issue<kUntracked>(ra, smem + s * STAGE, m0, kbase + s * BK, g.M, kend, g.lda, wid,
-                                            lane);
-            OpB::template issue<kUntracked>(rb, smem + s * STAGE + OpA::kBytes, n0, kbase + s * BK, g.N, kend, g.ldb,
-                                            wid, lane);
+            OpA::issue(ra, smem + s * STAGE, m0, kbase + s * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, kbase + s * BK, g.N, kend, g.ldb, wid, lane);
         }
         wait_vmcnt<LPT * (S - 1)>();  // tile 0 has landed
         __builtin_amdgcn_s_barrier();
@@ -559,12 +548,13 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
             wait_vmcnt<LPT * (S - 2)>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            OpA::template issue<kUntracked>(ra, smem + stage * STAGE, m0, kbase + (kt + S) * BK, g.M, kend, g.lda,
-                                            wid, lane);
-            OpB::template issue<kUntracked>(rb, smem + stage * STAGE + OpA::kBytes, n0, kbase + (kt + S) * BK, g.N,
-                                            kend, g.ldb, wid, lane);
-            stage = stage + 1 == S ? 0 : stage + 1;
-            reads(smem + stage * STAGE, 0, 0);
+            // the next tile's first fragments are read before the refill is
+            // issued: no load is then in flight for the compiler to wait on
+            const int next = stage + 1 == S ? 0 : stage + 1;
+            reads(smem + next * STAGE, 0, 0);
+            OpA::issue(ra, smem + stage * STAGE, m0, kbase + (kt + S) * BK, g.M, kend, g.lda, wid, lane);
+            OpB::issue(rb, smem + stage * STAGE + OpA::kBytes, n0, kbase + (kt + S) * BK, g.N, kend, g.ldb, wid, lane);
+            stage = next;
             mfmas((KSTEPS - 1) & 1);
             sched_interleave<NREAD, FM * FN, LPT>();
         }
