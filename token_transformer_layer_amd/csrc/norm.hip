@@ -34,56 +34,6 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
     return red[0] + red[1] + red[2] + red[3];
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, const T *__restrict__ x,
-                                                          const T *__restrict__ g, const T *__restrict__ b,
-                                                          T *__restrict__ u, float *__restrict__ mean,
-                                                          float *__restrict__ rstd) {
-    __shared__ float red[4];
-    const int row = blockIdx.x, nv = h >> 3;
-    const T *xr = x + (size_t)row * h;
-    float v[kMaxVec][8];
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i) {
-        int c = threadIdx.x + i * kThreads;
-        if (c < nv) {
-            load8(xr + c * 8, v[i]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s += v[i][j];
-        }
-    }
-    const float mu = block_sum(s, red) / (float)h;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i) {
-        int c = threadIdx.x + i * kThreads;
-        if (c < nv) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { float dlt = v[i][j] - mu; q += dlt * dlt; }
-        }
-    }
-    const float var = block_sum(q, red) / (float)h;
-    const float r = 1.0f / sqrtf(var + eps);
-    T *ur = u + (size_t)row * h;
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i) {
-        int c = threadIdx.x + i * kThreads;
-        if (c < nv) {
-            float gg[8], bb[8], o[8];
-            load8(g + c * 8, gg);
-            load8(b + c * 8, bb);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = (v[i][j] - mu) * r * gg[j] + bb[j];
-            store8(ur + c * 8, o);
-        }
-    }
-    if (threadIdx.x == 0) {
-        mean[row] = mu;
-        rstd[row] = r;
-    }
-}
-
 // Rows [blockIdx.x * rpb, ...): dx = resid + rstd (gg - mean(gg) - xhat mean(gg xhat))
 // with gg = du * gamma; the block's sums of du * xhat and du over its rows go
 // to partials[block][0][:] and partials[block][1][:].  Each thread owns NV
@@ -123,6 +73,66 @@ __device__ __forceinline__ void store8_buf(__amdgpu_buffer_rsrc_t r, uint32_t of
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = pack_bf2(v[2 * i], v[2 * i + 1]);
     __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+}
+
+// One row per block: u = (x - mean) rstd gamma + beta, two-pass statistics
+// (mean, then the centred sum of squares) through wavefront sums and one LDS
+// exchange each.  The row stays in registers as loaded (packed bf16: 4
+// registers per 8 columns), so a block holds few registers and many rows are
+// in flight per CU; loads and stores go through a buffer descriptor of the
+// row (vectors past it read zeros and drop their stores).
+template <typename T, int NV>
+__global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, const T *__restrict__ x,
+                                                          const T *__restrict__ g, const T *__restrict__ b,
+                                                          T *__restrict__ u, float *__restrict__ mean,
+                                                          float *__restrict__ rstd) {
+    __shared__ float red[4];
+    const int row = blockIdx.x, nv = h >> 3;
+    const uint32_t row_t = (uint32_t)h * sizeof(T);
+    const __amdgpu_buffer_rsrc_t px = make_rsrc(x + (size_t)row * h, row_t);
+    uint32_t ot[NV];
+    Raw8<T> xv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        ot[i] = c < nv ? (uint32_t)c * (8 * sizeof(T)) : kOOB;
+        xv[i].load(px, ot[i]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += xv[i][j];  // vectors past the row are zeros
+    const float mu = block_sum(s, red) / (float)h;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (threadIdx.x + i * kThreads < nv) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float dlt = xv[i][j] - mu;
+                q += dlt * dlt;
+            }
+        }
+    }
+    const float var = block_sum(q, red) / (float)h;
+    const float r = 1.0f / sqrtf(var + eps);
+    const __amdgpu_buffer_rsrc_t pg = make_rsrc(g, row_t), pb = make_rsrc(b, row_t);
+    const __amdgpu_buffer_rsrc_t pu = make_rsrc(u + (size_t)row * h, row_t);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        Raw8<T> gr, br;
+        gr.load(pg, ot[i]);
+        br.load(pb, ot[i]);
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (xv[i][j] - mu) * r * gr[j] + br[j];
+        store8_buf(pu, ot[i], o, (T *)nullptr);
+    }
+    if (threadIdx.x == 0) {
+        mean[row] = mu;
+        rstd[row] = r;
+    }
 }
 
 template <typename T>
@@ -395,6 +405,28 @@ __global__ __launch_bounds__(kThreads) void gelu_backward_kernel(int64_t n8, con
 size_t layernorm_bwd_partials_floats(int rows, int h) { return (size_t)ln_bwd_blocks(rows) * 2 * h; }
 size_t colsum_partials_floats(int rows, int n) { return (size_t)colsum_chunks(rows) * n; }
 
+template <typename T, int NV>
+static void launch_ln_fwd(int rows, int h, float eps, const void *x, const void *g, const void *b, void *u,
+                          float *mean, float *rstd, hipStream_t st) {
+    hipLaunchKernelGGL((ln_fwd_kernel<T, NV>), dim3(rows), dim3(kThreads), 0, st, h, eps, (const T *)x, (const T *)g,
+                       (const T *)b, (T *)u, mean, rstd);
+}
+
+template <typename T>
+static void dispatch_ln_fwd(int rows, int h, float eps, const void *x, const void *g, const void *b, void *u,
+                            float *mean, float *rstd, hipStream_t st) {
+    switch (((h >> 3) + kThreads - 1) / kThreads) {  // vectors per thread, 1..kMaxVec
+    case 1: launch_ln_fwd<T, 1>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    case 2: launch_ln_fwd<T, 2>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    case 3: launch_ln_fwd<T, 3>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    case 4: launch_ln_fwd<T, 4>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    case 5: launch_ln_fwd<T, 5>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    case 6: launch_ln_fwd<T, 6>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    case 7: launch_ln_fwd<T, 7>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    default: launch_ln_fwd<T, 8>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
+    }
+}
+
 hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, const void *g, const void *b,
                          void *u, float *mean, float *rstd, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
@@ -402,11 +434,9 @@ hipError_t layernorm_fwd(DType dt, int rows, int h, float eps, const void *x, co
     TraceScope ts(st, dt == DType::BF16 ? "ln_fwd_bf16" : "ln_fwd_f32", 0.0,
                   (double)rows * h * 2 * es + 8.0 * rows + 2.0 * h * es);
     if (dt == DType::BF16)
-        hipLaunchKernelGGL(ln_fwd_kernel<bf16>, dim3(rows), dim3(kThreads), 0, st, h, eps, (const bf16 *)x,
-                           (const bf16 *)g, (const bf16 *)b, (bf16 *)u, mean, rstd);
+        dispatch_ln_fwd<bf16>(rows, h, eps, x, g, b, u, mean, rstd, st);
     else
-        hipLaunchKernelGGL(ln_fwd_kernel<float>, dim3(rows), dim3(kThreads), 0, st, h, eps, (const float *)x,
-                           (const float *)g, (const float *)b, (float *)u, mean, rstd);
+        dispatch_ln_fwd<float>(rows, h, eps, x, g, b, u, mean, rstd, st);
     return hipGetLastError();
 }
 
