@@ -222,20 +222,21 @@ struct DlOperand {
         else return (r >> 2) & 3;
     }
     // [BK][ROWS] layout: the 16-byte unit u of row k sits at position
-    // unit_pos(u, k), shifted by 4 (k % 4) units (64 bytes), so the four
-    // consecutive rows a transposing read touches together land on distinct
-    // banks; XOR for power-of-two widths, rotation otherwise (both bijective).
+    // unit_pos(u, k), so that the 4 rows x 4 units (256 bytes) that half a
+    // wave's transposing read touches cover all 64 banks once.  Power-of-two
+    // widths XOR the unit with 4 (k % 4).  A 24-unit row (192 columns, 384
+    // bytes: consecutive rows start 32 banks apart) swaps neighbouring 4-unit
+    // blocks in the rows with k % 4 >= 2 (the rotation by 4 (k % 4) that
+    // preceded it wrapped past the row's end and conflicted up to 5-way,
+    // 23% of the LDS cycles of the input-gradient products).  Both are XORs:
+    // their own inverse.
     static constexpr bool kPow2Units = (kUnits & (kUnits - 1)) == 0;
+    static_assert(kPow2Units || kUnits % 8 == 0, "non-power-of-two rows pair their 4-unit blocks");
     __device__ static __forceinline__ int unit_pos(int u, int k) {
-        const int sh = (k & 3) * 4 % kUnits;
-        if constexpr (kPow2Units) return u ^ sh;
-        else return u + sh < kUnits ? u + sh : u + sh - kUnits;
+        if constexpr (kPow2Units) return u ^ ((k & 3) * 4 % kUnits);
+        else return u ^ (((k >> 1) & 1) << 2);
     }
-    __device__ static __forceinline__ int unit_src(int pos, int k) {
-        const int sh = (k & 3) * 4 % kUnits;
-        if constexpr (kPow2Units) return pos ^ sh;
-        else return pos >= sh ? pos - sh : pos - sh + kUnits;
-    }
+    __device__ static __forceinline__ int unit_src(int pos, int k) { return unit_pos(pos, k); }
 
     __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, char *stage, int mn0, int k0, int MN,
                                                  int K, int64_t ld, int wave, int lane) {
