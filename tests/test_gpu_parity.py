@@ -92,10 +92,12 @@ def test_forced_gemm_tiles(shape, tile):
 
 
 WIDE = [
-    # hidden widths that give the LayerNorm kernels 4, 7 and 8 vectors of 8
-    # columns per thread (the bf16 backward at 8192: 512 threads of 2), with
-    # and without the next-row prefetch
+    # hidden widths that give the LayerNorm kernels 2, 4, 5, 7 and 8 vectors
+    # of 8 columns per thread (the bf16 backward at 8192 and 10240: 512
+    # threads of 2 and 3), with and without the next-row prefetch
+    LayerShape("wide-3072-bf16", 3072, 24, 128, 1024, 8, 1, 24, (10, 14), "bf16", seed=2015),
     LayerShape("wide-8192-bf16", 8192, 64, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2011),
+    LayerShape("wide-10240-bf16", 10240, 80, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2016),
     LayerShape("wide-14336-bf16", 14336, 112, 128, 1792, 16, 1, 24, (10, 14), "bf16", seed=2012),
     LayerShape("wide-16384-bf16", 16384, 128, 128, 2048, 16, 1, 24, (10, 14), "bf16", seed=2013),
     LayerShape("wide-12288-f32", 12288, 96, 128, 1536, 16, 1, 16, (7, 9), "f32", seed=2014),
