@@ -1,6 +1,7 @@
 """GPU parity of one device's cube-partition ops through the C-ABI against
 the fp64 oracle: the three product forms (fp32 results of bf16 operands:
-1e-4 of the largest magnitude), the elementwise bias/GELU and GELU-backward
+1e-4 of the largest magnitude), also with every GEMM tile configuration
+forced, the elementwise bias/GELU and GELU-backward
 steps (bf16 results: 2e-2), the FFN block assembled from two devices'
 local products with the reduction before bias and GELU, forward and
 backward, and sampled rows of the full-size backward products."""
@@ -63,6 +64,32 @@ def test_cube_forms(form_id, M, N, K):
     gpu_matmul(form_id, a, b, M, N, K, c=c, accumulate=True)
     torch.cuda.synchronize()
     assert _rel(c, 2 * ref) <= 1e-4
+
+
+@pytest.mark.parametrize("tile", range(7))
+@pytest.mark.parametrize("form_id", list(FORMS))
+@pytest.mark.parametrize("M,N,K", [(264, 392, 328), (520, 200, 1032)])
+def test_cube_forms_forced_tiles(tile, form_id, M, N, K):
+    """Every GEMM tile configuration (tp_gemm_force_tile) in the three operand
+    layouts on ragged shapes: partial edge tiles in M and N, and K not a
+    multiple of the 32- or 64-deep K-tiles."""
+    import torch
+    form = FORMS[form_id]
+    print("[case] cube form %s tile %d M=%d N=%d K=%d" % (form, tile, M, N, K), flush=True)
+    rng = np.random.default_rng(1000 * tile + M + N + K + form_id)
+    sa, sb = _shapes(form, M, N, K)
+    a, b = synth.round_bf16(rng.normal(size=sa)), synth.round_bf16(rng.normal(size=sb))
+    ref = OC.cube_matmul(form, a, b)
+    abi.tp_gemm_force_tile(tile)
+    try:
+        c = gpu_matmul(form_id, a, b, M, N, K)
+        torch.cuda.synchronize()
+        assert _rel(c, ref) <= 1e-4
+        gpu_matmul(form_id, a, b, M, N, K, c=c, accumulate=True)
+        torch.cuda.synchronize()
+        assert _rel(c, 2 * ref) <= 1e-4
+    finally:
+        abi.tp_gemm_force_tile(-1)
 
 
 def test_cube_elementwise_steps():
