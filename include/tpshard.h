@@ -360,10 +360,11 @@ tp_status tp_slicing_plan(int32_t units, const double *cost, int32_t stages, int
 tp_status tp_fit_context_model(int32_t n, const int32_t *len, const int32_t *offset, const double *ctx,
                                double coef[3]);
 
-/* cost[a * (units + 1) + b] = fwd[b - a] + (a > 0 ? ctx((b - a) g, a g) : 0)
+/* cost[a * (units + 1) + b] = fwd[b - a] + (a > 0 ? max(0, ctx((b - a) g, a g)) : 0)
  * for a < b (+inf otherwise), with fwd[k] the measured latency of a slice of
  * k units without context (fwd has units + 1 entries; fwd[0] unused) and ctx
- * the model above: the cost table of tp_slicing_plan. */
+ * the model above, taken as 0 where the fitted line extrapolates below zero
+ * (it is a latency): the cost table of tp_slicing_plan. */
 tp_status tp_slice_cost_table(int32_t units, int32_t granularity, const double *fwd, const double coef[3],
                               double *cost);
 

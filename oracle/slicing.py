@@ -24,7 +24,8 @@ Readings where the page is silent (each listed in the design doc):
   best latency found;
 * slice lengths are multiples of a granularity g (units of g tokens);
 * context model: ctx(l, o) = a_lo * l * o + a_o * o + a_1 for a slice of l
-  tokens after o tokens of context, least squares over the samples given.
+  tokens after o tokens of context, least squares over the samples given;
+  as a latency it is taken as max(0, ctx) in the slice costs.
 """
 import numpy as np
 
@@ -104,11 +105,13 @@ def context_time(model, l, o):
 
 
 def slice_cost_table(units, g, fwd, model):
-    """cost[a][b] = fwd[(b-a) g] + ctx((b-a) g, a g) (ctx 0 without context);
-    fwd maps a slice length in tokens to its measured no-context latency."""
+    """cost[a][b] = fwd[(b-a) g] + max(0, ctx((b-a) g, a g)) (ctx 0 without
+    context); fwd maps a slice length in tokens to its measured no-context
+    latency.  The context term is a latency, never negative: where the fitted
+    line extrapolates below zero it adds nothing."""
     cost = np.full((units + 1, units + 1), np.inf)
     for a in range(units):
         for b in range(a + 1, units + 1):
             l, o = (b - a) * g, a * g
-            cost[a, b] = fwd[l] + (context_time(model, l, o) if o > 0 else 0.0)
+            cost[a, b] = fwd[l] + (max(0.0, context_time(model, l, o)) if o > 0 else 0.0)
     return cost

@@ -88,6 +88,11 @@ def table_errors(orc):
     cost = orc.slice_cost_table(8, 16, fwd, model)
     err = abs(cost[0, 3] - fwd[48])                                   # no context
     err = max(err, abs(cost[2, 5] - (fwd[48] + 1e-3 * 48 * 32 + 2e-2 * 32 + 0.5)))
+    # a fit that extrapolates below zero (short slice, little context) adds
+    # nothing: the context term is a latency
+    neg = orc.slice_cost_table(8, 16, fwd, (1e-3, 2e-2, -3.0))
+    err = max(err, abs(neg[1, 2] - fwd[16]))                          # ctx(16, 16) = 0.256 + 0.32 - 3 < 0
+    err = max(err, abs(neg[4, 8] - (fwd[64] + 1e-3 * 64 * 64 + 2e-2 * 64 - 3.0)))  # 4.096 + 1.28 - 3 > 0
     return err
 
 
@@ -136,6 +141,7 @@ MUTANTS = [
     ("fit_context_model", "A = np.stack([l * o, o, np.ones_like(l)], axis=1)",
      "A = np.stack([l * o, l, np.ones_like(l)], axis=1)"),
     ("slice_cost_table", "l, o = (b - a) * g, a * g", "l, o = (b - a) * g, b * g"),
+    ("slice_cost_table", "max(0.0, context_time(model, l, o))", "context_time(model, l, o)"),
 ]
 
 

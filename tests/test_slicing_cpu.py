@@ -55,6 +55,12 @@ def test_fit_and_cost_table_match_oracle():
     fin = np.isfinite(ref_cost)
     assert np.array_equal(np.isfinite(cost), fin)
     assert np.allclose(cost[fin], ref_cost[fin], rtol=1e-14, atol=0)
+    # a model that extrapolates below zero for short slices with little context
+    neg = (coef[0], coef[1], -0.05)
+    cost = abi.tp_slice_cost_table(units, g, fwd, neg)
+    ref_cost = S.slice_cost_table(units, g, {k * g: fwd[k] for k in range(1, units + 1)}, neg)
+    assert np.allclose(cost[fin], ref_cost[fin], rtol=1e-14, atol=0)
+    assert (cost[fin] >= fwd[1:].min()).all()
 
 
 def test_bad_arguments():

@@ -83,7 +83,9 @@ tp_status tp_slice_cost_table(int32_t units, int32_t granularity, const double *
             if (a < b) {
                 const double l = (double)(b - a) * granularity, o = (double)a * granularity;
                 v = fwd[b - a];
-                if (a > 0) v += coef[0] * l * o + coef[1] * o + coef[2];
+                // the context term is a latency: a fitted line that
+                // extrapolates below zero adds nothing
+                if (a > 0) v += std::max(0.0, coef[0] * l * o + coef[1] * o + coef[2]);
             }
             cost[a * W + b] = v;
         }
