@@ -23,7 +23,8 @@ gradient in one call over all slices afterwards.
 Prints ONE JSON line.  value = algorithmic fwd+bwd TFLOP/s of the step:
 GEMMs 3 x 2 T h (4 h_t + 2 f_t) plus causal attention 3 x 2 b h_t s (s+1)
 flops, over the measured time per step (K timed steps after W warm-up steps,
-HIP events on the launch stream).  Per-kernel durations (the `kernels` table
+HIP events on the launch stream); an event at the end of each timed step gives
+the median and minimum step times beside that average.  Per-kernel durations (the `kernels` table
 and the roofline of the dominant kernel) come from a second pass of K steps
 with the library's event trace on, whose step time is reported as
 `traced_step_ms` (the events between launches cost the step about 6%).
@@ -31,6 +32,7 @@ with the library's event trace on, whose step time is reported as
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -94,7 +96,11 @@ def make_step(layer, bufs, mode):
     return step
 
 
-def time_steps(torch, step, steps, warmup, trace=False):
+def time_steps(torch, step, steps, warmup, trace=False, per_step=None):
+    """Average ms per step over `steps` steps after `warmup` untimed ones, the
+    host's wall-clock ms per step, and the trace records (if `trace`).  With a
+    list as `per_step`, an event marks the end of every step inside the timed
+    region and the list receives each step's own duration in ms."""
     from token_transformer_layer_amd import abi
     for _ in range(warmup):
         step()
@@ -102,13 +108,18 @@ def time_steps(torch, step, steps, warmup, trace=False):
     if trace:
         abi.tp_trace_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if per_step is not None else []
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(steps):
+    for i in range(steps):
         step()
+        if marks:
+            marks[i].record()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if marks:
+        per_step[:] = [(ev0 if i == 0 else marks[i - 1]).elapsed_time(m) for i, m in enumerate(marks)]
     recs = []
     if trace:
         recs = abi.tp_trace_read()
@@ -359,7 +370,8 @@ def main():
     total = g_fl + a_fl
 
     step = make_step(layer, bufs, "whole")
-    ms, wall_ms, _ = time_steps(torch, step, args.steps, args.warmup, trace=False)
+    per_step = []
+    ms, wall_ms, _ = time_steps(torch, step, args.steps, args.warmup, trace=False, per_step=per_step)
     if args.profile_only:
         if args.copy_mib > 0:
             n = args.copy_mib * (1 << 20) // 4
@@ -414,6 +426,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_median": round(statistics.median(per_step), 4) if per_step else None,
+        "step_ms_min": round(min(per_step), 4) if per_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
