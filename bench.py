@@ -30,10 +30,13 @@ with the library's event trace on, whose step time is reported as
 `traced_step_ms` (the events between launches cost the step about 6%).
 """
 import argparse
+import glob
 import json
 import os
+import re
 import statistics
 import sys
+import threading
 import time
 
 import numpy as np
@@ -94,6 +97,82 @@ def make_step(layer, bufs, mode):
             first = False
         layer.bwd(abi.TP_BWD_WGRAD, 0, M, dy=dy, dh=dh, accumulate=False)
     return step
+
+
+PEAK_CLOCK_MHZ = 2400.0       # the clock the published peak assumes
+
+
+class ClockSampler:
+    """Samples the graphics clock (MHz) that the amdgpu driver reports as
+    current in the device's DPM table (sysfs `pp_dpm_sclk`, the line marked
+    `*`) on a host thread, every `period` seconds between start() and stop().
+    Only where the node shows exactly one GPU (else the card cannot be matched
+    to the device and nothing is sampled)."""
+
+    def __init__(self, period=0.002):
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if len(files) == 1 else None
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+                    return float(m.group(1)) if m else None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except OSError:
+                return
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def start(self):
+        if self.path:
+            self._stop.clear()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self, source):
+        if not self.samples:
+            return None
+        return dict(mean=round(statistics.fmean(self.samples), 1), min=min(self.samples), max=max(self.samples),
+                    samples=len(self.samples), source=source)
+
+
+def sustained_clock(torch, step, seconds=1.2, tail=0.6):
+    """The graphics clock while `step` repeats back to back for `seconds`,
+    sampled over the last `tail` seconds.  The driver's reading is a smoothed
+    one that takes about a second to rise from idle (in a 64 ms timed region
+    it reads 1.3-1.6 GHz while the step time equals that of runs where it
+    reads 1.9 GHz), so it is taken here, after the timed steps, rather than
+    during them."""
+    clock = ClockSampler(period=0.005)
+    if not clock.path:
+        return None
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        if not clock._thread and time.perf_counter() - t0 >= seconds - tail:
+            clock.start()
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+    clock.stop()
+    return clock.summary("amdgpu sysfs pp_dpm_sclk while the step repeats for %.1f s, last %.1f s" % (seconds, tail))
 
 
 def time_steps(torch, step, steps, warmup, trace=False, per_step=None):
@@ -372,6 +451,8 @@ def main():
     step = make_step(layer, bufs, "whole")
     per_step = []
     ms, wall_ms, _ = time_steps(torch, step, args.steps, args.warmup, trace=False, per_step=per_step)
+    clk = None if args.profile_only else sustained_clock(torch, step)
+    clock_peak = PEAK_BF16_TFLOPS * clk["mean"] / PEAK_CLOCK_MHZ if clk else None
     if args.profile_only:
         if args.copy_mib > 0:
             n = args.copy_mib * (1 << 20) // 4
@@ -402,7 +483,8 @@ def main():
                     frac=round(achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic, kernel=dom_name,
                     launches=len(dom_recs), avg_launch_ms=round(dom_ms / len(dom_recs), 5),
                     algorithmic_bytes_per_launch=round(sum(r[2] for r in dom_recs) / len(dom_recs)),
-                    traffic_unit="HBM bytes per launch")
+                    traffic_unit="HBM bytes per launch",
+                    frac_at_measured_clock=round(achieved / clock_peak, 4) if clock_peak else None)
     traced_ms = sum(r[3] for r in recs) / args.steps
     gemm_ms = sum(r[3] for r in recs if r[0].startswith("gemm")) / args.steps
     gemm_fl = sum(r[1] for r in recs if r[0].startswith("gemm")) / args.steps
@@ -438,6 +520,8 @@ def main():
                    "seq_len": shape.seq, "slices": list(shape.slices), "calls": "one per phase over all slices",
                    "parallelism": "one tp rank of 8 on 1 GPU"},
         "frac_of_bf16_peak": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gfx_clock_mhz": clk,
+        "frac_of_clock_peak": round(total / (ms * 1e-3) / 1e12 / clock_peak, 4) if clock_peak else None,
         "gemm": dict(ms_per_step=round(gemm_ms, 4), tflops=round(gemm_fl / (gemm_ms * 1e-3) / 1e12, 1),
                      frac=round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)),
         "traced_kernel_ms_per_step": round(traced_ms, 4),
