@@ -275,6 +275,66 @@ def cube_block(torch, steps, warmup):
     return dict(ms=round(ms, 4), tflops=round(fl / (ms * 1e-3) / 1e12, 1))
 
 
+def clock_probe(torch, seconds=1.6, tail=0.8):
+    """Throughput and sustained graphics clock of single kernels repeated back
+    to back: the 175B shard's FC1 weight-gradient product (A^T B, 6144 x 12288
+    x 2048), its FC2-shaped forward product (A B^T, 2048 x 6144 x 12288) and a
+    long-context attention block (12 heads x 128, 4096 queries against an
+    earlier 4096-key block).  One JSON line per kernel; the clock is sampled
+    over the last `tail` seconds, and so is the time per call."""
+    from token_transformer_layer_amd import abi
+    st = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device="cpu").manual_seed(1007)
+
+    def run(name, fn, flops):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        clock = ClockSampler(period=0.005)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, n, timing = time.perf_counter(), 0, False
+        while time.perf_counter() - t0 < seconds:
+            if not timing and time.perf_counter() - t0 >= seconds - tail:
+                torch.cuda.synchronize()
+                clock.start()
+                e0.record()
+                timing, n = True, 0
+            for _ in range(4):
+                fn()
+            n += 4
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        clock.stop()
+        ms = e0.elapsed_time(e1) / n
+        tf = flops / (ms * 1e-3) / 1e12
+        clk = clock.summary("amdgpu sysfs pp_dpm_sclk over the last %.1f s of %.1f s" % (tail, seconds))
+        rec = dict(kernel=name, ms=round(ms, 4), tflops=round(tf, 1), frac=round(tf / PEAK_BF16_TFLOPS, 4),
+                   gfx_clock_mhz=clk)
+        if clk:
+            rec["frac_at_measured_clock"] = round(tf / (PEAK_BF16_TFLOPS * clk["mean"] / PEAK_CLOCK_MHZ), 4)
+        print(json.dumps(rec), flush=True)
+
+    for name, form, (M, N, K) in [("weight-gradient product 6144x12288x2048 (A^T B)", abi.TP_CUBE_ATB, (6144, 12288, 2048)),
+                                  ("forward product 2048x6144x12288 (A B^T)", abi.TP_CUBE_ABT, (2048, 6144, 12288))]:
+        ashape = (K, M) if form == abi.TP_CUBE_ATB else (M, K)
+        bshape = (K, N) if form == abi.TP_CUBE_ATB else (N, K)
+        a = torch.randn(ashape, generator=g).to("cuda", torch.bfloat16)
+        b = torch.randn(bshape, generator=g).to("cuda", torch.bfloat16)
+        c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        run(name, lambda: abi.tp_cube_matmul(form, M, N, K, a.data_ptr(), b.data_ptr(), c.data_ptr(), 0, st),
+            2.0 * M * N * K)
+        del a, b, c
+    bq, n, d, L = 1, 12, 128, 4096
+    q, k, v = [torch.randn((bq, n, L, d), generator=g).to("cuda", torch.bfloat16) for _ in range(3)]
+    o = torch.empty((bq, n, L, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((bq, n, L), dtype=torch.float32, device="cuda")
+    shape = abi.tp_attn_block_shape(bq, n, d, L, L, L, 0)
+    run("attention block 12x128, 4096 queries x 4096 earlier keys",
+        lambda: abi.tp_attn_block_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      st), 4.0 * d * L * L * n * bq)
+
+
 def sequence_parallel_step(torch, layer, bufs, steps, warmup):
     """One rank's step in the sequence-parallel form: LayerNorm, its backward
     and the residual combines on the rank's 1/t shard of the rows, the
@@ -425,6 +485,8 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --profile-only: also run one plain streaming kernel over this many MiB "
                          "(read once, written once), the calibration of rocprofv3's HBM byte counters")
+    ap.add_argument("--clock-probe", action="store_true",
+                    help="only time single kernels repeated back to back with the graphics clock they sustain")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU's shard: this build has no multi-GPU path "
@@ -433,6 +495,10 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.clock_probe:
+        torch.cuda.set_device(0)
+        clock_probe(torch)
+        return
     from token_transformer_layer_amd import synth
     from token_transformer_layer_amd.shard import ShardLayer
 
