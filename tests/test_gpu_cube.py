@@ -68,11 +68,12 @@ def test_cube_forms(form_id, M, N, K):
 
 @pytest.mark.parametrize("tile", range(7))
 @pytest.mark.parametrize("form_id", list(FORMS))
-@pytest.mark.parametrize("M,N,K", [(264, 392, 328), (520, 200, 1032)])
+@pytest.mark.parametrize("M,N,K", [(264, 392, 328), (520, 200, 1032), (264, 392, 512)])
 def test_cube_forms_forced_tiles(tile, form_id, M, N, K):
     """Every GEMM tile configuration (tp_gemm_force_tile) in the three operand
-    layouts on ragged shapes: partial edge tiles in M and N, and K not a
-    multiple of the 32- or 64-deep K-tiles."""
+    layouts on ragged shapes: partial edge tiles in M and N, with K not a
+    multiple of the 32- or 64-deep K-tiles (every load tested against the end
+    of K) or a whole number of them (load offsets fixed per lane)."""
     import torch
     form = FORMS[form_id]
     print("[case] cube form %s tile %d M=%d N=%d K=%d" % (form, tile, M, N, K), flush=True)

@@ -65,6 +65,21 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_ba
     }
 }
 
+// The untracked load with the LDS destination given as a wave-uniform LDS
+// byte address (kept in scalar registers by its caller).
+__device__ __forceinline__ void lds_dma16_at(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
+// LDS byte address of a pointer into shared memory, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr_of(char *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)p);
+}
+
 // s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 template <int N>
