@@ -575,11 +575,17 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
         [[maybe_unused]] uint32_t smem_lds = 0;
         if constexpr (WHOLE) {
             la = OpA::lanes(m0, g.M, g.lda, wid, lane);
-            lb = OpB::lanes(n0, g.N, g.ldb, wid, lane);
+            if constexpr (!(AK && BK_)) lb = OpB::lanes(n0, g.N, g.ldb, wid, lane);
             smem_lds = lds_addr_of(smem);
         }
         auto issue = [&](int s, int k0) __attribute__((always_inline)) {
-            if constexpr (WHOLE) {
+            if constexpr (WHOLE && AK && BK_) {
+                // two K-contiguous operands: B keeps the per-load test (with
+                // both operands on fixed offsets these products ran 3-9%
+                // slower, with A alone on them 2-3% faster)
+                OpA::issue_whole(ra, smem_lds + s * STAGE, la, k0, kend, g.lda, wid);
+                OpB::issue(rb, smem + s * STAGE + OpA::kBytes, n0, k0, g.N, kend, g.ldb, wid, lane);
+            } else if constexpr (WHOLE) {
                 OpA::issue_whole(ra, smem_lds + s * STAGE, la, k0, kend, g.lda, wid);
                 OpB::issue_whole(rb, smem_lds + s * STAGE + OpA::kBytes, lb, k0, kend, g.ldb, wid);
             } else {
@@ -777,19 +783,14 @@ static hipError_t launch_pp_as(const GemmArgs &g, const E &epi, hipStream_t st) 
     return hipGetLastError();
 }
 
-// Reductions of whole K-tiles (every split too) with an M/N-contiguous
-// operand take the kernel whose load offsets are fixed per lane; others test
-// every load against the end of K.  (Measured in the layer step: weight
-// gradients 2%, the input-gradient products 2-5% faster with fixed offsets,
-// the products of two K-contiguous operands 3-9% slower.)
+// Reductions of whole K-tiles (every split too) take the kernel whose load
+// offsets are fixed per lane; others test every load against the end of K.
+// (Measured in the layer step: weight gradients 2%, the input-gradient
+// products 2-5%, the forward products 2-3% faster.)
 template <class C, bool AK, bool BK_, class E>
 static hipError_t launch_pp(const GemmArgs &g, const E &epi, hipStream_t st) {
-    if constexpr (AK && BK_) {
-        return launch_pp_as<C, AK, BK_, E, false>(g, epi, st);
-    } else {
-        const bool whole = g.K % C::kBK == 0 && (g.nsplit == 1 || g.kc % C::kBK == 0);
-        return whole ? launch_pp_as<C, AK, BK_, E, true>(g, epi, st) : launch_pp_as<C, AK, BK_, E, false>(g, epi, st);
-    }
+    const bool whole = g.K % C::kBK == 0 && (g.nsplit == 1 || g.kc % C::kBK == 0);
+    return whole ? launch_pp_as<C, AK, BK_, E, true>(g, epi, st) : launch_pp_as<C, AK, BK_, E, false>(g, epi, st);
 }
 
 using Dl128 = DlCfg<128, 128, 2, 2, 2>;              // 64 KB of LDS: two workgroups per compute unit
