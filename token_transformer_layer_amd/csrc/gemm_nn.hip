@@ -1,0 +1,12 @@
+// Product kernels of one operand layout (input-gradient products: B N-contiguous).
+#include "gemm_kernels.h"
+
+namespace tpk {
+
+hipError_t gemm_layout_nn(bool is_bf16, const GemmArgs &g, Epi kind, const EpiArgs &e, float *split_ws, Tile tile,
+                          hipStream_t st) {
+    if (is_bf16) return dispatch_epi<bf16, true, false>(g, kind, e, split_ws, tile, st);
+    return dispatch_epi<float, true, false>(g, kind, e, nullptr, tile, st);
+}
+
+}  // namespace tpk
