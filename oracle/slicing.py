@@ -59,13 +59,16 @@ def slicing_optimal(units, cost, stages):
     the slice covering granules [a, b).  Returns (latency, ends) with ends
     the cumulative slice boundaries (last = units).
 
-    For each candidate largest latency c (every distinct cost value, in
-    increasing order): best[b] = min over a < b with cost[a][b] <= c of
+    For each candidate largest latency c (every distinct finite cost value,
+    in increasing order): best[b] = min over a < b with cost[a][b] <= c of
     best[a] + cost[a][b] (best[0] = 0); the plan latency is
     best[units] + (K-1) c.  Stops once (K-1) c alone reaches the best plan
     latency found."""
     cost = np.asarray(cost, dtype=np.float64)
-    cands = np.unique([cost[a, b] for a in range(units) for b in range(a + 1, units + 1)])
+    # a +inf cost forbids its slice, so it is never the largest latency of a
+    # plan: only finite costs are candidates
+    cands = np.unique([cost[a, b] for a in range(units) for b in range(a + 1, units + 1)
+                       if np.isfinite(cost[a, b])])
     best_lat, best_ends = np.inf, None
     for c in cands:
         if (stages - 1) * c >= best_lat:

@@ -96,9 +96,59 @@ def table_errors(orc):
     return err
 
 
+class SimulatedDevice:
+    """A stand-in for measured slice latencies whose true values are known:
+    a slice of l tokens after o tokens of context takes base(l) +
+    ctx(l, o), with base drawn once per length (a noisy, increasing
+    function, as measured kernels behave) and ctx = max(0, a l o + b o + c)
+    (zero without context).  It is queried like the GPU: the no-context time
+    per length, and the context overhead of a few (l, o) samples."""
+
+    def __init__(self, seed, grid, coef):
+        rng = np.random.default_rng(seed)
+        self.coef = coef
+        self.base = {l: 0.02 + 1e-4 * l + 2e-3 * rng.random() for l in grid}
+
+    def latency(self, l, o):
+        a, b, c = self.coef
+        return self.base[l] + (max(0.0, a * l * o + b * o + c) if o > 0 else 0.0)
+
+
+def simulated_table_errors(orc):
+    """The cost table assembled from a simulated device's no-context times
+    and a context model fitted to its samples equals, entry by entry, the
+    device's own latency of that slice at that offset; and the plan chosen
+    from the table is the best over every composition of the simulated
+    latencies."""
+    err = 0.0
+    rng = np.random.default_rng(11)
+    for units, g, coef in [(8, 16, (2e-7, 3e-5, 1e-3)), (6, 32, (3e-7, 2e-5, -2e-3))]:
+        grid = [g * k for k in range(1, units + 1)]
+        dev = SimulatedDevice(5 + units, grid, coef)
+        # samples only where the device's overhead is on its linear part, so
+        # the fit recovers it exactly
+        samp = [(l, o) for l in grid for o in grid if l + o <= units * g
+                and coef[0] * l * o + coef[1] * o + coef[2] > 0]
+        samp = [samp[i] for i in rng.permutation(len(samp))[:max(6, len(samp) // 2)]]
+        ls, os_ = [p[0] for p in samp], [p[1] for p in samp]
+        model = orc.fit_context_model(ls, os_, [dev.latency(l, o) - dev.latency(l, 0) for l, o in samp])
+        fwd = {l: dev.latency(l, 0) for l in grid}
+        cost = orc.slice_cost_table(units, g, fwd, model)
+        for a in range(units):
+            for b in range(a + 1, units + 1):
+                err = max(err, abs(cost[a, b] - dev.latency((b - a) * g, a * g)) / cost[a, b])
+        for k in (1, 3, 8):
+            lat, ends = orc.slicing_optimal(units, cost, k)
+            starts = [0] + ends[:-1]
+            sim = S.pipeline_latency_sim([dev.latency((b - a) * g, a * g) for a, b in zip(starts, ends)], k)
+            err = max(err, abs(sim - brute_best(units, cost, k)) / sim)
+    return err
+
+
 def pin_failures(orc):
     checks = [("latency", lambda: latency_errors(orc) < 1e-12), ("dp", lambda: dp_errors(orc) < 1e-12),
-              ("fit", lambda: fit_errors(orc) < 1e-9), ("table", lambda: table_errors(orc) < 1e-12)]
+              ("fit", lambda: fit_errors(orc) < 1e-9), ("table", lambda: table_errors(orc) < 1e-12),
+              ("simulated", lambda: simulated_table_errors(orc) < 1e-9)]
     for name, ok in checks:
         with np.errstate(all="ignore"):
             try:
@@ -123,6 +173,22 @@ def test_context_fit_recovers_and_satisfies_normal_equations():
 
 def test_cost_table_closed_form():
     assert table_errors(S) < 1e-12
+
+
+def test_cost_table_matches_simulated_device():
+    assert simulated_table_errors(S) < 1e-9
+
+
+def test_single_stage_with_forbidden_slices():
+    """One stage and slices forbidden by +inf costs: the plan avoids them and
+    the search evaluates no 0 * inf."""
+    cost = random_cost(5, np.random.default_rng(4))
+    cost[0, 5] = cost[1, 3] = np.inf
+    with np.errstate(all="raise"):
+        lat, ends = S.slicing_optimal(5, cost, 1)
+    assert lat == pytest.approx(brute_best(5, cost, 1))
+    starts = [0] + ends[:-1]
+    assert all(np.isfinite(cost[a, b]) for a, b in zip(starts, ends))
 
 
 def test_single_stage_prefers_one_slice_with_overhead():
