@@ -24,7 +24,7 @@ import numpy as np
 
 from .layer import gelu, gelu_grad
 
-__all__ = ["cube_matmul", "cube_bias_gelu", "cube_gelu_backward", "matmul_grads"]
+__all__ = ["cube_matmul", "cube_bias_gelu", "cube_gelu_backward", "matmul_grads", "cube_ffn_devices"]
 
 FORMS = ("ab", "abt", "atb")
 
@@ -66,3 +66,25 @@ def cube_gelu_backward(dh, z):
     """dZ = dH * GELU'(Z) and the bias gradient db = sum of dZ over rows."""
     dz = np.asarray(dh, dtype=np.float64) * gelu_grad(z)
     return dz, dz.sum(axis=0)
+
+
+def cube_ffn_devices(x, w1, b1, w2, dout, p):
+    """The FFN block out = GELU(x w1^T + b1) w2^T over p devices along each
+    reduction (x [rows, hidden], w1 [ffn, hidden], w2 [hidden, ffn]), and its
+    backward for the output gradient dout: each device multiplies its
+    gathered blocks (the column ranges of the reduction it owns), the
+    partial sums are reduced (a sum), and only then are the bias and GELU
+    applied.  Returns (out, grads) with grads x, w1, b1, w2 (fp64).  With
+    p = 1 this is the unsharded block."""
+    x, w1, b1, w2, dout = (np.asarray(t, dtype=np.float64) for t in (x, w1, b1, w2, dout))
+    hs = np.array_split(np.arange(x.shape[1]), p)
+    fs = np.array_split(np.arange(w1.shape[0]), p)
+    z_sum = sum(cube_matmul("abt", x[:, c], w1[:, c]) for c in hs)
+    z, h = cube_bias_gelu(z_sum, b1)
+    out = sum(cube_matmul("abt", h[:, c], w2[:, c]) for c in fs)
+    dh = np.concatenate([cube_matmul("ab", dout, w2[:, c]) for c in fs], axis=1)
+    dz, db1 = cube_gelu_backward(dh, z)
+    dw2 = np.concatenate([cube_matmul("atb", dout, h[:, c]) for c in fs], axis=1)
+    dw1 = np.concatenate([cube_matmul("atb", dz, x[:, c]) for c in hs], axis=1)
+    dx = sum(cube_matmul("ab", dz[:, c], w1[c, :]) for c in fs)
+    return out, dict(x=dx, w1=dw1, b1=db1, w2=dw2)

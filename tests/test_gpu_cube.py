@@ -154,12 +154,8 @@ def test_cube_ffn_two_devices():
     dx = sum(gpu_matmul(abi.TP_CUBE_AB, dzb[:, c], w1[c, :], rows, hid, len(c)) for c in fs)
     torch.cuda.synchronize()
     # oracle: the unsharded block and its gradients
-    z = x.astype(np.float64) @ w1.T + b1
-    h = oracle.gelu(z)
-    r_out = h @ w2.T
-    r_dh = dout @ w2
-    r_dz = r_dh * oracle.gelu_grad(z)
-    ref = dict(out=r_out, dw2=dout.T @ h, dw1=r_dz.T @ x, dx=r_dz @ w1, db1=r_dz.sum(0))
+    r_out, r_g = OC.cube_ffn_devices(x, w1, b1, w2, dout, p=1)
+    ref = dict(out=r_out, dw2=r_g["w2"], dw1=r_g["w1"], dx=r_g["x"], db1=r_g["b1"])
     got = dict(out=out, dw2=dw2, dw1=dw1, dx=dx, db1=db1)
     for k in ref:
         assert _rel(got[k], ref[k]) <= 2e-2, k

@@ -67,30 +67,16 @@ def ffn_loops(x, w1, b1, w2):
     return loops_product("abt", h, w2)
 
 
-def cube_ffn(orc, x, w1, b1, w2, dout, p):
-    """The FFN over p devices along each reduction: local products of the
-    gathered blocks, the partial sums reduced, then bias and GELU; backward
-    with the same local products."""
-    hs = np.array_split(np.arange(x.shape[1]), p)
-    fs = np.array_split(np.arange(w1.shape[0]), p)
-    z_sum = sum(orc.cube_matmul("abt", x[:, c], w1[:, c]) for c in hs)
-    z, h = orc.cube_bias_gelu(z_sum, b1)
-    out = sum(orc.cube_matmul("abt", h[:, c], w2[:, c]) for c in fs)
-    dh = np.concatenate([orc.cube_matmul("ab", dout, w2[:, c]) for c in fs], axis=1)
-    dz, db1 = orc.cube_gelu_backward(dh, z)
-    dw2 = np.concatenate([orc.cube_matmul("atb", dout, h[:, c]) for c in fs], axis=1)
-    dw1 = np.concatenate([orc.cube_matmul("atb", dz, x[:, c]) for c in hs], axis=1)
-    dx = sum(orc.cube_matmul("ab", dz[:, c], w1[c, :]) for c in fs)
-    return out, dict(x=dx, w1=dw1, b1=db1, w2=dw2)
-
-
 def ffn_error(orc):
     rng = np.random.default_rng(3)
     rows, hid, f = 3, 4, 6
     x, w1, b1, w2 = (rng.normal(size=s) for s in ((rows, hid), (f, hid), (f,), (hid, f)))
     dout = rng.normal(size=(rows, hid))
-    out, g = cube_ffn(orc, x, w1, b1, w2, dout, p=2)
+    out, g = orc.cube_ffn_devices(x, w1, b1, w2, dout, p=2)
     err = float(np.abs(out - ffn_loops(x, w1, b1, w2)).max())
+    for p in (1, 3):
+        out_p, g_p = orc.cube_ffn_devices(x, w1, b1, w2, dout, p=p)
+        err = max(err, float(np.abs(out_p - out).max()), *(float(np.abs(g_p[k] - g[k]).max()) for k in g))
     eps = 1e-6
     params = dict(x=x, w1=w1, b1=b1, w2=w2)
     for name, val in params.items():
@@ -147,6 +133,9 @@ MUTANTS = [
     ("cube_bias_gelu", "return z, gelu(z)", "return z, gelu(np.asarray(z_sum, dtype=np.float64))"),
     ("cube_gelu_backward", "return dz, dz.sum(axis=0)", "return dz, dz.sum(axis=1)"),
     ("cube_gelu_backward", "dz = np.asarray(dh, dtype=np.float64) * gelu_grad(z)", "dz = np.asarray(dh, dtype=np.float64)"),
+    ("cube_ffn_devices", "dx = sum(cube_matmul(\"ab\", dz[:, c], w1[c, :]) for c in fs)",
+     "dx = sum(cube_matmul(\"ab\", dz[:, c], w1[c, :]) for c in fs[:1])"),
+    ("cube_ffn_devices", "z, h = cube_bias_gelu(z_sum, b1)", "z, h = cube_bias_gelu(z_sum, 0 * b1)"),
 ]
 
 
