@@ -30,10 +30,17 @@ def _layer(shape, sp):
     return ShardLayer(shape, sp)
 
 
-def _oracle_step(shape, sp, x, h_mid, dy, du2, du1):
-    # the oracle's result does not depend on the slice boundaries (pinned on
-    # the CPU), so it runs the sequence as one slice
-    return oracle.shard_layer_step(x, h_mid, dy, du2, du1, sp, shape.as_dict(), [0, shape.seq])
+# the last oracle result, reused by the groupings of one case (the oracle's
+# result does not depend on the slice boundaries: pinned on the CPU)
+_ORACLE_CACHE = {}
+
+
+def _oracle_step(key, shape, sp, x, h_mid, dy, du2, du1):
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE.clear()
+        # one slice: the result does not depend on the partition
+        _ORACLE_CACHE[key] = oracle.shard_layer_step(x, h_mid, dy, du2, du1, sp, shape.as_dict(), [0, shape.seq])
+    return _ORACLE_CACHE[key]
 
 
 def _check_shard(shape, variant, mode, rank=0, full=True, split_wgrad=False):
@@ -43,12 +50,12 @@ def _check_shard(shape, variant, mode, rank=0, full=True, split_wgrad=False):
     else:
         sp = synth.shard_params_direct(shape, variant, rank)
     h_mid, du2, du1 = H.step_inputs(shape, shape.seed + 1)
-    print("[case] %s variant=%s mode=%s rank=%d split_wgrad=%s" % (shape.name, variant, mode, rank, split_wgrad),
-          flush=True)
+    case = "%s variant=%s mode=%s rank=%d split_wgrad=%s" % (shape.name, variant, mode, rank, split_wgrad)
+    print("[case] " + case, flush=True)
     layer = _layer(shape, sp)
     got = H.run_shard_step(layer, x, h_mid, dy, du2, du1, H.groups_of(mode, len(shape.slices)), split_wgrad)
-    ref = _oracle_step(shape, sp, x, h_mid, dy, du2, du1)
-    bad = H.compare_step(got, ref, TOL[shape.dtype])
+    ref = _oracle_step((shape, variant, rank, full), shape, sp, x, h_mid, dy, du2, du1)
+    bad = H.compare_step(got, ref, TOL[shape.dtype], meta=H.step_meta(shape), case=case)
     assert not bad, bad
     return got
 
@@ -66,6 +73,34 @@ def test_tiny_fp32_ragged_sharp():
 @pytest.mark.parametrize("shape", [RAGGED_D64, RAGGED_D128], ids=lambda s: s.name)
 def test_bf16_shard_ragged(shape, mode):
     _check_shard(shape, "perturbed", mode, rank=1)
+
+
+# Slices of 1, 2 and 7 tokens and token-by-token partitions (a partition is
+# any l_1..l_M with sum L: "TeraPipe" summary page, section 3) on the bf16
+# kernels: single-query attention tiles, the empty prefix of a first slice
+# of one token, dK/dV query tiles that start off a 64-row boundary, and
+# products of M = batch rows that split their reduction.
+SHORT_D128 = LayerShape("short-slices-d128", 1024, 8, 128, 2816, 2, 2, 128, (1, 1, 2, 60, 64), "bf16", seed=2021)
+SHORT_D64 = LayerShape("short-slices-d64", 640, 10, 64, 4000, 2, 2, 128, (1, 2, 7, 63, 1, 54), "bf16", seed=2022)
+TOKENWISE_D64_B1 = LayerShape("token-by-token-d64-b1", 640, 10, 64, 4000, 2, 1, 8, (1,) * 8, "bf16", seed=2023)
+TOKENWISE_D64_B3 = LayerShape("token-by-token-d64-b3", 640, 10, 64, 4000, 2, 3, 8, (1,) * 8, "bf16", seed=2024)
+TOKENWISE_D128 = LayerShape("token-by-token-d128", 1024, 8, 128, 2816, 2, 2, 12, (1,) * 12, "bf16", seed=2025)
+SHORT = [SHORT_D128, SHORT_D64, TOKENWISE_D64_B1, TOKENWISE_D64_B3, TOKENWISE_D128]
+
+
+@pytest.mark.parametrize("mode", ["per-slice", "pairs", "whole"])
+@pytest.mark.parametrize("shape", SHORT, ids=lambda s: s.name)
+def test_bf16_short_slices(shape, mode):
+    _check_shard(shape, "perturbed", mode, rank=1)
+
+
+@pytest.mark.parametrize("shape", SHORT, ids=lambda s: s.name)
+def test_bf16_short_slices_split_weight_gradients(shape):
+    _check_shard(shape, "perturbed", "per-slice", rank=0, split_wgrad=True)
+
+
+def test_bf16_short_slices_peaked():
+    _check_shard(SHORT_D128, "peaked", "per-slice", rank=0)
 
 
 @pytest.mark.parametrize("shape", [TINY_RAGGED_F32, RAGGED_D64, RAGGED_D128], ids=lambda s: s.name)
@@ -118,15 +153,21 @@ def test_bf16_peaked_softmax():
     _check_shard(RAGGED_D128, "peaked", "per-slice", rank=0)
 
 
-def test_medium_bf16_config():
-    _check_shard(synth.CONFIGS["medium-bf16"], "standard", "whole", rank=2)
+@pytest.mark.parametrize("mode,split", [("whole", False), ("per-slice", False), ("per-slice", True)],
+                         ids=["whole", "per-slice", "per-slice-split-wgrad"])
+def test_medium_bf16_config(mode, split):
+    _check_shard(synth.CONFIGS["medium-bf16"], "standard", mode, rank=2, split_wgrad=split)
 
 
-@pytest.mark.parametrize("name", ["gpt13b-t8", "gpt3-175b-t8"])
-def test_full_size_shard(name):
+@pytest.mark.parametrize("name,mode,split", [("gpt13b-t8", "whole", False), ("gpt13b-t8", "per-slice", False),
+                                             ("gpt13b-t8", "per-slice", True), ("gpt3-175b-t8", "whole", False)],
+                         ids=["gpt13b-t8-whole", "gpt13b-t8-per-slice", "gpt13b-t8-per-slice-split-wgrad",
+                              "gpt3-175b-t8-whole"])
+def test_full_size_shard(name, mode, split):
     """The full-size shards in the grouping the benchmark times (one call
-    per phase over all slices), every output against the fp64 oracle."""
-    _check_shard(synth.CONFIGS[name], "standard", "whole", rank=0, full=False)
+    per phase over all slices) and, for the 13B shard's non-uniform
+    partition, one call per slice; every output against the fp64 oracle."""
+    _check_shard(synth.CONFIGS[name], "standard", mode, rank=0, full=False, split_wgrad=split)
 
 
 def _full_layer_on_gpu(shape, variant, mode):
