@@ -223,6 +223,25 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
                              int32_t phase, const void *in, float *partial_out,
                              tp_kv_cache *kv, void *saved, void *scratch, void *stream);
 
+/* tp_shard_layer_fwd without the scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same phases, arguments, checks,
+ * kernels and results (bit-identical) as tp_shard_layer_fwd; its work areas
+ * (split-product and split-KV attention partial sums) live in a static
+ * device array of tp_noalloc_scratch_bytes() bytes (128 MiB) that each GPU
+ * the library runs on holds until the process ends.  The call allocates
+ * nothing.  A call whose attention needs more work space than the array
+ * leaves returns TP_ESHAPE before anything is enqueued; with tracing on
+ * (tp_trace_enable, which creates events) it returns TP_EUNSUPPORTED.  All
+ * calls on one GPU share its array: calls that overlap on one GPU (other
+ * streams or threads) race and must be serialised by the caller. */
+tp_status tp_shard_layer_fwd_noalloc(const tp_shard_cfg *cfg, const tp_shard_weights *w,
+                                     const tp_partition *part, int32_t slice_begin,
+                                     int32_t slice_end, int32_t phase, const void *in,
+                                     float *partial_out, tp_kv_cache *kv, void *saved,
+                                     void *stream);
+size_t tp_noalloc_scratch_bytes(void);
+
 /* Backward of one phase over slices [slice_begin, slice_end).  Phases of one
  * slice range run in the order MLP, ATTN, LN1 (or their _DATA forms); slice
  * ranges run in reverse; TP_BWD_WGRAD runs after the _DATA calls of its rows.

@@ -23,7 +23,8 @@ EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fw
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_attn_block_fwd",
             "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table",
             "tp_cube_matmul", "tp_cube_bias_gelu", "tp_cube_work_bytes", "tp_cube_gelu_backward",
-            "tp_layernorm_work_bytes", "tp_layernorm_fwd", "tp_layernorm_bwd", "tp_trace_enable", "tp_trace_read", "tp_gemm_force_tile", "tp_last_error"]
+            "tp_layernorm_work_bytes", "tp_layernorm_fwd", "tp_layernorm_bwd", "tp_trace_enable", "tp_trace_read",
+            "tp_gemm_force_tile", "tp_last_error", "tp_shard_layer_fwd_noalloc", "tp_noalloc_scratch_bytes"]
 
 
 class TPError(RuntimeError):
@@ -92,6 +93,11 @@ def lib():
     L.tp_shard_layer_fwd.argtypes = [P(tp_shard_cfg), P(tp_shard_weights), P(tp_partition), i32, i32, i32,
                                      vp, vp, P(tp_kv_cache), vp, vp, vp]
     L.tp_shard_layer_fwd.restype = ctypes.c_int
+    L.tp_shard_layer_fwd_noalloc.argtypes = [P(tp_shard_cfg), P(tp_shard_weights), P(tp_partition), i32, i32,
+                                             i32, vp, vp, P(tp_kv_cache), vp, vp]
+    L.tp_shard_layer_fwd_noalloc.restype = ctypes.c_int
+    L.tp_noalloc_scratch_bytes.argtypes = []
+    L.tp_noalloc_scratch_bytes.restype = ctypes.c_size_t
     L.tp_shard_layer_bwd.argtypes = [P(tp_shard_cfg), P(tp_shard_weights), P(tp_partition), i32, i32, i32,
                                      vp, vp, vp, vp, vp, vp, P(tp_shard_grads), P(tp_kv_cache), P(tp_kv_grad),
                                      vp, vp, vp]
@@ -169,6 +175,17 @@ def tp_shard_layer_fwd(cfg, w, part, slice_begin, slice_end, phase, in_ptr, part
     _check(lib().tp_shard_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(part), slice_begin,
                                     slice_end, phase, in_ptr, partial_out,
                                     ctypes.byref(kv) if kv is not None else None, saved, scratch, stream))
+
+
+def tp_shard_layer_fwd_noalloc(cfg, w, part, slice_begin, slice_end, phase, in_ptr, partial_out, kv, saved,
+                               stream):
+    _check(lib().tp_shard_layer_fwd_noalloc(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(part), slice_begin,
+                                            slice_end, phase, in_ptr, partial_out,
+                                            ctypes.byref(kv) if kv is not None else None, saved, stream))
+
+
+def tp_noalloc_scratch_bytes():
+    return lib().tp_noalloc_scratch_bytes()
 
 
 def tp_shard_layer_bwd(cfg, w, part, slice_begin, slice_end, phase, dy, ln_in, reduced_in, partial_out, dh, dx,

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtpshard.so")
 SOURCES = ["gemm_tn.hip", "gemm_nn.hip", "gemm_nt.hip", "attention.hip", "norm.hip", "gemm.hip", "api.cpp", "trace.cpp",
-           "slicing.cpp"]
+           "slicing.cpp", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -204,9 +204,16 @@ tp_status tp_gemm_force_tile(int32_t tile) {
     return TP_OK;
 }
 
-tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part,
-                             int32_t slice_begin, int32_t slice_end, int32_t phase, const void *in,
-                             float *partial_out, tp_kv_cache *kv, void *saved, void *scratch, void *stream) {
+}  // extern "C"
+
+// The forward of one phase with its two work areas given: the split-product
+// partial sums (split_floats floats at split_ws) and the split-KV partial
+// sums of attention (attn_floats floats at attn_work).  A call whose
+// attention needs more than attn_floats fails before anything is enqueued.
+__attribute__((visibility("hidden"))) tp_status tp_internal_shard_fwd(
+    const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part, int32_t slice_begin,
+    int32_t slice_end, int32_t phase, const void *in, float *partial_out, tp_kv_cache *kv, void *saved,
+    float *split_ws, int64_t split_floats, float *attn_work, int64_t attn_floats, void *stream) {
     Dims d;
     tp_status s = check_cfg(cfg, &d);
     if (s != TP_OK) return s;
@@ -219,17 +226,23 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     NEED(in, "in");
     NEED(partial_out, "partial_out");
     NEED(saved, "saved");
-    NEED(scratch, "scratch");
+    if (phase == TP_FWD_ATTN || phase == TP_FWD_ATTN_SP) {
+        const int64_t need = d.dt == DType::BF16
+                                 ? (int64_t)attn_fwd_call_work_floats((int)d.b, (int)d.nt, (int)o0, (int)o1, (int)d.d)
+                                 : 0;
+        if (need > attn_floats)
+            return fail(TP_ESHAPE, "attention of this call needs %lld bytes of work space, %lld are available",
+                        (long long)need * 4, (long long)attn_floats * 4);
+    }
     const Saved L = saved_layout(d);
-    const Scratch S = scratch_layout(d);
     const int64_t r0 = o0 * d.b, nrows = (o1 - o0) * d.b;
     hipStream_t st = (hipStream_t)stream;
     const int es = d.es;
-    // every product may split its reduction through the scratch workspace
+    // every product may split its reduction through the split workspace
     auto fresh = [&]() {
         EpiArgs x;
-        x.split_ws = at<float *>(scratch, S.split);
-        x.split_ws_floats = d.dt == DType::BF16 ? (int64_t)gemm_split_workspace_floats() : 0;
+        x.split_ws = split_ws;
+        x.split_ws_floats = d.dt == DType::BF16 ? split_floats : 0;
         return x;
     };
     EpiArgs e = fresh();
@@ -271,7 +284,7 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         a.scale = 1.0f / std::sqrt((float)d.d);
         a.q = at<char *>(saved, L.q); a.k = kv->k; a.v = kv->v;
         a.o = at<char *>(saved, L.o); a.lse = at<float *>(saved, L.lse);
-        a.work = at<float *>(scratch, S.attn);
+        a.work = attn_work;
         HIPCALL(attn_fwd(d.dt, a, st), "attention forward");
         e = fresh();
         e.c = partial_out + r0 * d.h;
@@ -310,6 +323,21 @@ tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
                  st),
             "FC2 product");
     return TP_OK;
+}
+
+extern "C" {
+
+tp_status tp_shard_layer_fwd(const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part,
+                             int32_t slice_begin, int32_t slice_end, int32_t phase, const void *in,
+                             float *partial_out, tp_kv_cache *kv, void *saved, void *scratch, void *stream) {
+    Dims d;
+    tp_status s = check_cfg(cfg, &d);
+    if (s != TP_OK) return s;
+    NEED(scratch, "scratch");
+    const Scratch S = scratch_layout(d);
+    return tp_internal_shard_fwd(cfg, w, part, slice_begin, slice_end, phase, in, partial_out, kv, saved,
+                                 at<float *>(scratch, S.split), (int64_t)gemm_split_workspace_floats(),
+                                 at<float *>(scratch, S.attn), (S.split - S.attn) / 4, stream);
 }
 
 tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w, const tp_partition *part,

@@ -1205,6 +1205,16 @@ static void fwd_split(const AttnArgs &x, AttnFwdP &p) {
     p.n_items = p.items_bh * bh;
 }
 
+size_t attn_fwd_call_work_floats(int batch, int nt, int q0, int q1, int d) {
+    if (q1 <= q0) return 0;
+    AttnArgs x{};
+    x.batch = batch; x.nt = nt; x.q0 = q0; x.q1 = q1; x.d = d;
+    AttnFwdP p{};
+    fwd_split(x, p);
+    if (p.max_chunks <= 1) return 0;  // no query tile is split: nothing is written
+    return (size_t)batch * nt * p.nqt * p.max_chunks * kFwdBQ * (d + 2);
+}
+
 size_t attn_fwd_work_floats(int batch, int nt, int seq, int d) {
     const int nqt = (seq + kFwdBQ - 1) / kFwdBQ;
     const size_t fwd = (size_t)batch * nt * nqt * kFwdMaxChunks * kFwdBQ * (d + 2);

@@ -96,6 +96,8 @@ struct AttnArgs {
     float *work;          // partial sums of split work (attn_fwd_work_floats floats; fwd and bwd)
 };
 size_t attn_fwd_work_floats(int batch, int nt, int seq, int d);
+// floats of split-KV partial sums the forward over queries [q0, q1) writes
+size_t attn_fwd_call_work_floats(int batch, int nt, int q0, int q1, int d);
 hipError_t attn_fwd(DType dt, const AttnArgs &a, hipStream_t st);
 hipError_t attn_bwd(DType dt, const AttnArgs &a, hipStream_t st);
 
