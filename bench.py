@@ -246,10 +246,77 @@ def cpu_baseline(shape, budget_slices):
     oracle.shard_layer_step(x, h_mid, dy, du2, du1, sp, sample.as_dict(), synth.slice_bounds(sample.slices))
     dt = time.perf_counter() - t0
     g, a = step_flops(sample)
+    ncpu, model = host_cpu()
     return dict(value=round((g + a) / dt / 1e12, 5), unit="TFLOP/s", cores=threads, kind="oracle",
                 sample="%d of %d token slices (positions 0-%d, batch %d) of the same shard, fp64 numpy, %.1f s"
                        % (budget_slices, len(shape.slices), seq - 1, shape.batch, dt),
-                seconds=round(dt, 2))
+                seconds=round(dt, 2), host_logical_cpus=ncpu, cpu_model=model,
+                threads="%d BLAS threads (numpy's thread pool) on a host with %s logical CPUs" % (threads, ncpu))
+
+
+def per_slice_figures(torch, layer, bufs, steps, warmup):
+    """The pipeline-faithful schedule (one call per slice; backward data
+    phases per slice in reverse, then every weight gradient in one call): its
+    step time, and the HBM roofline of its 128-row products.  Every slice's
+    forward products and backward input-gradient products read the whole
+    shard's weights once, so a step streams 2 x slices x (weight bytes) from
+    HBM; those products are the launches that split their reduction (the
+    `_split` kernels and their reduction kernel), timed in a traced pass."""
+    step = make_step(layer, bufs, "per-slice")
+    ms, _, _ = time_steps(torch, step, steps, warmup)
+    _, _, recs = time_steps(torch, step, steps, 1, trace=True)
+    sh = layer.shape
+    ht, ft = sh.hidden // sh.tp, sh.ffn // sh.tp
+    weight_bytes = 2.0 * (3 * ht * sh.hidden + sh.hidden * ht + 2 * ft * sh.hidden)  # bf16 W_qkv, W_o, W1, W2
+    streamed = 2.0 * len(sh.slices) * weight_bytes
+    prod_ms = sum(r[3] for r in recs if r[0].endswith("_split") or r[0].startswith("splitk_reduce")) / steps
+    g_fl, a_fl = step_flops(sh)
+    achieved = streamed / (prod_ms * 1e-3) / 1e9 if prod_ms > 0 else None
+    return dict(ms_per_step=round(ms, 4), tflops=round((g_fl + a_fl) / (ms * 1e-3) / 1e12, 1),
+                roofline=dict(bound="hbm", unit="GB/s", peak=PEAK_HBM_GBS,
+                              achieved=round(achieved, 1) if achieved else None,
+                              frac=round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
+                              weight_bytes_per_step=streamed, products_ms_per_step=round(prod_ms, 4),
+                              what="shard weights streamed by the per-slice 128-row products (forward and "
+                                   "input-gradient, each slice reads every weight once) over those products' "
+                                   "kernel time, traced pass"))
+
+
+def config_step(torch, name, steps, warmup):
+    """The whole-partition step of another workload's shard (same schedule
+    as the headline): ms per step and algorithmic TFLOP/s."""
+    from token_transformer_layer_amd import synth
+    from token_transformer_layer_amd.shard import ShardLayer
+    sh = synth.CONFIGS[name]
+    x, dy = synth.activations(sh)
+    L = ShardLayer(sh, synth.shard_params_direct(sh, "standard", 0))
+    bufs = dict(x=L.act(x), dy=L.act(dy), h_mid=L.act(), y=L.act(), dh=L.act(), dx=L.act(), p_attn=L.f32(),
+                p_mlp=L.f32(), p_du2=L.f32(), p_du1=L.f32())
+    L.new_step()
+    ms, _, _ = time_steps(torch, make_step(L, bufs, "whole"), steps, warmup)
+    g_fl, a_fl = step_flops(sh)
+    tf = (g_fl + a_fl) / (ms * 1e-3) / 1e12
+    out = dict(ms_per_step=round(ms, 4), tflops=round(tf, 1), frac_of_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4),
+               gflop_per_step=round((g_fl + a_fl) / 1e9, 1),
+               shape="h %d, %d x %d heads, t %d, batch %d, seq %d, slices %s" % (
+                   sh.hidden, sh.heads, sh.head_dim, sh.tp, sh.batch, sh.seq, list(sh.slices)))
+    del L, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_cpu():
+    """The host's logical CPU count and model name (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count(), model
 
 
 def cube_block(torch, steps, warmup):
@@ -557,14 +624,14 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        ps_ms, _, _ = time_steps(torch, make_step(layer, bufs, "per-slice"), max(3, args.steps // 2), 2)
-        extra["per_slice_calls"] = dict(ms_per_step=round(ps_ms, 4),
-                                        tflops=round(total / (ps_ms * 1e-3) / 1e12, 1))
+        extra["per_slice_calls"] = per_slice_figures(torch, layer, bufs, max(3, args.steps // 2), 2)
         extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
         extra["cube_ffn_backward"] = cube_backward(torch, max(3, args.steps // 2), 2)
         extra["sequence_parallel_step"] = sequence_parallel_step(torch, layer, bufs, max(3, args.steps // 2), 2)
         extra["ring_attention_block"] = ring_block(torch, max(3, args.steps // 2), 2)
         extra["terapipe_slicing"] = terapipe_plan(layer, bufs, stages=8)
+        extra["other_workloads"] = {n: config_step(torch, n, max(5, args.steps // 2), 3)
+                                    for n in ("gpt13b-t8", "medium-bf16") if n != shape.name}
 
     out = {
         "metric": "shard-layer fwd+bwd TFLOP/s, GPT-3 175B t=8 shard, one MI355X",
