@@ -320,9 +320,9 @@ tp_status tp_cube_gelu_backward(int32_t rows, int32_t n, const float *dh, const 
                                 float *dbias, int32_t accumulate, void *work, void *stream);
 
 /* Attention with the keys split into blocks ("Transformer Training 11:
- * model parallelism", the passage on very long sequences: a device keeps its
- * own queries and receives every device's keys and values, passed round a
- * ring while it computes).  One call takes the device's queries against one
+ * model parallelism", the passage after the sequence-parallelism slide on
+ * very long sequences, where the key/value blocks travel between devices and
+ * the queries stay put).  One call takes the device's queries against one
  * block of keys and values; tp_attn_merge combines the results of two
  * disjoint blocks into the result over their union (log-sum-exp rule), so
  * merging the results of all blocks gives causal attention over all keys.

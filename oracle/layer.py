@@ -50,7 +50,7 @@ __all__ = [
     "layer_norm", "layer_norm_backward",
     "heads_split", "heads_merge",
     "causal_attention", "causal_attention_backward",
-    "attention_block", "merge_partials",
+    "attention_block", "merge_partials", "attention_block_backward",
     "layer_forward", "layer_backward",
     "shard_params", "new_kv_cache", "new_kv_grad",
     "shard_attn_forward", "shard_mlp_forward",
@@ -190,12 +190,13 @@ def causal_attention_backward(do, q, k, v, p, o):
 
 # ----------------------------------------------------------------------------
 # Attention over one block of keys and values, and the merge of two partial
-# results ([TT11], the passage on very long sequences: each device keeps its
-# own queries and receives every device's keys and values, passed round a
-# ring while it computes).  A device therefore sees the keys one block at a
-# time; the exact result over all keys follows from the per-block results by
-# the log-sum-exp identity (a reading: the pages do not spell out how blocks
-# are combined, and exact attention over the union is the plainest one).
+# results ([TT11], the passage after the sequence-parallelism slide on very
+# long sequences: the queries stay on their device while the key/value blocks
+# of all devices circulate between them).  A device therefore sees the keys
+# one block at a time; the exact result over all keys follows from the
+# per-block results by the log-sum-exp identity (a reading: the pages do not
+# spell out how blocks are combined, and exact attention over the union is
+# the plainest one).  The backward of one block takes the merged result.
 # ----------------------------------------------------------------------------
 
 def attention_block(q, k, v, q_pos0, k_pos0):
@@ -247,6 +248,38 @@ def merge_partials(o_a, lse_a, o_b, lse_b):
     o = (w_a[..., None] * o_a + w_b[..., None] * o_b) / tot_safe[..., None]
     lse = np.where(empty, -np.inf, m_safe + np.log(tot_safe))
     return o, lse
+
+
+def attention_block_backward(do, q, k, v, o, lse, q_pos0, k_pos0):
+    """Backward of attention_block for one key block, given the result over
+    all blocks: o and lse are the merged output and log-sum-exp of each
+    query (over every key it sees, in any block) and do the gradient of o.
+
+    On the block's visible keys the full softmax is P_pj = exp(S_pj - lse_p)
+    (S_pj = q_p . k_j / sqrt(d)); with D_p = rowsum(do_p * o_p) the
+    gradients of the two products and the softmax (as in
+    causal_attention_backward) restricted to the block are dV = P^T do,
+    dP = do V^T, dS = P * (dP - D), dq = dS K / sqrt(d) (this block's share
+    of the query gradient) and dK = dS^T q / sqrt(d).  Summed over all
+    blocks the shares give the full dQ, and each block's dK, dV are the full
+    gradients of its keys.  Returns (dq_share, dk, dv)."""
+    do, q, k, v, o = (np.asarray(a, dtype=np.float64) for a in (do, q, k, v, o))
+    lse = np.asarray(lse, dtype=np.float64)
+    d = q.shape[-1]
+    lq, lk = q.shape[-2], k.shape[-2]
+    scores = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(d)
+    pos_q = q_pos0 + np.arange(lq)
+    pos_k = k_pos0 + np.arange(lk)
+    visible = (pos_k[None, :] <= pos_q[:, None]) & np.isfinite(lse)[..., None]
+    lse_safe = np.where(np.isfinite(lse), lse, 0.0)[..., None]
+    p = np.where(visible, np.exp(np.where(visible, scores, 0.0) - lse_safe), 0.0)
+    dv = np.swapaxes(p, -1, -2) @ do
+    dp = do @ np.swapaxes(v, -1, -2)
+    row_dot = (do * o).sum(axis=-1, keepdims=True)
+    ds = p * (dp - row_dot)
+    dq = (ds @ k) / math.sqrt(d)
+    dk = (np.swapaxes(ds, -1, -2) @ q) / math.sqrt(d)
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

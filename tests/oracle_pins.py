@@ -314,3 +314,49 @@ def ring_error(orc, seed=5):
         rev = (o, lse) if rev is None else orc.merge_partials(rev[0], rev[1], o, lse)
     err = max(err, float(np.abs(rev[0] - acc[0]).max()), float(np.abs(rev[1] - acc[1]).max()))
     return err
+
+
+def ring_backward_error(orc, seed=7):
+    """Largest deviation of attention_block_backward, run block by block with
+    the merged forward result (o, lse taken from the brute force over all
+    keys), from central finite differences of L = sum(do * o) through the
+    pure-Python brute-force forward: the per-block query shares summed over
+    the blocks against dL/dq, each block's dk and dv against dL/dk and dL/dv
+    of its keys.  Blocks before, across and after the queries."""
+    rng = np.random.default_rng(seed)
+    b, n, d = 1, 2, 4
+    q_pos0, lq = 4, 3
+    lk_total = q_pos0 + lq + 1
+    q = rng.normal(size=(b, n, lq, d))
+    k = rng.normal(size=(b, n, lk_total, d))
+    v = rng.normal(size=(b, n, lk_total, d))
+    do = rng.normal(size=(b, n, lq, d))
+
+    def loss(qq, kk, vv):
+        o, _ = brute_block_attention(qq.tolist(), kk.tolist(), vv.tolist(), q_pos0, 0)
+        return float((np.array(o) * do).sum())
+
+    fo, fl = brute_block_attention(q.tolist(), k.tolist(), v.tolist(), q_pos0, 0)
+    fo, fl = np.array(fo), np.array(fl)
+    blocks = [(0, 3), (3, 6), (6, lk_total)]
+    dq = np.zeros_like(q)
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    for k0, k1 in blocks:
+        sq, sk, sv = orc.attention_block_backward(do, q, k[:, :, k0:k1], v[:, :, k0:k1], fo, fl, q_pos0, k0)
+        dq += sq
+        dk[:, :, k0:k1] = sk
+        dv[:, :, k0:k1] = sv
+    eps = 1e-6
+    err = 0.0
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(arr.shape):
+            args = {"q": q, "k": k, "v": v}
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args[name] = plus
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = minus
+            lm = loss(args["q"], args["k"], args["v"])
+            err = max(err, abs((lp - lm) / (2 * eps) - grad[idx]))
+    return err

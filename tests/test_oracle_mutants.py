@@ -52,6 +52,13 @@ MUTANTS = [
     ("merge_partials", "lse = np.where(empty, -np.inf, m_safe + np.log(tot_safe))", "lse = np.where(empty, -np.inf, m_safe)"),
     ("merge_partials", "w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - m_safe))",
      "w_b = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_a - m_safe))"),
+    ("attention_block_backward", "ds = p * (dp - row_dot)", "ds = p * dp"),
+    ("attention_block_backward", "pos_k = k_pos0 + np.arange(lk)", "pos_k = np.arange(lk)"),
+    ("attention_block_backward", "dk = (np.swapaxes(ds, -1, -2) @ q) / math.sqrt(d)",
+     "dk = (np.swapaxes(ds, -1, -2) @ q)"),
+    ("attention_block_backward", "dv = np.swapaxes(p, -1, -2) @ do", "dv = np.swapaxes(p, -1, -2) @ o"),
+    ("attention_block_backward", "np.exp(np.where(visible, scores, 0.0) - lse_safe)",
+     "np.exp(np.where(visible, scores, 0.0))"),
 ]
 
 
@@ -68,6 +75,7 @@ def _pin_failures(orc):
         ("slices", lambda: pins.tp_error(orc, 2, [2, 1, 3]) < 1e-12),
         ("cube", lambda: pins.cube_error(orc) < 1e-12),
         ("ring", lambda: pins.ring_error(orc) < 1e-12),
+        ("ring-backward", lambda: pins.ring_backward_error(orc) < 1e-7),
     ]
     for name, ok in checks:
         with np.errstate(all="ignore"):

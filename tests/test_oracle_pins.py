@@ -116,3 +116,21 @@ def test_attention_block_special_cases():
     o1, l1 = oracle.attention_block(q, k, v, q_pos0=4, k_pos0=4)
     assert np.allclose(o1[..., 0, :], v[..., 0, :], atol=1e-15)
     assert np.allclose(l1[..., 0], (q[..., 0, :] * k[..., 0, :]).sum(-1) / 2.0, atol=1e-15)
+
+
+def test_attention_block_backward_matches_finite_differences():
+    """Per-block backward with the merged forward result, summed over a ring
+    of blocks, against finite differences of the brute-force forward."""
+    assert pins.ring_backward_error(oracle) < 1e-7
+
+
+def test_attention_block_backward_single_block_is_causal_backward():
+    """One block holding every key from position 0 is plain causal attention:
+    its backward equals causal_attention_backward."""
+    rng = np.random.default_rng(9)
+    q, k, v, do = (rng.normal(size=(2, 3, 5, 8)) for _ in range(4))
+    o, p, lse = oracle.causal_attention(q, k, v)
+    ref = oracle.causal_attention_backward(do, q, k, v, p, o)
+    got = oracle.attention_block_backward(do, q, k, v, o, lse, 0, 0)
+    for a, b in zip(got, ref):
+        assert np.abs(a - b).max() < 1e-12
