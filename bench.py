@@ -491,7 +491,8 @@ def cube_backward(torch, steps, warmup):
 def ring_block(torch, steps, warmup):
     """Attention over key/value blocks (long-context shape: 4096 queries of 12
     heads of 128 against a 4096-key block of an earlier device, and against
-    their own diagonal block), and the merge of two partial results."""
+    their own diagonal block), its per-block backward, and the merge of two
+    partial results."""
     from token_transformer_layer_amd import abi, synth
     b, n, d, L = 1, 12, 128, 4096
     g = torch.Generator(device="cpu").manual_seed(1006)
@@ -508,6 +509,24 @@ def ring_block(torch, steps, warmup):
             abi.tp_attn_block_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), st)
         ms, _, _ = time_steps(torch, step, steps, warmup)
         tf = 4.0 * d * pairs * b * n / (ms * 1e-3) / 1e12
+        out[name] = dict(ms=round(ms, 4), tflops=round(tf, 1), frac=round(tf / PEAK_BF16_TFLOPS, 4))
+    # the per-block backward (dQ share, dK, dV) of the same blocks, each taken
+    # as the only block (its own forward is the merged result)
+    do = torch.randn((b, n, L, d), generator=g).to("cuda", torch.bfloat16)
+    dq = torch.empty((b, n, L, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    for name, qp, kp, pairs in [("backward_off_diagonal", L, 0, float(L) * L),
+                                ("backward_diagonal", L, L, L * (L + 1) / 2.0)]:
+        shape = abi.tp_attn_block_shape(b, n, d, L, L, qp, kp)
+        abi.tp_attn_block_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), st)
+        work = torch.empty(abi.tp_attn_block_bwd_work_bytes(shape), dtype=torch.uint8, device="cuda")
+
+        def bstep():
+            abi.tp_attn_block_bwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), False, work.data_ptr(),
+                                  st)
+        ms, _, _ = time_steps(torch, bstep, steps, warmup)
+        tf = 8.0 * d * pairs * b * n / (ms * 1e-3) / 1e12  # algorithmic: twice the forward's 4 d per pair
         out[name] = dict(ms=round(ms, 4), tflops=round(tf, 1), frac=round(tf / PEAK_BF16_TFLOPS, 4))
     shape = abi.tp_attn_block_shape(b, n, d, L, L, 0, 0)
 

@@ -355,6 +355,28 @@ tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, con
 tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, const float *lse_a,
                         const float *o_b, const float *lse_b, float *o, float *lse, void *stream);
 
+/* Backward of tp_attn_block_fwd for one key block, given the result over
+ * every block (ring attention's backward step, same passage): o and lse are
+ * the merged output and log-sum-exp of each query over all its keys (as
+ * tp_attn_merge leaves them, fp32 [batch, heads, nq, head_dim] and [batch,
+ * heads, nq]) and dout (bf16, shaped like q) the gradient of o.  With
+ * P = exp(score - lse) on the block's visible keys and D = rowsum(dout * o):
+ *   dq (fp32, shaped like q)  = this block's share of the query gradient,
+ *                               (P * (dout v^T - D)) k / sqrt(head_dim);
+ *   dk, dv (fp32, shaped like k and v) = the gradients of the block's keys
+ *                               and values from these queries.
+ * Summing dq over all blocks gives the full query gradient.  accumulate = 0
+ * stores dq, dk and dv, accumulate = 1 adds to them (a ring sums dq over
+ * blocks and dk, dv over the devices the block visits).  A query whose lse is
+ * -inf (it sees no key) takes no gradient.  work: device memory of
+ * tp_attn_block_bwd_work_bytes(shape) bytes (rowsum(dout * o)); every
+ * pointer 16-byte aligned; same shape limits as tp_attn_block_fwd. */
+size_t tp_attn_block_bwd_work_bytes(const tp_attn_block_shape *shape);
+tp_status tp_attn_block_bwd(const tp_attn_block_shape *shape, const void *q, const void *k,
+                            const void *v, const float *o, const float *lse, const void *dout,
+                            float *dq, float *dk, float *dv, int32_t accumulate, void *work,
+                            void *stream);
+
 /* Token-slicing plan of a token-level pipeline ("TeraPipe: Token-Level
  * Pipeline Parallelism ...", section 3, selecting the slicing scheme).
  * Host functions: every pointer is host memory; nothing is enqueued.

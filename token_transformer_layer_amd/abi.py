@@ -24,7 +24,8 @@ EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fw
             "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table",
             "tp_cube_matmul", "tp_cube_bias_gelu", "tp_cube_work_bytes", "tp_cube_gelu_backward",
             "tp_layernorm_work_bytes", "tp_layernorm_fwd", "tp_layernorm_bwd", "tp_trace_enable", "tp_trace_read",
-            "tp_gemm_force_tile", "tp_last_error", "tp_shard_layer_fwd_noalloc", "tp_noalloc_scratch_bytes"]
+            "tp_gemm_force_tile", "tp_last_error", "tp_shard_layer_fwd_noalloc", "tp_noalloc_scratch_bytes",
+            "tp_attn_block_bwd_work_bytes", "tp_attn_block_bwd"]
 
 
 class TPError(RuntimeError):
@@ -109,6 +110,10 @@ def lib():
     L.tp_attn_block_fwd.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp]
     L.tp_attn_block_fwd.restype = ctypes.c_int
     L.tp_attn_merge.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp, vp]
+    L.tp_attn_block_bwd_work_bytes.argtypes = [P(tp_attn_block_shape)]
+    L.tp_attn_block_bwd_work_bytes.restype = ctypes.c_size_t
+    L.tp_attn_block_bwd.argtypes = [P(tp_attn_block_shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    L.tp_attn_block_bwd.restype = ctypes.c_int
     L.tp_attn_merge.restype = ctypes.c_int
     L.tp_layernorm_work_bytes.argtypes = [P(tp_shard_cfg), i64]
     L.tp_layernorm_work_bytes.restype = ctypes.c_size_t
@@ -206,6 +211,15 @@ def tp_cube_ffn_block(rows, hidden, ffn, x, w1, b1, w2, hbuf, out, stream):
 
 def tp_attn_block_fwd(shape, q, k, v, o, lse, stream):
     _check(lib().tp_attn_block_fwd(ctypes.byref(shape), q, k, v, o, lse, stream))
+
+
+def tp_attn_block_bwd_work_bytes(shape):
+    return lib().tp_attn_block_bwd_work_bytes(ctypes.byref(shape))
+
+
+def tp_attn_block_bwd(shape, q, k, v, o, lse, dout, dq, dk, dv, accumulate, work, stream):
+    _check(lib().tp_attn_block_bwd(ctypes.byref(shape), q, k, v, o, lse, dout, dq, dk, dv, 1 if accumulate else 0,
+                                   work, stream))
 
 
 def tp_attn_merge(shape, o_a, lse_a, o_b, lse_b, o, lse, stream):

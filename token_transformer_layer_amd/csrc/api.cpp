@@ -615,6 +615,42 @@ tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, cons
                       "attention merge");
 }
 
+size_t tp_attn_block_bwd_work_bytes(const tp_attn_block_shape *shape) {
+    if (check_block(shape) != TP_OK) return 0;
+    const size_t n = attn_block_bwd_work_floats(shape->batch * shape->heads, shape->nq) * sizeof(float);
+    return n > 0 ? (n + 255) / 256 * 256 : 256;
+}
+
+tp_status tp_attn_block_bwd(const tp_attn_block_shape *shape, const void *q, const void *k, const void *v,
+                            const float *o, const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                            int32_t accumulate, void *work, void *stream) {
+    tp_status s = check_block(shape);
+    if (s != TP_OK) return s;
+    if (accumulate != 0 && accumulate != 1) return fail(TP_EINVAL, "accumulate must be 0 or 1");
+    NEED(q, "q");
+    NEED(k, "k");
+    NEED(v, "v");
+    NEED(o, "o");
+    NEED(lse, "lse");
+    NEED(dout, "dout");
+    NEED(dq, "dq");
+    NEED(dk, "dk");
+    NEED(dv, "dv");
+    NEED(work, "work");
+    AttnBlockBwdArgs a{};
+    a.bh = shape->batch * shape->heads;
+    a.nq = shape->nq;
+    a.nk = shape->nk;
+    a.d = shape->head_dim;
+    a.q_pos0 = shape->q_pos0;
+    a.k_pos0 = shape->k_pos0;
+    a.accumulate = accumulate != 0;
+    a.scale = 1.0f / std::sqrt((float)shape->head_dim);
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.work = (float *)work;
+    return hip_status(attn_block_bwd(a, (hipStream_t)stream), "block attention backward");
+}
+
 tp_status tp_cube_matmul(int32_t form, int32_t M, int32_t N, int32_t K, const void *a, const void *b, float *c,
                          int32_t accumulate, void *stream) {
     if (form < TP_CUBE_AB || form > TP_CUBE_ATB) return fail(TP_EINVAL, "form %d is not a tp_cube_form", form);

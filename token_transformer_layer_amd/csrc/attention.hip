@@ -1144,6 +1144,283 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (g == 0) a.lse[(int64_t)bh * a.nq + my_lq] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Backward of attention over one key block (the per-block step of ring
+// attention's backward): queries at positions q_pos0.., keys at k_pos0..,
+// with the merged forward result's log-sum-exp and rowsum(dO * O) of every
+// query.  Two kernels as for the prefix form: per 128 keys (dK, dV, looping
+// over the query tiles that see them; K and V in registers, Q and dO tiles
+// through LDS, three stages) and per 128 queries (this block's share of dQ,
+// looping over the visible key tiles).  Results are fp32, stored or added to
+// the caller's buffers (a ring sums dQ shares over blocks and dK, dV over
+// devices).  A query whose merged log-sum-exp is -inf sees no key anywhere
+// and takes no gradient.
+// ---------------------------------------------------------------------------
+
+struct AttnBlockBwdP {
+    int nq, nk, q_pos0, k_pos0, accumulate;
+    float scale;
+    const bf16 *q, *k, *v, *dout;   // q, dout [bh][nq][D]; k, v [bh][nk][D]
+    const float *o;                 // merged O [bh][nq][D]
+    const float *lse;               // merged log-sum-exp [bh][nq]
+    float *delta;                   // rowsum(dO * O) [bh][nq]
+    float *dq, *dk, *dv;            // dq [bh][nq][D]; dk, dv [bh][nk][D]
+    uint32_t q_bytes, kv_bytes;
+};
+
+// log2-domain log-sum-exp of a query for P = exp2(s * scale * log2 e - it):
+// +inf for a query that sees no key (so P = 0)
+__device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// delta[row] = sum_j dO[row][j] O[row][j]; D/8 lanes per row, 8 columns each
+template <int D>
+__global__ __launch_bounds__(256) void attn_block_delta(int64_t rows, const bf16 *__restrict__ dout,
+                                                        const float *__restrict__ o, float *__restrict__ delta) {
+    constexpr int LPG = D / 8;
+    const int64_t row = (blockIdx.x * 256LL + threadIdx.x) / LPG;
+    const int part = threadIdx.x % LPG;
+    float s = 0.f;
+    if (row < rows) {
+        float x[8], y[8];
+        load8(dout + row * D + part * 8, x);
+        load8(o + row * D + part * 8, y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += x[j] * y[j];
+    }
+#pragma unroll
+    for (int m = LPG / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, 64);
+    if (row < rows && part == 0) delta[row] = s;
+}
+
+// fp32 result rows: stored, or added to what the buffer holds
+__device__ __forceinline__ void put4(float *p, f32x4 v, bool add) {
+    if (add) v += *(const f32x4 *)p;
+    *(f32x4 *)p = v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_block_bwd_dkdv_mfma32(AttnBlockBwdP a) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE = 64 * D * 2;
+    constexpr int STAGE = 2 * TILE + 1024;  // Q, dO, lse (log2 units) and delta of 64 queries
+    constexpr int NST = kBwdKvStages;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
+    const int bh = blockIdx.y;
+    const int kb0 = blockIdx.x * kBwdBK;  // first key (block-local index) of the workgroup
+    const int kw0 = kb0 + w * 32;
+    const int my_k = kw0 + li;
+    const bool kok = my_k < a.nk;
+    const int my_kpos = a.k_pos0 + my_k;
+    const int64_t qslab = (int64_t)bh * a.nq * D, kslab = (int64_t)bh * a.nk * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+
+    // B operands of S = Q K^T and dP = dO V^T: lane holds key my_k, d = 16 s + 8 g + j
+    bf16x8 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint32_t off = kok ? (uint32_t)((kslab + (int64_t)my_k * D + s * 16 + g * 8) * 2) : kOOB;
+        kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+        vreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+    }
+    f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) { acc_dk[i] = f32x16{}; acc_dv[i] = f32x16{}; }
+
+    // the first query (block-local) that sees a key of this workgroup
+    const int qstart = max(0, a.k_pos0 + kb0 - a.q_pos0);
+    const int nqt = qstart < a.nq ? (a.nq - qstart + 63) / 64 : 0;
+    const int64_t stat0 = (int64_t)bh * a.nq;
+
+    auto issue = [&](int t, char *st) {
+        const int p0 = qstart + t * 64;
+        rows_tile_dma<D>(rq, st, qslab, D, p0, a.nq, w, lane);
+        rows_tile_dma<D>(rdo, st + TILE, qslab, D, p0, a.nq, w, lane);
+    };
+    float stat = 0.f;
+    auto load_stat = [&](int t) {
+        if (tid < 128) {
+            const int p = qstart + t * 64 + (tid & 63);
+            stat = p < a.nq ? (tid < 64 ? lse2_of(a.lse[stat0 + p]) : a.delta[stat0 + p]) : 0.f;
+        }
+    };
+    auto store_stat = [&](char *st) {
+        if (tid < 128) ((float *)(st + 2 * TILE))[tid] = stat;
+    };
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t) {
+        if (t < nqt) {
+            load_stat(t);
+            issue(t, smem + t * STAGE);
+            store_stat(smem + t * STAGE);
+        }
+    }
+    for (int t = 0; t < nqt; ++t) {
+        if (t + 1 < nqt) wait_vmcnt<kBwdTileLoads<D>>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        const char *st = smem + (t % NST) * STAGE;
+        char *nx = smem + ((t + NST - 1) % NST) * STAGE;
+        if (t + NST - 1 < nqt) {
+            load_stat(t + NST - 1);
+            issue(t + NST - 1, nx);
+        }
+        const int p0 = qstart + t * 64;
+        const float *lse_s = (const float *)(st + 2 * TILE);
+        const float *del_s = lse_s + 64;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int qr0 = p0 + qb * 32;
+            if (a.q_pos0 + qr0 + 31 < a.k_pos0 + kw0) continue;  // every query precedes every key of this wave
+            f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = kv_chunk_off<D>(qb * 32 + li, 2 * s + g);
+                sc = mfma32(*(const bf16x8 *)(st + off), kreg[s], sc);
+                dp = mfma32(*(const bf16x8 *)(st + TILE + off), vreg[s], dp);
+            }
+            // register v: query qr0 + 8(v/4) + 4g + v%4, key my_k
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ql = qb * 32 + 8 * r + 4 * g;
+                const f32x4 l4 = *(const f32x4 *)(lse_s + ql);
+                const f32x4 d4 = *(const f32x4 *)(del_s + ql);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int q = p0 + ql + u;
+                    const bool vis = kok && q < a.nq && my_kpos <= a.q_pos0 + q;
+                    const float pr = vis ? __builtin_amdgcn_exp2f(sc[4 * r + u] * sl2 - l4[u]) : 0.f;
+                    sc[4 * r + u] = pr;
+                    dp[4 * r + u] = pr * (dp[4 * r + u] - d4[u]);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8 pb = pack_half(sc, h), sb = pack_half(dp, h);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    acc_dv[db] = mfma32(tr_frag<D>(st + TILE, qb * 32 + 16 * h, db, lane), pb, acc_dv[db]);
+                    acc_dk[db] = mfma32(tr_frag<D>(st, qb * 32 + 16 * h, db, lane), sb, acc_dk[db]);
+                }
+            }
+        }
+        if (t + NST - 1 < nqt) store_stat(nx);
+    }
+    if (!kok) return;
+    float *pk = a.dk + kslab + (int64_t)my_k * D, *pv = a.dv + kslab + (int64_t)my_k * D;
+    const bool add = a.accumulate != 0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = db * 32 + 8 * r + 4 * g;
+            put4(pk + j, f32x4{acc_dk[db][4 * r], acc_dk[db][4 * r + 1], acc_dk[db][4 * r + 2],
+                               acc_dk[db][4 * r + 3]} * a.scale, add);
+            put4(pv + j, f32x4{acc_dv[db][4 * r], acc_dv[db][4 * r + 1], acc_dv[db][4 * r + 2],
+                               acc_dv[db][4 * r + 3]}, add);
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_block_bwd_dq_mfma32(
+    AttnBlockBwdP a) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE = 64 * D * 2;
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, li = lane & 31;
+    const int bh = blockIdx.y;
+    const int lq0 = blockIdx.x * kBwdBQ;
+    const int my_q = lq0 + w * 32 + li;  // block-local query
+    const bool qok = my_q < a.nq;
+    const int q_pos = a.q_pos0 + min(my_q, a.nq - 1);
+    // keys after the workgroup's last query position are never seen
+    const int last_pos = a.q_pos0 + min(lq0 + kBwdBQ - 1, a.nq - 1);
+    const int kend = max(0, min(a.nk, last_pos - a.k_pos0 + 1));
+    const int ntiles = (kend + 63) / 64;
+    const int64_t qslab = (int64_t)bh * a.nq * D, kslab = (int64_t)bh * a.nk * D;
+    const float sl2 = a.scale * kLog2e;
+
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout, a.q_bytes);
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k, a.kv_bytes);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v, a.kv_bytes);
+
+    // B operands of S^T = K Q^T and dP^T = V dO^T: lane holds query my_q, d = 16 s + 8 g + j
+    bf16x8 qreg[KS], doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const uint32_t off = qok ? (uint32_t)((qslab + (int64_t)my_q * D + s * 16 + g * 8) * 2) : kOOB;
+        qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+        doreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+    }
+    const float lse2 = qok ? lse2_of(a.lse[(int64_t)bh * a.nq + my_q]) : INFINITY;
+    const float del = qok ? a.delta[(int64_t)bh * a.nq + my_q] : 0.f;
+    f32x16 acc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+    if (ntiles > 0) {
+        kv_tile_dma<D>(rk, smem, kslab, 0, kend, w, lane);
+        kv_tile_dma<D>(rv, smem + TILE, kslab, 0, kend, w, lane);
+    }
+    const int wave_last_pos = a.q_pos0 + lq0 + w * 32 + 31;
+    for (int t = 0; t < ntiles; ++t) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        const char *ks = smem + (t & 1) * 2 * TILE;
+        const char *vs = ks + TILE;
+        if (t + 1 < ntiles) {
+            char *nx = smem + ((t + 1) & 1) * 2 * TILE;
+            kv_tile_dma<D>(rk, nx, kslab, (t + 1) * 64, kend, w, lane);
+            kv_tile_dma<D>(rv, nx + TILE, kslab, (t + 1) * 64, kend, w, lane);
+        }
+        const int key0 = t * 64;  // block-local
+        if (a.k_pos0 + key0 > wave_last_pos) continue;  // every key of the tile is after this wave's queries
+        bf16x8 sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 sc = f32x16{}, dp = f32x16{};
+            const int row = kb * 32 + li;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int off = kv_chunk_off<D>(row, 2 * s + g);
+                sc = mfma32(*(const bf16x8 *)(ks + off), qreg[s], sc);
+                dp = mfma32(*(const bf16x8 *)(vs + off), doreg[s], dp);
+            }
+            // register v: key key0 + 32 kb + 8(v/4) + 4g + v%4, query my_q
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int kl = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
+                const bool vis = kl < kend && a.k_pos0 + kl <= q_pos;
+                const float pr = vis ? __builtin_amdgcn_exp2f(sc[v] * sl2 - lse2) : 0.f;
+                dp[v] = pr * (dp[v] - del);
+            }
+            sb[2 * kb] = pack_half(dp, 0);
+            sb[2 * kb + 1] = pack_half(dp, 1);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) acc[db] = mfma32(tr_frag<D>(ks, 16 * k4, db, lane), sb[k4], acc[db]);
+    }
+    if (!qok) return;
+    float *pq = a.dq + qslab + (int64_t)my_q * D;
+    const bool add = a.accumulate != 0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            put4(pq + db * 32 + 8 * r + 4 * g,
+                 f32x4{acc[db][4 * r], acc[db][4 * r + 1], acc[db][4 * r + 2], acc[db][4 * r + 3]} * a.scale, add);
+}
+
 // o = (w_a o_a + w_b o_b) / (w_a + w_b), lse = m + log(w_a + w_b) with
 // m = max(lse_a, lse_b) and w_x = exp(lse_x - m) (0 for lse_x = -inf); D/8
 // threads per row, each on 8 columns (a row's threads share one wave, so the
@@ -1437,6 +1714,62 @@ hipError_t attn_merge(int64_t rows, int d, const float *oa, const float *la, con
     const int64_t threads = rows * (d / 8);
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, rows, d, oa, la,
                        ob, lb, o, lse);
+    return hipGetLastError();
+}
+
+size_t attn_block_bwd_work_floats(int bh, int nq) { return (size_t)bh * (size_t)(nq > 0 ? nq : 0); }
+
+hipError_t attn_block_bwd(const AttnBlockBwdArgs &x, hipStream_t st) {
+    if (x.bh <= 0) return hipSuccess;
+    AttnBlockBwdP p{};
+    p.nq = x.nq; p.nk = x.nk; p.q_pos0 = x.q_pos0; p.k_pos0 = x.k_pos0; p.accumulate = x.accumulate ? 1 : 0;
+    p.scale = x.scale;
+    p.q = (const bf16 *)x.q; p.k = (const bf16 *)x.k; p.v = (const bf16 *)x.v; p.dout = (const bf16 *)x.dout;
+    p.o = x.o; p.lse = x.lse; p.delta = x.work; p.dq = x.dq; p.dk = x.dk; p.dv = x.dv;
+    p.q_bytes = (uint32_t)((int64_t)x.bh * x.nq * x.d * 2);
+    p.kv_bytes = (uint32_t)((int64_t)x.bh * x.nk * x.d * 2);
+    const int64_t rows = (int64_t)x.bh * x.nq;
+    if (rows > 0) {
+        TraceScope ts(st, "attn_block_delta", 2.0 * x.d * rows, (double)rows * x.d * 6 + 4.0 * rows);
+        const unsigned grid = (unsigned)((rows * (x.d / 8) + 255) / 256);
+        if (x.d == 128) hipLaunchKernelGGL(attn_block_delta<128>, dim3(grid), dim3(256), 0, st, rows, p.dout, p.o, p.delta);
+        else hipLaunchKernelGGL(attn_block_delta<64>, dim3(grid), dim3(256), 0, st, rows, p.dout, p.o, p.delta);
+    }
+    AttnBlockArgs fw{};
+    fw.bh = x.bh; fw.nq = x.nq; fw.nk = x.nk; fw.d = x.d; fw.q_pos0 = x.q_pos0; fw.k_pos0 = x.k_pos0;
+    const double pairs = block_pairs(fw);
+    const int tile = 64 * x.d * 2;
+    const int lds_kv = kBwdKvStages * (2 * tile + 1024), lds_q = 2 * 2 * tile;
+    // dK/dV: workgroups of 128 keys (every key block, also one that no query
+    // sees: its gradients are zero and are stored or added as such)
+    if (x.nk > 0) {
+        TraceScope ts(st, "attn_block_bwd_dkdv_bf16", 8.0 * x.d * pairs,
+                      (double)x.bh * x.d * (4.0 * x.nk + 4.0 * x.nq + 8.0 * x.nk));
+        dim3 grid((x.nk + kBwdBK - 1) / kBwdBK, x.bh);
+        if (x.d == 128) {
+            hipFuncSetAttribute((const void *)attn_block_bwd_dkdv_mfma32<128>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+            hipLaunchKernelGGL(attn_block_bwd_dkdv_mfma32<128>, grid, dim3(256), lds_kv, st, p);
+        } else {
+            hipFuncSetAttribute((const void *)attn_block_bwd_dkdv_mfma32<64>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+            hipLaunchKernelGGL(attn_block_bwd_dkdv_mfma32<64>, grid, dim3(256), lds_kv, st, p);
+        }
+    }
+    if (x.nq > 0) {
+        TraceScope ts(st, "attn_block_bwd_dq_bf16", 6.0 * x.d * pairs,
+                      (double)x.bh * x.d * (4.0 * x.nq + 4.0 * x.nk + 4.0 * x.nq));
+        dim3 grid((x.nq + kBwdBQ - 1) / kBwdBQ, x.bh);
+        if (x.d == 128) {
+            hipFuncSetAttribute((const void *)attn_block_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds_q);
+            hipLaunchKernelGGL(attn_block_bwd_dq_mfma32<128>, grid, dim3(256), lds_q, st, p);
+        } else {
+            hipFuncSetAttribute((const void *)attn_block_bwd_dq_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds_q);
+            hipLaunchKernelGGL(attn_block_bwd_dq_mfma32<64>, grid, dim3(256), lds_q, st, p);
+        }
+    }
     return hipGetLastError();
 }
 

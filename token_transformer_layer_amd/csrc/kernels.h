@@ -117,6 +117,20 @@ struct AttnBlockArgs {
     float *o, *lse;
 };
 hipError_t attn_block_fwd(const AttnBlockArgs &a, hipStream_t st);
+// Backward of attention over one key block given the merged forward result
+// (o fp32 [bh, nq, d], lse [bh, nq]) and dout bf16 [bh, nq, d]: this block's
+// share of dq (fp32 [bh, nq, d]) and the block's dk, dv (fp32 [bh, nk, d]),
+// stored or (accumulate) added; work: attn_block_bwd_work_floats floats.
+struct AttnBlockBwdArgs {
+    int bh, nq, nk, d, q_pos0, k_pos0;
+    bool accumulate;
+    float scale;
+    const void *q, *k, *v, *dout;
+    const float *o, *lse;
+    float *dq, *dk, *dv, *work;
+};
+size_t attn_block_bwd_work_floats(int bh, int nq);
+hipError_t attn_block_bwd(const AttnBlockBwdArgs &a, hipStream_t st);
 // merge of two partial results over disjoint key sets (rows = bh * nq)
 hipError_t attn_merge(int64_t rows, int d, const float *oa, const float *la, const float *ob, const float *lb,
                       float *o, float *lse, hipStream_t st);
