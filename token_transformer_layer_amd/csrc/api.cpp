@@ -97,7 +97,7 @@ Saved saved_layout(const Dims &d) {
 }
 
 struct Scratch {
-    int64_t dz, dO, delta, dqkv, red, attn, split, total;
+    int64_t dz, dO, delta, dqkv, red, red_cs, attn, split, total;  // red: LayerNorm partials; red_cs: column sums
 };
 Scratch scratch_layout(const Dims &d) {
     Scratch L;
@@ -108,11 +108,12 @@ Scratch scratch_layout(const Dims &d) {
     L.delta = take(d.b * d.nt * d.s * 4);
     L.dqkv = take(d.T * 3 * d.ht * d.es);
     int64_t red = (int64_t)layernorm_bwd_partials_floats((int)d.T, (int)d.h);
-    int64_t widest = d.h;
-    if (d.ft > widest) widest = d.ft;
-    if (3 * d.ht > widest) widest = 3 * d.ht;
+    // column sums of two matrices at once: (b1, b2) or (b_o, b_qkv)
+    int64_t widest = d.ft + d.h;
+    if (d.h + 3 * d.ht > widest) widest = d.h + 3 * d.ht;
     int64_t cs = (int64_t)colsum_partials_floats((int)d.T, (int)widest);
-    L.red = take((red > cs ? red : cs) * 4);
+    L.red = take(red * 4);
+    L.red_cs = take(cs * 4);
     L.attn = take((int64_t)attn_fwd_work_floats((int)d.b, (int)d.nt, (int)d.s, (int)d.d) * 4);
     L.split = d.dt == DType::BF16 ? take((int64_t)gemm_split_workspace_floats() * 4) : off;
     L.total = off;
@@ -420,6 +421,11 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
     hipStream_t st = (hipStream_t)stream;
     const int es = d.es;
     float *red = at<float *>(scratch, S.red);
+    float *red_cs = at<float *>(scratch, S.red_cs);
+    // bias-gradient and LayerNorm-parameter reductions still to finish (their
+    // first stages leave partial sums; one launch finishes up to two)
+    ReduceSpec pend_ln{}, pend_cs{};
+    bool has_ln = false, has_cs = false;
     const Epi wepi = acc ? Epi::AccumF32 : Epi::StoreF32;  // weight-gradient epilogue
     auto fresh = [&]() {
         EpiArgs x;
@@ -460,18 +466,26 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         HIPCALL(gemm(d.dt, (int)d.ft, (int)d.h, (int)nrows, Mat{dz, d.ft, false},
                      Mat{at<const char *>(saved, L.u2 + r0 * d.h * es), d.h, false}, wepi, e, st),
                 "FC1 weight-gradient product");
-        HIPCALL(colsum(d.dt, (int)nrows, (int)d.ft, dz, d.ft, g->b1, acc, red, st), "b1 gradient");
-        HIPCALL(colsum(d.dt, (int)nrows, (int)d.h, dyr, d.h, g->b2, acc, red, st), "b2 gradient");
+        // db1 = sum of dZ and db2 = sum of dY over the rows: one column-sum
+        // launch over both matrices, one reduction
+        HIPCALL(colsum_rows(d.dt, (int)nrows, (int)d.ft, dz, d.ft, (int)d.h, dyr, d.h, red_cs, st),
+                "b1 and b2 gradients");
+        const ReduceSpec r = colsum_reduce_spec((int)nrows, (int)d.ft, (int)d.h, red_cs, g->b1, g->b2);
+        HIPCALL(reduce_partials(&r, nullptr, acc, st), "b1 and b2 gradients");
     }
     if (attn) {
         // dH = dY + LN2^T(sum_r dU2,r) (given in the sequence-parallel form);
         // dO = dH W_o; attention backward
-        if (!sp)
-            HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dyr,
-                                  at<const char *>(ln_in, r0 * d.h * es), w->ln2_g,
-                                  at<const float *>(saved, L.mu2 + r0 * 4), at<const float *>(saved, L.rs2 + r0 * 4), dhr,
-                                  g->ln2_g, g->ln2_b, acc, red, st),
+        if (!sp) {
+            // dgamma2 and dbeta2 are finished with the phase's other reductions
+            HIPCALL(layernorm_bwd_rows(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dyr,
+                                       at<const char *>(ln_in, r0 * d.h * es), w->ln2_g,
+                                       at<const float *>(saved, L.mu2 + r0 * 4),
+                                       at<const float *>(saved, L.rs2 + r0 * 4), dhr, red, st),
                     "layernorm backward (LN2)");
+            pend_ln = ln_bwd_reduce_spec((int)nrows, (int)d.h, red, g->ln2_g, g->ln2_b);
+            has_ln = true;
+        }
         e = fresh();
         e.c = dO; e.ldc = d.ht;
         HIPCALL(gemm(d.dt, (int)nrows, (int)d.ht, (int)d.h, Mat{dhr, d.h, true}, Mat{w->w_o, d.ht, false}, Epi::Store, e,
@@ -506,14 +520,20 @@ tp_status tp_shard_layer_bwd(const tp_shard_cfg *cfg, const tp_shard_weights *w,
         HIPCALL(gemm(d.dt, (int)d.h, (int)d.ht, (int)nrows, Mat{dhr, d.h, false},
                      Mat{at<const char *>(saved, L.o + r0 * d.ht * es), d.ht, false}, wepi, e, st),
                 "out-projection weight-gradient product");
-        HIPCALL(colsum(d.dt, (int)nrows, (int)d.h, dhr, d.h, g->b_o, acc, red, st), "b_o gradient");
         e = fresh();
         e.c = g->w_qkv; e.ldc = d.h;
         HIPCALL(gemm(d.dt, (int)(3 * d.ht), (int)d.h, (int)nrows, Mat{dqkv, 3 * d.ht, false},
                      Mat{at<const char *>(saved, L.u1 + r0 * d.h * es), d.h, false}, wepi, e, st),
                 "QKV weight-gradient product");
-        HIPCALL(colsum(d.dt, (int)nrows, (int)(3 * d.ht), dqkv, 3 * d.ht, g->b_qkv, acc, red, st), "b_qkv gradient");
+        // db_o = sum of dH and db_qkv = sum of dQKV: one column-sum launch
+        HIPCALL(colsum_rows(d.dt, (int)nrows, (int)d.h, dhr, d.h, (int)(3 * d.ht), dqkv, 3 * d.ht, red_cs, st),
+                "b_o and b_qkv gradients");
+        pend_cs = colsum_reduce_spec((int)nrows, (int)d.h, (int)(3 * d.ht), red_cs, g->b_o, g->b_qkv);
+        has_cs = true;
     }
+    if (has_ln || has_cs)
+        HIPCALL(reduce_partials(has_ln ? &pend_ln : nullptr, has_cs ? &pend_cs : nullptr, acc, st),
+                "attention-block parameter gradients");
     if (phase == TP_BWD_LN1) {
         HIPCALL(layernorm_bwd(d.dt, (int)nrows, (int)d.h, reduced_in + r0 * d.h, dhr,
                               at<const char *>(ln_in, r0 * d.h * es), w->ln1_g, at<const float *>(saved, L.mu1 + r0 * 4),

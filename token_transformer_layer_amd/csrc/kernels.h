@@ -71,6 +71,27 @@ hipError_t colsum(DType dt, int rows, int n, const void *a, int64_t lda, float *
                   float *partials, hipStream_t st);
 size_t colsum_partials_floats(int rows, int n);
 
+// The same two reductions split into their stages, so that one launch can
+// finish several of them: the first stage writes per-block partial sums
+// (LayerNorm: [blocks][2 h], dgamma then dbeta; column sums of one or two
+// matrices with the same rows: [chunks][n1 + n2]); a ReduceSpec names the
+// partials and their outputs (columns c < n0 to out0, the rest to out1), and
+// reduce_partials finishes up to two of them in one launch.
+struct ReduceSpec {
+    int nblk, n, n0;
+    int64_t stride;
+    const float *partials;
+    float *out0, *out1;
+};
+hipError_t layernorm_bwd_rows(DType dt, int rows, int h, const float *du, const void *resid, const void *x,
+                              const void *g, const float *mean, const float *rstd, void *dx, float *partials,
+                              hipStream_t st);
+hipError_t colsum_rows(DType dt, int rows, int n1, const void *a1, int64_t lda1, int n2, const void *a2, int64_t lda2,
+                       float *partials, hipStream_t st);
+ReduceSpec ln_bwd_reduce_spec(int rows, int h, const float *partials, float *dg, float *db);
+ReduceSpec colsum_reduce_spec(int rows, int n1, int n2, const float *partials, float *out1, float *out2);
+hipError_t reduce_partials(const ReduceSpec *a, const ReduceSpec *b, bool accumulate, hipStream_t st);
+
 // out = resid + reduced + bias[c]
 hipError_t residual_combine(DType dt, int64_t rows, int h, const void *resid, const float *reduced,
                             const void *bias, void *out, hipStream_t st);

@@ -278,16 +278,26 @@ __global__ __launch_bounds__(TPB) void ln_bwd_kernel(int rows, int h, int rpb, c
 // out[c] (+)= sum over blocks of partials[blk][c], for c < n; partial rows are
 // `stride` floats apart.  A workgroup owns 32 columns; its 8 row groups each
 // sum every 8th partial row, and the 8 sums are added in a fixed order.
-constexpr int kRedCols = 32, kRedGroups = kThreads / kRedCols;
 // Columns c < n0 go to out0[c], columns n0 <= c < n to out1[c - n0] (two
-// vectors reduced by one launch).
-__global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n, int n0, int64_t stride,
-                                                                 const float *__restrict__ partials,
-                                                                 float *__restrict__ out0, float *__restrict__ out1,
-                                                                 int accumulate) {
+// vectors reduced together).  Up to two such segments (independent partial
+// arrays) share one launch: workgroups [0, seg[0].groups) take the first.
+constexpr int kRedCols = 32, kRedGroups = kThreads / kRedCols;
+struct RedSeg {
+    int nblk, n, n0, groups;
+    int64_t stride;
+    const float *partials;
+    float *out0, *out1;
+};
+__global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(RedSeg s0, RedSeg s1, int accumulate) {
     __shared__ float part[kRedGroups][kRedCols];
+    const bool second = (int)blockIdx.x >= s0.groups;
+    const RedSeg &sg = second ? s1 : s0;
+    const int gx = second ? (int)blockIdx.x - s0.groups : (int)blockIdx.x;
     const int cx = threadIdx.x % kRedCols, gy = threadIdx.x / kRedCols;
-    const int c = blockIdx.x * kRedCols + cx;
+    const int c = gx * kRedCols + cx;
+    const int nblk = sg.nblk, n = sg.n;
+    const int64_t stride = sg.stride;
+    const float *partials = sg.partials;
     float s = 0.f;
     if (c < n) {
         int k = gy;
@@ -307,18 +317,24 @@ __global__ __launch_bounds__(kThreads) void reduce_blocks_kernel(int nblk, int n
         float t = 0.f;
 #pragma unroll
         for (int k = 0; k < kRedGroups; ++k) t += part[k][cx];
-        float *o = c < n0 ? out0 + c : out1 + (c - n0);
+        float *o = c < sg.n0 ? sg.out0 + c : sg.out1 + (c - sg.n0);
         *o = accumulate ? *o + t : t;
     }
 }
 
-// Per-chunk column sums: partials[chunk][c] = sum of a[r][c] over the rows of
-// chunk `blockIdx.y`; each thread owns 8 columns.
+// Per-chunk column sums of one or two matrices with the same rows:
+// partials[chunk][c] = sum of the chunk's rows of column c of a1 (c < n1) or
+// of column c - n1 of a2 (n1 <= c < n1 + n2), over the rows of chunk
+// `blockIdx.y`; each thread owns 8 columns of one matrix.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void colsum_kernel(int rows, int n, int64_t lda, int rpc,
-                                                          const T *__restrict__ a, float *__restrict__ partials) {
+__global__ __launch_bounds__(kThreads) void colsum_kernel(int rows, int n1, const T *__restrict__ a1, int64_t lda1,
+                                                          int n2, const T *__restrict__ a2, int64_t lda2, int rpc,
+                                                          float *__restrict__ partials) {
     const int c8 = (blockIdx.x * kThreads + threadIdx.x) * 8;
-    if (c8 >= n) return;
+    if (c8 >= n1 + n2) return;
+    const bool first = c8 < n1;
+    const T *a = first ? a1 + c8 : a2 + (c8 - n1);
+    const int64_t lda = first ? lda1 : lda2;
     const int r0 = blockIdx.y * rpc, r1 = min(rows, r0 + rpc);
     float s[8] = {};
     int r = r0;
@@ -326,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(int rows, int n, int64
     for (; r + 4 <= r1; r += 4) {
         float v[4][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) load8(a + (size_t)(r + u) * lda + c8, v[u]);
+        for (int u = 0; u < 4; ++u) load8(a + (size_t)(r + u) * lda, v[u]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -334,11 +350,11 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(int rows, int n, int64
     }
     for (; r < r1; ++r) {
         float v[8];
-        load8(a + (size_t)r * lda + c8, v);
+        load8(a + (size_t)r * lda, v);
 #pragma unroll
         for (int j = 0; j < 8; ++j) s[j] += v[j];
     }
-    store8(partials + (size_t)blockIdx.y * n + c8, s);
+    store8(partials + (size_t)blockIdx.y * (n1 + n2) + c8, s);
 }
 
 template <typename T>
@@ -478,53 +494,85 @@ static void dispatch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du,
     }
 }
 
+hipError_t layernorm_bwd_rows(DType dt, int rows, int h, const float *du, const void *resid, const void *x,
+                              const void *g, const float *mean, const float *rstd, void *dx, float *partials,
+                              hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    const int nblk = ln_bwd_blocks(rows), rpb = (rows + nblk - 1) / nblk;
+    const int es = dt == DType::BF16 ? 2 : 4;
+    TraceScope ts(st, dt == DType::BF16 ? "ln_bwd_bf16" : "ln_bwd_f32", 0.0,
+                  (double)rows * h * (4 + 3 * es) + 8.0 * rows + (double)nblk * 2 * h * 4);
+    if (dt == DType::BF16)
+        dispatch_ln_bwd<bf16>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
+    else
+        dispatch_ln_bwd<float>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
+    return hipGetLastError();
+}
+
+hipError_t colsum_rows(DType dt, int rows, int n1, const void *a1, int64_t lda1, int n2, const void *a2, int64_t lda2,
+                       float *partials, hipStream_t st) {
+    if (rows <= 0 || n1 + n2 <= 0) return hipSuccess;
+    const int nch = colsum_chunks(rows), rpc = (rows + nch - 1) / nch;
+    const int n = n1 + n2;
+    dim3 grid((n / 8 + kThreads - 1) / kThreads, nch);
+    const int es = dt == DType::BF16 ? 2 : 4;
+    TraceScope ts(st, dt == DType::BF16 ? "colsum_bf16" : "colsum_f32", (double)rows * n,
+                  (double)rows * n * es + (double)nch * n * 4);
+    if (dt == DType::BF16)
+        hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(kThreads), 0, st, rows, n1, (const bf16 *)a1, lda1, n2,
+                           (const bf16 *)a2, lda2, rpc, partials);
+    else
+        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(kThreads), 0, st, rows, n1, (const float *)a1, lda1, n2,
+                           (const float *)a2, lda2, rpc, partials);
+    return hipGetLastError();
+}
+
+ReduceSpec ln_bwd_reduce_spec(int rows, int h, const float *partials, float *dg, float *db) {
+    return ReduceSpec{ln_bwd_blocks(rows), 2 * h, h, (int64_t)2 * h, partials, dg, db};
+}
+
+ReduceSpec colsum_reduce_spec(int rows, int n1, int n2, const float *partials, float *out1, float *out2) {
+    return ReduceSpec{colsum_chunks(rows), n1 + n2, n1, (int64_t)(n1 + n2), partials, out1, out2};
+}
+
+hipError_t reduce_partials(const ReduceSpec *a, const ReduceSpec *b, bool accumulate, hipStream_t st) {
+    auto seg = [](const ReduceSpec *r) {
+        RedSeg g{};
+        if (r && r->n > 0 && r->nblk > 0) {
+            g.nblk = r->nblk; g.n = r->n; g.n0 = r->n0; g.stride = r->stride; g.partials = r->partials;
+            g.out0 = r->out0; g.out1 = r->out1; g.groups = (r->n + kRedCols - 1) / kRedCols;
+        }
+        return g;
+    };
+    RedSeg s0 = seg(a), s1 = seg(b);
+    if (s0.groups == 0) std::swap(s0, s1);
+    const int groups = s0.groups + s1.groups;
+    if (groups == 0) return hipSuccess;
+    TraceScope ts(st, "block_reduce", 0.0,
+                  ((double)s0.nblk * s0.n + (double)s1.nblk * s1.n) * 4 + 8.0 * (s0.n + s1.n) * (accumulate ? 2 : 1));
+    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(groups), dim3(kThreads), 0, st, s0, s1, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t layernorm_bwd(DType dt, int rows, int h, const float *du, const void *resid, const void *x,
                          const void *g, const float *mean, const float *rstd, void *dx, float *dg, float *db,
                          bool accumulate, float *partials, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
-    const int nblk = ln_bwd_blocks(rows), rpb = (rows + nblk - 1) / nblk;
-    const int es = dt == DType::BF16 ? 2 : 4;
-    {
-        TraceScope ts(st, dt == DType::BF16 ? "ln_bwd_bf16" : "ln_bwd_f32", 0.0,
-                      (double)rows * h * (4 + 3 * es) + 8.0 * rows + (double)nblk * 2 * h * 4);
-        if (dt == DType::BF16)
-            dispatch_ln_bwd<bf16>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
-        else
-            dispatch_ln_bwd<float>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st);
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = layernorm_bwd_rows(dt, rows, h, du, resid, x, g, mean, rstd, dx, partials, st);
     if (e != hipSuccess) return e;
     // dgamma and dbeta: the partial rows are [2][h] per block, one launch
     // reduces both halves
-    const int gb = (2 * h + kRedCols - 1) / kRedCols;
-    TraceScope ts(st, "block_reduce", 0.0, (double)nblk * 2 * h * 4 + 16.0 * h);
-    hipLaunchKernelGGL(reduce_blocks_kernel, dim3(gb), dim3(kThreads), 0, st, nblk, 2 * h, h, (int64_t)2 * h,
-                       (const float *)partials, dg, db, accumulate ? 1 : 0);
-    return hipGetLastError();
+    const ReduceSpec r = ln_bwd_reduce_spec(rows, h, partials, dg, db);
+    return reduce_partials(&r, nullptr, accumulate, st);
 }
 
 hipError_t colsum(DType dt, int rows, int n, const void *a, int64_t lda, float *out, bool accumulate,
                   float *partials, hipStream_t st) {
     if (rows <= 0 || n <= 0) return hipSuccess;
-    const int nch = colsum_chunks(rows), rpc = (rows + nch - 1) / nch;
-    dim3 grid((n / 8 + kThreads - 1) / kThreads, nch);
-    const int es = dt == DType::BF16 ? 2 : 4;
-    {
-    TraceScope ts(st, dt == DType::BF16 ? "colsum_bf16" : "colsum_f32", (double)rows * n,
-                  (double)rows * n * es + (double)nch * n * 4);
-    if (dt == DType::BF16)
-        hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(kThreads), 0, st, rows, n, lda, rpc, (const bf16 *)a,
-                           partials);
-    else
-        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(kThreads), 0, st, rows, n, lda, rpc, (const float *)a,
-                           partials);
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = colsum_rows(dt, rows, n, a, lda, 0, nullptr, 0, partials, st);
     if (e != hipSuccess) return e;
-    TraceScope ts(st, "block_reduce", 0.0, (double)nch * n * 4 + 8.0 * n);
-    hipLaunchKernelGGL(reduce_blocks_kernel, dim3((n + kRedCols - 1) / kRedCols), dim3(kThreads), 0, st, nch, n, n,
-                       (int64_t)n, (const float *)partials, out, out, accumulate ? 1 : 0);
-    return hipGetLastError();
+    const ReduceSpec r = colsum_reduce_spec(rows, n, 0, partials, out, out);
+    return reduce_partials(&r, nullptr, accumulate, st);
 }
 
 hipError_t residual_combine(DType dt, int64_t rows, int h, const void *resid, const float *reduced,
