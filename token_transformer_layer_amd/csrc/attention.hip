@@ -304,10 +304,13 @@ __device__ __forceinline__ void kv_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst,
 
 // One 64-key tile of the online softmax of the forward: scores of the tile's
 // keys (LDS [64][D] at ks, positions key0 .. key0+63) for this lane's query
-// (Q in qreg as the B operand), the running sum updated and O^T += V^T P^T
-// accumulated (V at vs).  MASK: some key of the tile is after a query of the
-// wave (position > q_pos) or at or past kmax, and those scores are dropped;
-// other tiles skip the test.
+// (Q in qreg as the B operand), O^T += V^T P^T accumulated (V at vs) and the
+// running sum l += sum of P taken by the matrix cores as one more block of
+// the same product with a V^T of ones (accl: every row holds the lane's
+// query's sum), so the sum costs 4 MFMAs instead of 32 vector adds and
+// matches the bf16 P that O is built from.  MASK: some key of the tile is
+// after a query of the wave (position > q_pos) or at or past kmax, and those
+// scores are dropped; other tiles skip the test.
 //
 // The exponentials are taken against a reference maximum m_ref per query
 // (scaled, log2 units) that is raised only when a score exceeds it by more
@@ -318,21 +321,19 @@ __device__ __forceinline__ void kv_tile_dma(__amdgpu_buffer_rsrc_t r, char *dst,
 // was used.
 template <int D, bool MASK>
 __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const bf16x8 (&qreg)[D / 16],
-                                         f32x16 (&acc)[D / 32], float &m_ref, float &l_run, int key0, int q_pos,
+                                         f32x16 (&acc)[D / 32], f32x16 &accl, float &m_ref, int key0, int q_pos,
                                          int kmax, float sl2, int lane) {
     constexpr int KS = D / 16, DB = D / 32;
     const int g = lane >> 5, li = lane & 31;
-    f32x16 sc[2];
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    // the two key blocks' products interleaved (independent accumulators)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = f32x16{};
-        const int row = kb * 32 + li;
+    for (int st = 0; st < KS; ++st)
 #pragma unroll
-        for (int st = 0; st < KS; ++st)
-            sc[kb] = mfma32(*(const bf16x8 *)(ks + kv_chunk_off<D>(row, 2 * st + g)), qreg[st], sc[kb]);
-    }
+        for (int kb = 0; kb < 2; ++kb)
+            sc[kb] = mfma32(*(const bf16x8 *)(ks + kv_chunk_off<D>(kb * 32 + li, 2 * st + g)), qreg[st], sc[kb]);
     // sc[kb][v]: raw score of key key0 + 32 kb + 8(v/4) + 4g + v%4 for the lane's query
-    float mt = -INFINITY;
+    float mk[2] = {-INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -341,29 +342,24 @@ __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const b
                 const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
                 if (!(key <= q_pos && key < kmax)) sc[kb][v] = -INFINITY;
             }
-            mt = fmaxf(mt, sc[kb][v]);
+            mk[kb] = fmaxf(mk[kb], sc[kb][v]);
         }
+    float mt = fmaxf(mk[0], mk[1]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;  // sl2 > 0: the scaled maximum
     if (__builtin_amdgcn_ballot_w64(mt > m_ref + 8.f)) {  // wave-uniform
         const float m_new = fmaxf(m_ref, mt);
         // a query that has seen no key yet keeps m = -inf (weights 0, nothing to rescale)
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
         m_ref = m_new;
-        l_run *= alpha;
+        accl *= alpha;
 #pragma unroll
         for (int i = 0; i < DB; ++i) acc[i] *= alpha;
     }
     const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
-    float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][v], sl2, nm));
-            sc[kb][v] = p;
-            ls += p;
-        }
-    l_run += ls;
+        for (int v = 0; v < 16; ++v) sc[kb][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][v], sl2, nm));
     // P^T for key step ks (16 keys): registers 8h..8h+7 of block ks/2, h = ks%2
     bf16x8 pb[4];
 #pragma unroll
@@ -374,18 +370,22 @@ __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const b
                  pack_bf2(src[h + 6], src[h + 7])};
         pb[ks4] = __builtin_bit_cast(bf16x8, wv);
     }
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     const int G = lane >> 4, L = lane & 15;
+    // key steps outer, the D/32 output blocks (and the sum block) inner:
+    // consecutive MFMAs go to independent accumulators
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        const int col = db * 32 + 16 * (G & 1) + 4 * (L & 3);
-        const int cc = col >> 3, within = (col & 7) * 2;
+    for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const int r0 = 16 * ks4 + 4 * g + (L >> 2);
 #pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) {
-            const int r0 = 16 * ks4 + 4 * g + (L >> 2);
+        for (int db = 0; db < DB; ++db) {
+            const int col = db * 32 + 16 * (G & 1) + 4 * (L & 3);
+            const int cc = col >> 3, within = (col & 7) * 2;
             u32x2 lo = lds_read_tr16(vs + kv_chunk_off<D>(r0, cc) + within);
             u32x2 hi = lds_read_tr16(vs + kv_chunk_off<D>(r0 + 8, cc) + within);
             acc[db] = mfma32(__builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks4], acc[db]);
         }
+        accl = mfma32(ones, pb[ks4], accl);
     }
 }
 
@@ -394,12 +394,12 @@ __device__ __forceinline__ void fwd_tile(const char *ks, const char *vs, const b
 // kmax.
 template <int D>
 __device__ __forceinline__ void fwd_tile_step(const char *ks, const char *vs, const bf16x8 (&qreg)[D / 16],
-                                              f32x16 (&acc)[D / 32], float &m_ref, float &l_run, int key0,
+                                              f32x16 (&acc)[D / 32], f32x16 &accl, float &m_ref, int key0,
                                               int q_pos, int wave_first_pos, int kmax, float sl2, int lane) {
     if (key0 + 63 > wave_first_pos || key0 + 64 > kmax)
-        fwd_tile<D, true>(ks, vs, qreg, acc, m_ref, l_run, key0, q_pos, kmax, sl2, lane);
+        fwd_tile<D, true>(ks, vs, qreg, acc, accl, m_ref, key0, q_pos, kmax, sl2, lane);
     else
-        fwd_tile<D, false>(ks, vs, qreg, acc, m_ref, l_run, key0, q_pos, kmax, sl2, lane);
+        fwd_tile<D, false>(ks, vs, qreg, acc, accl, m_ref, key0, q_pos, kmax, sl2, lane);
 }
 
 template <int D>
@@ -448,7 +448,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     f32x16 acc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 accl = f32x16{};
+    float m_run = -INFINITY;
 
     kv_tile_dma<D>(rk, smem, slab, t0 * 64, kend, w, lane);
     kv_tile_dma<D>(rv, smem + TILE, slab, t0 * 64, kend, w, lane);
@@ -467,9 +468,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         const int key0 = t * 64;
         if (key0 > qt0 + w * 32 + 31) continue;  // every key of the tile is after this wave's queries
-        fwd_tile_step<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_eff, wave_first, kend, a.sl2, lane);
+        fwd_tile_step<D>(ks, vs, qreg, acc, accl, m_run, key0, q_eff, wave_first, kend, a.sl2, lane);
     }
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = accl[0];
     if (my_q >= a.q1) return;
     if (nch == 1) {
         const float inv = 1.0f / l_tot;
@@ -1108,7 +1109,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     f32x16 acc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 accl = f32x16{};
+    float m_run = -INFINITY;
 
     if (ntiles > 0) {
         kv_tile_dma<D>(rk, smem, kslab, 0, kend, w, lane);
@@ -1128,9 +1130,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         const int key0 = a.k_pos0 + t * 64;
         if (key0 > wave_last_pos) continue;  // every key of the tile is after this wave's queries
-        fwd_tile_step<D>(ks, vs, qreg, acc, m_run, l_run, key0, q_pos, wave_first_pos, a.k_pos0 + kend, a.sl2, lane);
+        fwd_tile_step<D>(ks, vs, qreg, acc, accl, m_run, key0, q_pos, wave_first_pos, a.k_pos0 + kend, a.sl2, lane);
     }
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = accl[0];
     if (!qok) return;
     const bool seen = l_tot > 0.f;
     const float inv = seen ? 1.0f / l_tot : 0.f;
