@@ -549,8 +549,8 @@ def terapipe_plan(layer, bufs, stages):
     from token_transformer_layer_amd import terapipe
     timer = terapipe.SliceTimer(layer, bufs)
     L = layer.shape.seq
-    fit = [(l, o) for l in (16, 64, 256, 1024) for o in (128, 512, 1024) if l + o <= L]
-    check = [(32, 256), (128, 768), (512, 1024), (96, 1536), (768, 1280)]
+    fit = [(l, o) for l in (16, 64, 256, 512, 1024) for o in (128, 384, 768, 1024, 1536) if l + o <= L]
+    check = [(32, 256), (128, 640), (512, 896), (96, 1536), (768, 1280), (192, 1152), (48, 1920)]
     check = [(l, o) for l, o in check if l + o <= L]
     out = terapipe.plan(timer, L, 16, stages, fit, check)
     layer.new_step()

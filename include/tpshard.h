@@ -394,6 +394,12 @@ tp_status tp_attn_block_bwd(const tp_attn_block_shape *shape, const void *q, con
 tp_status tp_slicing_plan(int32_t units, const double *cost, int32_t stages, int32_t *num_slices,
                           int32_t *ends, double *latency);
 
+/* The latency of a given plan (slice ends in units, increasing, the last one
+ * = units) under the same cost table and pipeline model as tp_slicing_plan:
+ * sum_i t_i + (stages - 1) max_i t_i with t_i = cost[a_i * (units + 1) + b_i]. */
+tp_status tp_plan_latency(int32_t units, const double *cost, int32_t stages, int32_t num_slices,
+                          const int32_t *ends, double *latency);
+
 /* Slice-latency model: the context overhead of a slice of l tokens after o
  * tokens of context is modelled as ctx = coef[0] * l * o + coef[1] * o +
  * coef[2], fitted by least squares to n >= 3 measured samples (len[i],

@@ -72,3 +72,30 @@ def test_bad_arguments():
         with pytest.raises(abi.TPError) as ei:
             call()
         assert ei.value.status == abi.TP_EINVAL
+
+
+def test_plan_latency_matches_oracle_pipeline_latency():
+    """The library's latency of a given plan against the oracle's pipeline
+    latency of the same slices (and the stage-by-stage recurrence)."""
+    rng = np.random.default_rng(21)
+    for units in (1, 4, 9):
+        cost = random_cost(units, rng)
+        for stages in (1, 3, 8):
+            for _ in range(5):
+                cuts = sorted(set(int(x) for x in rng.integers(1, units + 1, rng.integers(1, units + 1)))) or [units]
+                ends = [c for c in cuts if c < units] + [units]
+                starts = [0] + ends[:-1]
+                times = [cost[a, b] for a, b in zip(starts, ends)]
+                got = abi.tp_plan_latency(units, cost, stages, ends)
+                assert abs(got - S.pipeline_latency(times, stages)) < 1e-12
+                assert abs(got - S.pipeline_latency_sim(times, stages)) < 1e-12
+        # the optimal plan's own latency
+        lat, ends = abi.tp_slicing_plan(units, cost, 3)
+        assert abs(abi.tp_plan_latency(units, cost, 3, ends) - lat) < 1e-12
+
+
+def test_plan_latency_rejects_bad_plans():
+    cost = random_cost(4, np.random.default_rng(2))
+    for ends in ([2, 1, 4], [1, 2], [0, 4], [2, 5]):
+        with pytest.raises(abi.TPError):
+            abi.tp_plan_latency(4, cost, 2, ends)

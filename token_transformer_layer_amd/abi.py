@@ -21,7 +21,7 @@ TP_BWD_ATTN_SP, TP_BWD_ATTN_DATA_SP = 6, 7
 
 EXPORTED = ["tp_shard_saved_bytes", "tp_shard_scratch_bytes", "tp_shard_layer_fwd",
             "tp_shard_layer_bwd", "tp_residual_combine", "tp_cube_ffn_block", "tp_attn_block_fwd",
-            "tp_attn_merge", "tp_slicing_plan", "tp_fit_context_model", "tp_slice_cost_table",
+            "tp_attn_merge", "tp_slicing_plan", "tp_plan_latency", "tp_fit_context_model", "tp_slice_cost_table",
             "tp_cube_matmul", "tp_cube_bias_gelu", "tp_cube_work_bytes", "tp_cube_gelu_backward",
             "tp_layernorm_work_bytes", "tp_layernorm_fwd", "tp_layernorm_bwd", "tp_trace_enable", "tp_trace_read",
             "tp_gemm_force_tile", "tp_last_error", "tp_shard_layer_fwd_noalloc", "tp_noalloc_scratch_bytes",
@@ -133,6 +133,8 @@ def lib():
     ip = ctypes.POINTER(ctypes.c_int32)
     L.tp_slicing_plan.argtypes = [i32, dp, i32, ip, ip, dp]
     L.tp_slicing_plan.restype = ctypes.c_int
+    L.tp_plan_latency.argtypes = [i32, dp, i32, i32, ip, dp]
+    L.tp_plan_latency.restype = ctypes.c_int
     L.tp_fit_context_model.argtypes = [i32, ip, ip, dp, dp]
     L.tp_fit_context_model.restype = ctypes.c_int
     L.tp_slice_cost_table.argtypes = [i32, i32, dp, dp, dp]
@@ -281,6 +283,18 @@ def tp_slicing_plan(units, cost, stages):
     lat = ctypes.c_double()
     _check(lib().tp_slicing_plan(units, cp, stages, ctypes.byref(n), ep, ctypes.byref(lat)))
     return lat.value, [int(x) for x in ends[:n.value]]
+
+
+def tp_plan_latency(units, cost, stages, ends):
+    """Latency of the plan with the given slice ends under cost (the same
+    pipeline model as tp_slicing_plan)."""
+    c, cp = _dbl(cost)
+    if c.shape != (units + 1, units + 1):
+        raise ValueError("cost must be (units+1, units+1)")
+    e, ep = _i32(ends)
+    lat = ctypes.c_double()
+    _check(lib().tp_plan_latency(units, cp, stages, len(e), ep, ctypes.byref(lat)))
+    return lat.value
 
 
 def tp_fit_context_model(lens, offsets, ctx):

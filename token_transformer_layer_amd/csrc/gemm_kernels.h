@@ -514,6 +514,38 @@ __device__ __forceinline__ void sched_interleave() {
     }
 }
 
+// The vector-memory bookkeeping of gemm_bf16_pp_kernel replayed at compile
+// time for LPT loads per wave per K-tile (the direct-to-LDS loads one
+// issue() or issue_whole() makes: the two operands' kPerWave), S stages and
+// the two wait counts the kernel passes to wait_vmcnt (W0 before the first
+// tile, WH at each hand-over).  Loads retire in issue order, so a wait until
+// at most N are outstanding completes every load but the last N issued.  The
+// kernel issues S K-tiles ahead, waits to W0, and at each hand-over waits to
+// WH and then refills one stage; the replay checks that every wait completes
+// exactly the tile about to be read (all of its loads, none of a later
+// tile's) and that the counts fit the 6-bit vmcnt field.
+template <int LPT, int S, int W0, int WH>
+constexpr bool pp_waits_complete_next_tile(int nkt = 12) {
+    if (LPT <= 0 || S < 2 || W0 >= 64 || WH >= 64 || W0 < 0 || WH < 0 || nkt > 60) return false;
+    long issued = 0, last_of[64] = {};
+    int next = 0;
+    for (int s = 0; s < S; ++s) {
+        issued += LPT;
+        last_of[next++] = issued;  // count of loads issued when tile s's last load was
+    }
+    long completed = issued - W0;
+    if (completed != last_of[0]) return false;
+    for (int kt = 0; kt + 1 < nkt; ++kt) {
+        const long now = issued - WH;
+        if (now > completed) completed = now;
+        if (completed < last_of[kt + 1]) return false;          // the next tile would be read too early
+        if (S > 2 && completed > last_of[kt + 1]) return false;  // a later tile's loads would be waited for
+        issued += LPT;
+        last_of[next++] = issued;
+    }
+    return true;
+}
+
 template <class C, bool AK, bool BK_, class Epi, bool WHOLE>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(C::kOcc * C::kThreads / 256)))
 void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
@@ -529,6 +561,10 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
     constexpr int LPT = OpA::kPerWave + OpB::kPerWave;  // DMA issues per wave per K-tile
     constexpr int NREAD = (AK ? 1 : 2) * FM + (BK_ ? 1 : 2) * FN;
     static_assert(LPT * (S - 1) < 64, "vmcnt range");
+    static_assert(OpA::kPerWave * NW * 1024 == OpA::kBytes && OpB::kPerWave * NW * 1024 == OpB::kBytes,
+                  "the loads of one K-tile cover its stage exactly once");
+    constexpr int W0 = LPT * (S - 1), WH = LPT * (S - 2);  // the kernel's two wait counts
+    static_assert(pp_waits_complete_next_tile<LPT, S, W0, WH>(), "the waits do not match the loads issued per K-tile");
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -579,7 +615,7 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
         // has no branches for the scheduler to stop at.
 #pragma unroll
         for (int s = 0; s < S; ++s) issue(s, kbase + s * BK);
-        wait_vmcnt<LPT * (S - 1)>();  // tile 0 has landed
+        wait_vmcnt<W0>();  // tile 0 has landed
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
@@ -621,7 +657,7 @@ void gemm_bf16_pp_kernel(GemmArgs g, Epi epi, int gm_rows) {
             // registers once lgkmcnt drains; tiles kt + 2 .. kt + S - 1 may
             // still be in flight)
             wait_lgkm0();
-            wait_vmcnt<LPT * (S - 2)>();
+            wait_vmcnt<WH>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
             // the next tile's first fragments are read before the refill is

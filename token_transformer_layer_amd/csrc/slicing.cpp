@@ -92,6 +92,29 @@ tp_status tp_slice_cost_table(int32_t units, int32_t granularity, const double *
     return TP_OK;
 }
 
+tp_status tp_plan_latency(int32_t units, const double *cost, int32_t stages, int32_t num_slices, const int32_t *ends,
+                          double *latency) {
+    if (units < 1 || units > 4096) return set_error(TP_EINVAL, "units must be in [1, 4096]");
+    if (stages < 1) return set_error(TP_EINVAL, "stages must be positive");
+    if (num_slices < 1) return set_error(TP_EINVAL, "a plan has at least one slice");
+    if (!cost || !ends || !latency) return set_error(TP_EINVAL, "NULL argument");
+    const int W = units + 1;
+    double sum = 0.0, mx = 0.0;
+    int a = 0;
+    for (int i = 0; i < num_slices; ++i) {
+        const int b = ends[i];
+        if (b <= a || b > units) return set_error(TP_EINVAL, "slice ends must increase within [1, units]");
+        const double t = cost[a * W + b];
+        if (!(t >= 0) || std::isnan(t)) return set_error(TP_EINVAL, "slice costs must be >= 0 (or +inf)");
+        sum += t;
+        mx = std::max(mx, t);
+        a = b;
+    }
+    if (a != units) return set_error(TP_EINVAL, "the last slice must end at units");
+    *latency = sum + (double)(stages - 1) * mx;
+    return TP_OK;
+}
+
 tp_status tp_slicing_plan(int32_t units, const double *cost, int32_t stages, int32_t *num_slices, int32_t *ends,
                           double *latency) {
     if (units < 1 || units > 4096) return set_error(TP_EINVAL, "units must be in [1, 4096]");

@@ -64,10 +64,13 @@ class SliceTimer:
         return float(np.median(times))
 
 
-def plan(timer, seq, granularity, stages, fit_points, check_points, reps=3):
+def plan(timer, seq, granularity, stages, fit_points, check_points, reps=5):
     """Measure, fit, plan.  fit_points / check_points: (length, offset) token
     pairs with offset > 0 used to fit the context model / to measure its
-    error.  Returns a dict with the plan and the model's figures."""
+    error.  Every latency figure comes from the library: the model's
+    prediction of a slice is its entry of the cost table, and the latencies
+    of the plan and of uniform slicings are the library's pipeline latency
+    over that table.  Returns a dict with the plan and the model's figures."""
     units = seq // granularity
     fwd = np.zeros(units + 1)
     for k in range(1, units + 1):
@@ -78,23 +81,20 @@ def plan(timer, seq, granularity, stages, fit_points, check_points, reps=3):
     fl = [l for l, _ in fit_points]
     fo = [o for _, o in fit_points]
     coef = abi.tp_fit_context_model(fl, fo, [ctx_of(l, o) for l, o in fit_points])
+    cost = abi.tp_slice_cost_table(units, granularity, fwd, coef)
     rel = []
     for l, o in check_points:
         t = timer.ms(l, o, reps)
-        pred = fwd[l // granularity] + coef[0] * l * o + coef[1] * o + coef[2]
+        pred = cost[o // granularity, (o + l) // granularity]
         rel.append(abs(pred - t) / t)
-    cost = abi.tp_slice_cost_table(units, granularity, fwd, coef)
     lat, ends = abi.tp_slicing_plan(units, cost, stages)
     lengths = [(b - a) * granularity for a, b in zip([0] + ends[:-1], ends)]
-
-    def uniform(n):
-        k = units // n
-        ts = [cost[i * k, (i + 1) * k] for i in range(n)]
-        return float(np.sum(ts) + (stages - 1) * np.max(ts))
-    uni = {n: round(uniform(n), 4) for n in (1, 2, 4, 8, 16, 32, 64, 128) if units % n == 0 and n <= units}
+    uni = {n: round(abi.tp_plan_latency(units, cost, stages, [(i + 1) * (units // n) for i in range(n)]), 4)
+           for n in (1, 2, 4, 8, 16, 32, 64, 128) if units % n == 0 and n <= units}
     return dict(granularity=granularity, stages=stages, slices=lengths, modeled_latency_ms=round(lat, 4),
                 uniform_modeled_latency_ms=uni, context_model=[float("%.6g" % c) for c in coef],
                 model_rel_error_max=round(max(rel), 4) if rel else None,
                 model_rel_error_mean=round(float(np.mean(rel)), 4) if rel else None,
+                fit_points=len(fit_points), check_points=len(check_points), reps=reps,
                 fwd_no_context_ms={int(k * granularity): round(float(fwd[k]), 4)
                                    for k in (1, units // 8, units // 2, units) if k >= 1})
