@@ -557,6 +557,12 @@ def terapipe_plan(layer, bufs, stages):
     return out
 
 
+def note(msg):
+    """A progress line on stderr (the JSON result stays alone on stdout)."""
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -641,16 +647,22 @@ def main():
     gemm_ms = sum(r[3] for r in recs if r[0].startswith("gemm")) / args.steps
     gemm_fl = sum(r[1] for r in recs if r[0].startswith("gemm")) / args.steps
 
+    note("headline step timed: %.4f ms" % ms)
     extra = {}
     if not args.no_extra:
         extra["per_slice_calls"] = per_slice_figures(torch, layer, bufs, max(3, args.steps // 2), 2)
+        note("per-slice schedule timed")
         extra["cube_ffn_block"] = cube_block(torch, max(3, args.steps // 2), 2)
         extra["cube_ffn_backward"] = cube_backward(torch, max(3, args.steps // 2), 2)
+        note("cube block timed")
         extra["sequence_parallel_step"] = sequence_parallel_step(torch, layer, bufs, max(3, args.steps // 2), 2)
         extra["ring_attention_block"] = ring_block(torch, max(3, args.steps // 2), 2)
+        note("sequence-parallel step and ring blocks timed")
         extra["terapipe_slicing"] = terapipe_plan(layer, bufs, stages=8)
+        note("slicing plan measured")
         extra["other_workloads"] = {n: config_step(torch, n, max(5, args.steps // 2), 3)
                                     for n in ("gpt13b-t8", "medium-bf16") if n != shape.name}
+        note("other workloads timed")
 
     out = {
         "metric": "shard-layer fwd+bwd TFLOP/s, GPT-3 175B t=8 shard, one MI355X",
@@ -684,6 +696,7 @@ def main():
     }
     out.update(extra)
     if not args.no_cpu:
+        note("timing the CPU oracle on a sample of the step")
         out["cpu_baseline"] = cpu_baseline(shape, args.cpu_slices)
     print(json.dumps(out), flush=True)
 
