@@ -24,6 +24,7 @@
 // configuration only).
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -623,6 +624,98 @@ __device__ __forceinline__ bf16x8 pack_half(const f32x16 &s, int h) {
                                             pack_bf2(s[b + 4], s[b + 5]), pack_bf2(s[b + 6], s[b + 7])});
 }
 
+// One 64-query tile of the dK/dV kernels for one wave's 32 keys (K and V
+// fragments in kreg, vreg; the tile's Q, dO, log2-domain log-sum-exp and
+// delta in LDS at st): S and dP of the tile's two 32-query blocks, P and
+// dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS.  `full` (wave-
+// uniform): every query of the tile sees every key of the wave, so no mask
+// is applied, and the second block's products are issued before the first
+// block's exponentials so the matrix cores work during them.  Otherwise a
+// block is skipped when skip(qb) (every query precedes every key of the
+// wave) and each probability is masked by vis(query index in the tile).
+template <int D, class Skip, class Vis>
+__device__ __forceinline__ void dkdv_tile(const char *st, const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
+                                          f32x16 (&acc_dk)[D / 32], f32x16 (&acc_dv)[D / 32], float sl2, int lane,
+                                          bool full, Skip skip, Vis vis) {
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int TILE = 64 * D * 2;
+    const int g = lane >> 5, li = lane & 31;
+    const float *lse_s = (const float *)(st + 2 * TILE);
+    const float *del_s = lse_s + 64;
+    auto scores = [&](int qb, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+        sc = f32x16{};
+        dp = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int off = kv_chunk_off<D>(qb * 32 + li, 2 * s + g);
+            sc = mfma32(*(const bf16x8 *)(st + off), kreg[s], sc);
+            dp = mfma32(*(const bf16x8 *)(st + TILE + off), vreg[s], dp);
+        }
+    };
+    // register v: query 32 qb + 8(v/4) + 4g + v%4 of the tile
+    auto probs = [&](int qb, f32x16 &sc, f32x16 &dp, bf16x8 (&pb)[2], bf16x8 (&sb)[2], auto mask)
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ql = qb * 32 + 8 * r + 4 * g;
+            const f32x4 l4 = *(const f32x4 *)(lse_s + ql);
+            const f32x4 d4 = *(const f32x4 *)(del_s + ql);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float pr = __builtin_amdgcn_exp2f(sc[4 * r + u] * sl2 - l4[u]);
+                if constexpr (decltype(mask)::value) pr = vis(ql + u) ? pr : 0.f;
+                sc[4 * r + u] = pr;
+                dp[4 * r + u] = pr * (dp[4 * r + u] - d4[u]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            pb[h] = pack_half(sc, h);
+            sb[h] = pack_half(dp, h);
+        }
+    };
+    auto grads = [&](int qb, const bf16x8 (&pb)[2], const bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc_dv[db] = mfma32(tr_frag<D>(st + TILE, qb * 32 + 16 * h, db, lane), pb[h], acc_dv[db]);
+                acc_dk[db] = mfma32(tr_frag<D>(st, qb * 32 + 16 * h, db, lane), sb[h], acc_dk[db]);
+            }
+    };
+    if (full) {
+        f32x16 sc0, dp0, sc1, dp1;
+        bf16x8 pb0[2], sb0[2], pb1[2], sb1[2];
+        scores(0, sc0, dp0);
+        scores(1, sc1, dp1);
+        probs(0, sc0, dp0, pb0, sb0, std::false_type{});
+        grads(0, pb0, sb0);
+        probs(1, sc1, dp1, pb1, sb1, std::false_type{});
+        grads(1, pb1, sb1);
+        // keep the fragment reads of the score products six ahead of the
+        // MFMAs that use them (left to itself the scheduler issues each read
+        // just before its MFMA, which then waits out an LDS round trip)
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * 2 * KS - 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            if (skip(qb)) continue;
+            f32x16 sc, dp;
+            bf16x8 pb[2], sb[2];
+            scores(qb, sc, dp);
+            probs(qb, sc, dp, pb, sb, std::true_type{});
+            grads(qb, pb, sb);
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
     constexpr int KS = D / 16, DB = D / 32;
@@ -739,44 +832,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma32(AttnP a) {
             issue(t + NST - 1, nx);
         }
         const int p0 = qstart + (t_first + t) * 64;
-        const float *lse_s = (const float *)(st + 2 * TILE);
-        const float *del_s = lse_s + 64;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int qr0 = p0 + qb * 32;          // first query of the block
-            if (qr0 + 31 < kw0) continue;          // every query precedes every key of this wave
-            f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int off = kv_chunk_off<D>(qb * 32 + li, 2 * s + g);
-                sc = mfma32(*(const bf16x8 *)(st + off), kreg[s], sc);
-                dp = mfma32(*(const bf16x8 *)(st + TILE + off), vreg[s], dp);
-            }
-            // register v: query qr0 + 8(v/4) + 4g + v%4, key my_k
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ql = qb * 32 + 8 * r + 4 * g;
-                const f32x4 l4 = *(const f32x4 *)(lse_s + ql);
-                const f32x4 d4 = *(const f32x4 *)(del_s + ql);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int q = p0 + ql + u;
-                    const float pr =
-                        (my_k <= q && q < a.q1) ? __builtin_amdgcn_exp2f(sc[4 * r + u] * sl2 - l4[u]) : 0.f;
-                    sc[4 * r + u] = pr;
-                    dp[4 * r + u] = pr * (dp[4 * r + u] - d4[u]);
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x8 pb = pack_half(sc, h), sb = pack_half(dp, h);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    acc_dv[db] = mfma32(tr_frag<D>(st + TILE, qb * 32 + 16 * h, db, lane), pb, acc_dv[db]);
-                    acc_dk[db] = mfma32(tr_frag<D>(st, qb * 32 + 16 * h, db, lane), sb, acc_dk[db]);
-                }
-            }
-        }
+        dkdv_tile<D>(st, kreg, vreg, acc_dk, acc_dv, sl2, lane, p0 >= kw0 + 31 && p0 + 63 < a.q1,
+                     [&](int qb) { return p0 + qb * 32 + 31 < kw0; },
+                     [&](int ql) { const int q = p0 + ql; return my_k <= q && q < a.q1; });
         if (t + NST - 1 < nqt) store_stat(nx);
     }
     if (my_k >= a.q1) return;
@@ -1274,44 +1332,10 @@ __global__ __launch_bounds__(256) void attn_block_bwd_dkdv_mfma32(AttnBlockBwdP 
             issue(t + NST - 1, nx);
         }
         const int p0 = qstart + t * 64;
-        const float *lse_s = (const float *)(st + 2 * TILE);
-        const float *del_s = lse_s + 64;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int qr0 = p0 + qb * 32;
-            if (a.q_pos0 + qr0 + 31 < a.k_pos0 + kw0) continue;  // every query precedes every key of this wave
-            f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int off = kv_chunk_off<D>(qb * 32 + li, 2 * s + g);
-                sc = mfma32(*(const bf16x8 *)(st + off), kreg[s], sc);
-                dp = mfma32(*(const bf16x8 *)(st + TILE + off), vreg[s], dp);
-            }
-            // register v: query qr0 + 8(v/4) + 4g + v%4, key my_k
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ql = qb * 32 + 8 * r + 4 * g;
-                const f32x4 l4 = *(const f32x4 *)(lse_s + ql);
-                const f32x4 d4 = *(const f32x4 *)(del_s + ql);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int q = p0 + ql + u;
-                    const bool vis = kok && q < a.nq && my_kpos <= a.q_pos0 + q;
-                    const float pr = vis ? __builtin_amdgcn_exp2f(sc[4 * r + u] * sl2 - l4[u]) : 0.f;
-                    sc[4 * r + u] = pr;
-                    dp[4 * r + u] = pr * (dp[4 * r + u] - d4[u]);
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x8 pb = pack_half(sc, h), sb = pack_half(dp, h);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    acc_dv[db] = mfma32(tr_frag<D>(st + TILE, qb * 32 + 16 * h, db, lane), pb, acc_dv[db]);
-                    acc_dk[db] = mfma32(tr_frag<D>(st, qb * 32 + 16 * h, db, lane), sb, acc_dk[db]);
-                }
-            }
-        }
+        const bool full = kw0 + 31 < a.nk && p0 + 63 < a.nq && a.q_pos0 + p0 >= a.k_pos0 + kw0 + 31;
+        dkdv_tile<D>(st, kreg, vreg, acc_dk, acc_dv, sl2, lane, full,
+                     [&](int qb) { return a.q_pos0 + p0 + qb * 32 + 31 < a.k_pos0 + kw0; },
+                     [&](int ql) { const int q = p0 + ql; return kok && q < a.nq && my_kpos <= a.q_pos0 + q; });
         if (t + NST - 1 < nqt) store_stat(nx);
     }
     if (!kok) return;
