@@ -970,6 +970,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4) acc[db] = mfma32(tr_frag<D>(ks, 16 * k4, db, lane), sb[k4], acc[db]);
+        // each key block's score fragments read four ahead of their MFMAs
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KS - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
     }
     if (!qok) return;
     if (nch > 1) {
@@ -1435,6 +1447,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int k4 = 0; k4 < 4; ++k4) acc[db] = mfma32(tr_frag<D>(ks, 16 * k4, db, lane), sb[k4], acc[db]);
+        // each key block's score fragments read four ahead of their MFMAs
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KS - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
     }
     if (!qok) return;
     float *pq = a.dq + qslab + (int64_t)my_q * D;
