@@ -1500,6 +1500,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int64_t rows, int d, co
 
 }  // namespace
 
+// Raises a kernel's dynamic LDS limit (above the 64 KB default) before its
+// launch; the caller returns the error, if any, before launching.
+static hipError_t set_lds(const void *fn, int bytes) {
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 // (query, key) pairs of the causal product for queries [q0, q1) of every
 // (batch row, head): query p sees p + 1 keys.
 static double causal_pairs(const AttnArgs &x) {
@@ -1584,10 +1590,10 @@ hipError_t attn_fwd(DType dt, const AttnArgs &x, hipStream_t st) {
         const int lds = 2 * 2 * 64 * x.d * 2;
         dim3 grid(xcd_grid(p.n_items));
         if (x.d == 128) {
-            hipFuncSetAttribute((const void *)attn_fwd_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (hipError_t e = set_lds((const void *)attn_fwd_mfma32<128>, lds); e != hipSuccess) return e;
             hipLaunchKernelGGL(attn_fwd_mfma32<128>, grid, dim3(256), lds, st, p);
         } else {
-            hipFuncSetAttribute((const void *)attn_fwd_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (hipError_t e = set_lds((const void *)attn_fwd_mfma32<64>, lds); e != hipSuccess) return e;
             hipLaunchKernelGGL(attn_fwd_mfma32<64>, grid, dim3(256), lds, st, p);
         }
         if (p.max_chunks > 1) {
@@ -1662,13 +1668,11 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
             dim3 gk(xcd_grid(p.n_items));
             TraceScope ts(st, "attn_bwd_dkdv_bf16", 8.0 * x.d * pairs, kv_bytes);
             if (x.d == 128) {
-                hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<128>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+                if (hipError_t e = set_lds((const void *)attn_bwd_dkdv_mfma32<128>, lds_kv); e != hipSuccess) return e;
                 hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<128>, gk, dim3(256), lds_kv, st, p);
                 if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<128>, dim3(nkb * (kBwdBK * x.d / 2048), bh), dim3(256), 0, st, p);
             } else {
-                hipFuncSetAttribute((const void *)attn_bwd_dkdv_mfma32<64>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+                if (hipError_t e = set_lds((const void *)attn_bwd_dkdv_mfma32<64>, lds_kv); e != hipSuccess) return e;
                 hipLaunchKernelGGL(attn_bwd_dkdv_mfma32<64>, gk, dim3(256), lds_kv, st, p);
                 if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dkdv_combine<64>, dim3(nkb * (kBwdBK * x.d / 2048), bh), dim3(256), 0, st, p);
             }
@@ -1695,13 +1699,11 @@ hipError_t attn_bwd(DType dt, const AttnArgs &x, hipStream_t st) {
             dim3 gq(xcd_grid(p.n_items));
             TraceScope ts(st, "attn_bwd_dq_bf16", 6.0 * x.d * pairs, q_bytes);
             if (x.d == 128) {
-                hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    lds_q);
+                if (hipError_t e = set_lds((const void *)attn_bwd_dq_mfma32<128>, lds_q); e != hipSuccess) return e;
                 hipLaunchKernelGGL(attn_bwd_dq_mfma32<128>, gq, dim3(256), lds_q, st, p);
                 if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<128>, dim3(nqb * (kBwdBQ * x.d / 2048), bh), dim3(256), 0, st, p);
             } else {
-                hipFuncSetAttribute((const void *)attn_bwd_dq_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    lds_q);
+                if (hipError_t e = set_lds((const void *)attn_bwd_dq_mfma32<64>, lds_q); e != hipSuccess) return e;
                 hipLaunchKernelGGL(attn_bwd_dq_mfma32<64>, gq, dim3(256), lds_q, st, p);
                 if (p.max_chunks > 1) hipLaunchKernelGGL(attn_bwd_dq_combine<64>, dim3(nqb * (kBwdBQ * x.d / 2048), bh), dim3(256), 0, st, p);
             }
@@ -1748,10 +1750,10 @@ hipError_t attn_block_fwd(const AttnBlockArgs &x, hipStream_t st) {
     const int lds = 2 * 2 * 64 * x.d * 2;
     dim3 grid((x.nq + kFwdBQ - 1) / kFwdBQ, x.bh);
     if (x.d == 128) {
-        hipFuncSetAttribute((const void *)attn_block_fwd_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (hipError_t e = set_lds((const void *)attn_block_fwd_mfma32<128>, lds); e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_block_fwd_mfma32<128>, grid, dim3(256), lds, st, p);
     } else {
-        hipFuncSetAttribute((const void *)attn_block_fwd_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (hipError_t e = set_lds((const void *)attn_block_fwd_mfma32<64>, lds); e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_block_fwd_mfma32<64>, grid, dim3(256), lds, st, p);
     }
     return hipGetLastError();
@@ -1797,12 +1799,10 @@ hipError_t attn_block_bwd(const AttnBlockBwdArgs &x, hipStream_t st) {
                       (double)x.bh * x.d * (4.0 * x.nk + 4.0 * x.nq + 8.0 * x.nk));
         dim3 grid((x.nk + kBwdBK - 1) / kBwdBK, x.bh);
         if (x.d == 128) {
-            hipFuncSetAttribute((const void *)attn_block_bwd_dkdv_mfma32<128>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+            if (hipError_t e = set_lds((const void *)attn_block_bwd_dkdv_mfma32<128>, lds_kv); e != hipSuccess) return e;
             hipLaunchKernelGGL(attn_block_bwd_dkdv_mfma32<128>, grid, dim3(256), lds_kv, st, p);
         } else {
-            hipFuncSetAttribute((const void *)attn_block_bwd_dkdv_mfma32<64>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds_kv);
+            if (hipError_t e = set_lds((const void *)attn_block_bwd_dkdv_mfma32<64>, lds_kv); e != hipSuccess) return e;
             hipLaunchKernelGGL(attn_block_bwd_dkdv_mfma32<64>, grid, dim3(256), lds_kv, st, p);
         }
     }
@@ -1811,12 +1811,10 @@ hipError_t attn_block_bwd(const AttnBlockBwdArgs &x, hipStream_t st) {
                       (double)x.bh * x.d * (4.0 * x.nq + 4.0 * x.nk + 4.0 * x.nq));
         dim3 grid((x.nq + kBwdBQ - 1) / kBwdBQ, x.bh);
         if (x.d == 128) {
-            hipFuncSetAttribute((const void *)attn_block_bwd_dq_mfma32<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds_q);
+            if (hipError_t e = set_lds((const void *)attn_block_bwd_dq_mfma32<128>, lds_q); e != hipSuccess) return e;
             hipLaunchKernelGGL(attn_block_bwd_dq_mfma32<128>, grid, dim3(256), lds_q, st, p);
         } else {
-            hipFuncSetAttribute((const void *)attn_block_bwd_dq_mfma32<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds_q);
+            if (hipError_t e = set_lds((const void *)attn_block_bwd_dq_mfma32<64>, lds_q); e != hipSuccess) return e;
             hipLaunchKernelGGL(attn_block_bwd_dq_mfma32<64>, grid, dim3(256), lds_q, st, p);
         }
     }
