@@ -441,7 +441,8 @@ tp_status tp_layernorm_bwd(const tp_shard_cfg *cfg, int64_t rows, const float *d
  * tp_trace_enable(0) stops recording.  tp_trace_read() waits for the
  * recorded events, writes the first `max` records to `out` (which may be
  * NULL), releases all records and returns how many there were.  ms is the
- * event-measured duration (-1 if the events could not be read). */
+ * event-measured duration (-1 if the events could not be read); a launch
+ * whose events could not be created or recorded has no record. */
 typedef struct {
     char name[64];
     double flops;

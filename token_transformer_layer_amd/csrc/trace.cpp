@@ -43,19 +43,22 @@ bool trace_enabled() { return g_on.load(std::memory_order_relaxed); }
 void trace_begin(hipStream_t st) {
     std::lock_guard<std::mutex> lk(g_mu);
     t_open = get_event();
-    if (t_open) hipEventRecord(t_open, st);
+    if (t_open && hipEventRecord(t_open, st) != hipSuccess) {  // no record for this launch
+        g_pool.push_back(t_open);
+        t_open = nullptr;
+    }
 }
 
 void trace_end(hipStream_t st, const char *name, double flops, double bytes) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (!t_open) return;
     hipEvent_t b = get_event();
-    if (!b) {
+    if (!b || hipEventRecord(b, st) != hipSuccess) {
         g_pool.push_back(t_open);
+        if (b) g_pool.push_back(b);
         t_open = nullptr;
         return;
     }
-    hipEventRecord(b, st);
     g_recs.push_back(Rec{name, flops, bytes, t_open, b});
     t_open = nullptr;
 }
@@ -81,8 +84,8 @@ int32_t tp_trace_read(tp_trace_record *out, int32_t max) {
     int32_t n = (int32_t)g_recs.size();
     for (int32_t i = 0; i < n; ++i) {
         Rec &r = g_recs[i];
-        float ms = -1.f;
-        if (hipEventSynchronize(r.b) == hipSuccess) hipEventElapsedTime(&ms, r.a, r.b);
+        float ms = -1.f;  // -1: the events could not be timed
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) ms = -1.f;
         if (out && i < max) {
             std::memset(&out[i], 0, sizeof(out[i]));
             std::strncpy(out[i].name, r.name.c_str(), sizeof(out[i].name) - 1);
