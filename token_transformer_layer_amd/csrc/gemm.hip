@@ -66,8 +66,17 @@ static Tile pick_tile(int M, int N, int K, bool ak, bool bk) {
     // 128x128 tiles and split their reduction.
     const double f256 = round_fill(t256, 256), f128x192 = round_fill(t128x192, 512);
     if (ak && bk && K >= 4096 && f256 >= 0.97) return Tile::Pp256w8;
-    if (ak && !bk && K >= 4096 && t128x192 >= 192 && f256 >= f128x192 - 0.02) return Tile::Pp256w8;
-    if (!ak && !bk && K >= 1024 && f256 >= 0.75 && t256 >= 128) return Tile::Pp256w8;
+    // input gradients and weight gradients: the 8-wave tile also for
+    // reductions of 1024-4095 and for weight gradients whose last round is
+    // 60% full (measured on the 13B shard's products with the operands
+    // flushed from the MALL: 4-10% over 128x192 tiles)
+    if (ak && !bk && K >= 1024 && t128x192 >= 192 && f256 >= f128x192 - 0.02) return Tile::Pp256w8;
+    if (!ak && !bk && K >= 1024 && f256 >= 0.6 && t256 >= 128) return Tile::Pp256w8;
+    // long reductions into outputs whose width wastes more than 15% of a
+    // 192-wide tile column (640 columns: 768 computed) take 128-wide tiles
+    // (7-9% faster there)
+    const int n192 = (N + 191) / 192 * 192;
+    if ((double)N / n192 < 0.85 && M >= 256 && K >= 4096) return Tile::Pp128;
     if (t128x192 >= 192 && K >= 512) return Tile::Pp128x192;
     // narrow outputs of a long reduction over many rows (the attention
     // output projection's input gradient): 128x192 tiles with the reduction
