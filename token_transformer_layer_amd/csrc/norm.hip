@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, cons
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        if (threadIdx.x + i * kThreads < nv) {
+        if ((int)threadIdx.x + i * kThreads < nv) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float dlt = xv[i][j] - mu;
@@ -431,6 +431,7 @@ static void launch_ln_fwd(int rows, int h, float eps, const void *x, const void 
 template <typename T>
 static void dispatch_ln_fwd(int rows, int h, float eps, const void *x, const void *g, const void *b, void *u,
                             float *mean, float *rstd, hipStream_t st) {
+    static_assert(kMaxVec == 8, "the cases below cover 1..kMaxVec vectors per thread");
     switch (((h >> 3) + kThreads - 1) / kThreads) {  // vectors per thread, 1..kMaxVec
     case 1: launch_ln_fwd<T, 1>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
     case 2: launch_ln_fwd<T, 2>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
