@@ -50,12 +50,7 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // the next tile's first fragments before it issues the refill.  Measured in
 // the layer step, the GEMM kernels take the untracked form (weight
 // gradients 7% faster, input-gradient products 3-16%), and the attention
-// kernels, 1-3% slower with it, keep the tracked builtin.  The asm sets m0
-// (the LDS destination) itself and lists it as clobbered; m0 is a register
-// the compiler reserves and does not promise to preserve across such a
-// statement, so the untracked form is used only in kernels where nothing
-// else reads m0 (in the GEMM kernels' ISA every m0 write is this asm's and
-// every read its load's).
+// kernels, 1-3% slower with it, keep the tracked builtin.
 typedef __attribute__((address_space(3))) void lds_void;
 template <bool UNTRACKED = false>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char *lds_base, uint32_t voff) {
