@@ -18,6 +18,9 @@ def test_gemm_symbols_map_to_trace_names():
     assert profiling.trace_name(p) == "gemm_bf16_256x192w8_nt_bias_gelu"
     d = "void tpk::gemm_bf16_pp_kernel<tpk::DlCfg<256, 256, 2, 4, 2, 64, 1>, false, false, tpk::EpiStoreF32<__bf16> >(tpk::GemmArgs)"
     assert profiling.trace_name(d) == "gemm_bf16_256w8_tn_store_f32"
+    # a short slice's input-gradient product computed transposed (split partial sums)
+    p = "_ZN3tpk19gemm_bf16_pp_kernelINS_5DlCfgILi256ELi128ELi4ELi2ELi3ELi64ELi1EEELb0ELb1ENS_8EpiSplitELb1EEEvNS_8GemmArgsET2_i"
+    assert profiling.trace_name(p) == "gemm_bf16_sk256x128_mk_split"
     assert profiling.trace_name("_ZN3tpk12_GLOBAL__N_113ln_bwd_kernelIDF16bEEviiiPKf") == "ln_bwd_kernel<bf16>"
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtpshard.so")
-SOURCES = ["gemm_tn.hip", "gemm_nn.hip", "gemm_nt.hip", "attention.hip", "norm.hip", "gemm.hip", "api.cpp", "trace.cpp",
+SOURCES = ["gemm_tn.hip", "gemm_nn.hip", "gemm_nt.hip", "gemm_mk.hip", "attention.hip", "norm.hip", "gemm.hip", "api.cpp", "trace.cpp",
            "slicing.cpp", "noalloc.hip"]
 
 HIPCC_FLAGS = [

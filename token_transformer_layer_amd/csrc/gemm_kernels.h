@@ -745,6 +745,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     epi.row8(m, n, v);
 }
 
+// The same for partial products stored transposed (a product computed as
+// C^T = B A^T: split sp holds element (m, n) at ws[sp * stride + n * ldm + m]).
+// Consecutive threads take consecutive rows m, so every partial-sum load of a
+// wave reads one contiguous run.
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_reduce_t_kernel(const float *__restrict__ ws, int nsplit, int M,
+                                                              int ldm, int N, Epi epi) {
+    const int64_t i = blockIdx.x * 256LL + threadIdx.x;
+    if (i >= (int64_t)M * (N >> 3)) return;
+    const int m = (int)(i % M), n = (int)(i / M) * 8;
+    const int64_t stride = (int64_t)N * ldm;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ws[(int64_t)(n + j) * ldm + m];
+    for (int sp = 1; sp < nsplit; ++sp) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] += ws[sp * stride + (int64_t)(n + j) * ldm + m];
+    }
+    epi.row8(m, n, v);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -816,6 +837,10 @@ using Pp256w8 = DlCfg<256, 256, 2, 4, 2, 64>;        // 128 KB; waves 2x4 (128x6
 // at any depth (a K-contiguous operand's 64-byte rows would split every
 // 128-byte line in two): 1.5% faster on the weight gradients in the step
 using Pp256w8k32 = DlCfg<256, 256, 2, 4, 4, 32>;     // 128 KB
+// products of at most 128 token rows computed transposed (C^T = W X^T): 256
+// weight rows by the 128 token rows, three stages (two K-tiles in flight);
+// 8 waves measured 1-3% ahead of 4 (128x64 each) on the forward products
+using Sk256x128 = DlCfg<256, 128, 4, 2, 3, 64>;      // 144 KB; waves 4x2 (64x64 each)
 
 // Tile configurations, chosen per product shape from measurements on MI355X
 // (TFLOP/s of each candidate on the GPT-3 175B t=8 shard's products and on
@@ -824,7 +849,7 @@ using Pp256w8k32 = DlCfg<256, 256, 2, 4, 4, 32>;     // 128 KB
 // load path delivers, so larger tiles win wherever there are enough of them
 // to fill the 256 compute units; the plain (non-pipelined) 128x128 kernel
 // is the best fit for short reductions and narrow outputs.
-enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192, Pp256w8 };
+enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192, Pp256w8, Sk256x128 };
 
 template <typename T, bool AK, bool BK_, class E>
 static hipError_t launch(const GemmArgs &g, const E &epi, Tile tile, hipStream_t st) {
@@ -838,6 +863,7 @@ static hipError_t launch(const GemmArgs &g, const E &epi, Tile tile, hipStream_t
             else return launch_pp<Pp256w8k32, AK, BK_>(g, epi, st);
         case Tile::Pp256x128: return launch_pp<Pp256x128, AK, BK_>(g, epi, st);
         case Tile::Pp128: return launch_pp<Dl128, AK, BK_>(g, epi, st);
+        case Tile::Sk256x128: return launch_pp<Sk256x128, AK, BK_>(g, epi, st);
         case Tile::Dl128: break;
         }
         return launch_dl<Dl128, AK, BK_>(g, epi, st);
@@ -885,5 +911,8 @@ hipError_t gemm_layout_nn(bool is_bf16, const GemmArgs &g, Epi kind, const EpiAr
                           hipStream_t st);
 hipError_t gemm_layout_tn(bool is_bf16, const GemmArgs &g, Epi kind, const EpiArgs &e, float *split_ws, Tile tile,
                           hipStream_t st);
+// A M-contiguous, B K-contiguous: the input-gradient products computed
+// transposed (split partial sums only)
+hipError_t gemm_layout_mk_split(const GemmArgs &g, float *split_ws, int64_t ldc, Tile tile, hipStream_t st);
 
 }  // namespace tpk

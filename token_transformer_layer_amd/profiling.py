@@ -29,7 +29,7 @@ CSRC = os.path.join(PKG, "csrc")
 # The trace name of a kernel starts with the name of its family; each family
 # is defined by these sources (plus the shared helpers).
 _FAMILY_SOURCES = {
-    "gemm": ["gemm.hip", "gemm_kernels.h", "gemm_nt.hip", "gemm_nn.hip", "gemm_tn.hip"],
+    "gemm": ["gemm.hip", "gemm_kernels.h", "gemm_nt.hip", "gemm_nn.hip", "gemm_tn.hip", "gemm_mk.hip"],
     "attn": ["attention.hip"],
     "ln": ["norm.hip"],
     "colsum": ["norm.hip"],
@@ -41,7 +41,8 @@ _SHARED = ["common.h", "kernels.h"]
 
 _EPI = {"EpiStoreF32": "store_f32", "EpiAccumF32": "accum_f32", "EpiStore": "store", "EpiBiasGelu": "bias_gelu",
         "EpiGeluGrad": "gelu_grad", "EpiQkv": "qkv", "EpiSplit": "split"}
-_LAYOUT = {("1", "1"): "nt", ("1", "0"): "nn", ("0", "0"): "tn", ("0", "1"): "tt"}
+# ("0", "1"): the input-gradient products of short slices computed transposed
+_LAYOUT = {("1", "1"): "nt", ("1", "0"): "nn", ("0", "0"): "tn", ("0", "1"): "mk"}
 
 
 def kernel_sources(trace_name):
@@ -62,6 +63,8 @@ def _tile_tag(pp, bm, bn, waves=4):
     """The library's name for a tile configuration (see pick_tile in gemm.hip)."""
     if bm == bn == "128":
         return "p128" if pp else "128"
+    if (bm, bn, waves) == ("256", "128", 8):
+        return "sk256x128"
     tag = bm if bm == bn else "%sx%s" % (bm, bn)
     return tag + ("w%d" % waves if waves != 4 else "")
 
