@@ -552,7 +552,7 @@ def terapipe_plan(layer, bufs, stages):
     fit = [(l, o) for l in (16, 64, 256, 512, 1024) for o in (128, 384, 768, 1024, 1536) if l + o <= L]
     check = [(32, 256), (128, 640), (512, 896), (96, 1536), (768, 1280), (192, 1152), (48, 1920)]
     check = [(l, o) for l, o in check if l + o <= L]
-    out = terapipe.plan(timer, L, 16, stages, fit, check)
+    out = terapipe.plan(timer, L, 16, stages, fit, check, reps=11)
     layer.new_step()
     return out
 
