@@ -99,6 +99,23 @@ def test_bf16_short_slices_split_weight_gradients(shape):
     _check_shard(shape, "perturbed", "per-slice", rank=0, split_wgrad=True)
 
 
+def test_short_slice_products_run_transposed():
+    """Forward and input-gradient products of at most 128 token rows (the
+    120- and 128-row slices of this case) take the transposed path, 256
+    weight rows a workgroup with split partial sums, and the step still
+    matches the oracle."""
+    from token_transformer_layer_amd import abi
+    abi.tp_trace_enable(True)
+    try:
+        _check_shard(SHORT_D128, "perturbed", "per-slice", rank=0)
+        names = {r[0] for r in abi.tp_trace_read()}
+    finally:
+        abi.tp_trace_enable(False)
+        abi.tp_trace_read(1)
+    assert any(n.startswith("gemm_bf16_sk256x128_nt_") for n in names), sorted(names)
+    assert any(n.startswith("gemm_bf16_sk256x128_nn_") for n in names), sorted(names)
+
+
 def test_bf16_short_slices_peaked():
     _check_shard(SHORT_D128, "peaked", "per-slice", rank=0)
 
