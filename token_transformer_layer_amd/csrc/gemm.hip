@@ -123,8 +123,11 @@ static int pick_splits(int M, int N, int K, Tile t, int64_t ws_floats) {
     int sp;
     if (t == Tile::Pp128x192) {
         // two workgroups per compute unit: the largest split that keeps the
-        // launch within one round of 512 (tiles filling at most half a round)
-        if (tiles > 256) return 1;
+        // launch within one round of 512 (tiles filling at most half a round;
+        // a product with a tile per compute unit already does not split: the
+        // medium configuration's QKV product, 256 tiles over K = 1024, 37 ->
+        // 25 us unsplit)
+        if (tiles >= 256) return 1;
         sp = (int)(512 / tiles);
     } else {
         if (tiles >= 256) return 1;
