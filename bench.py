@@ -581,7 +581,7 @@ def main():
                     help="only time single kernels repeated back to back with the graphics clock they sustain")
     args = ap.parse_args()
     if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU's shard: this build has no multi-GPU path "
+        sys.stderr.write("bench.py measures one GPU's shard: the library has no multi-GPU path "
                          "(the all-reduce between tensor-parallel ranks is left to the caller); "
                          "run with --gpus 1\n")
         sys.exit(2)

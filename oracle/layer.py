@@ -27,7 +27,7 @@ Sources, cited by page title and section:
       one (feed-forward), so a sequence can run as slices l_1..l_M with
       sum l_j = L; section "Takeaways": unidirectional (causal) models only.
 
-Readings where the pages are silent (each is listed in the design doc): LayerNorm
+Readings where the pages are silent: LayerNorm
 with biased variance and eps = 1e-5; exact erf GELU; attention scale 1/sqrt(d);
 the causal mask keeps the diagonal; pre-LN with a residual around each block;
 the row-split biases b_o and b2 are left out of the partial sums and added

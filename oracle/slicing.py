@@ -12,7 +12,7 @@ of a slice is its forward time without extra context plus a context
 overhead that a linear model predicts, fitted from a subset of measured
 (slice, context) combinations.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
 * pipeline latency: K stages, every stage taking t_i for slice i, slices in
   order; the last slice leaves the last stage at sum_i t_i + (K-1) max_i t_i
   (pipeline_latency; pinned against the stage-by-stage recurrence
