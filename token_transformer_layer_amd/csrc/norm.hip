@@ -135,6 +135,65 @@ __global__ __launch_bounds__(kThreads) void ln_fwd_kernel(int h, float eps, cons
     }
 }
 
+// Rows of at most 2048 columns: one wave per row, four rows a workgroup,
+// the two row sums by wave reduction (no barrier).  Lane l owns the column
+// vectors l + 64 i.
+template <typename T, int NVW>
+__global__ __launch_bounds__(256) void ln_fwd_wave_kernel(int rows, int h, float eps, const T *__restrict__ x,
+                                                          const T *__restrict__ g, const T *__restrict__ b,
+                                                          T *__restrict__ u, float *__restrict__ mean,
+                                                          float *__restrict__ rstd) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (row >= rows) return;  // whole wave
+    const int nv = h >> 3;
+    const uint32_t row_t = (uint32_t)h * sizeof(T);
+    const __amdgpu_buffer_rsrc_t px = make_rsrc(x + (size_t)row * h, row_t);
+    uint32_t ot[NVW];
+    Raw8<T> xv[NVW];
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) {
+        const int c = lane + i * 64;
+        ot[i] = c < nv ? (uint32_t)c * (8 * sizeof(T)) : kOOB;
+        xv[i].load(px, ot[i]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NVW; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s += xv[i][j];  // vectors past the row are zeros
+    const float mu = wave_sum(s) / (float)h;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) {
+        if (lane + i * 64 < nv) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float dlt = xv[i][j] - mu;
+                q += dlt * dlt;
+            }
+        }
+    }
+    const float var = wave_sum(q) / (float)h;
+    const float r = 1.0f / sqrtf(var + eps);
+    const __amdgpu_buffer_rsrc_t pg = make_rsrc(g, row_t), pb = make_rsrc(b, row_t);
+    const __amdgpu_buffer_rsrc_t pu = make_rsrc(u + (size_t)row * h, row_t);
+#pragma unroll
+    for (int i = 0; i < NVW; ++i) {
+        Raw8<T> gr, br;
+        gr.load(pg, ot[i]);
+        br.load(pb, ot[i]);
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (xv[i][j] - mu) * r * gr[j] + br[j];
+        store8_buf(pu, ot[i], o, (T *)nullptr);
+    }
+    if (lane == 0) {
+        mean[row] = mu;
+        rstd[row] = r;
+    }
+}
+
 template <typename T>
 struct LnRow {
     // one thread's share of a row: du fp32, x and resid as stored
@@ -176,7 +235,7 @@ __global__ __launch_bounds__(TPB) void ln_bwd_kernel(int rows, int h, int rpb, c
     // loads), so waiting for them does not wait for the next row
     auto load_row = [&](int row, LnRow<T> (&d)[NV], float &mu, float &rs) __attribute__((always_inline)) {
         const bool valid = row < r1;
-        const int rr = valid ? row : r0;
+        const int rr = valid ? row : min(r0, rows - 1);  // a workgroup past the last row still reads in bounds
         mu = mean[rr];
         rs = rstd[rr];
         const size_t base = (size_t)rr * h;
@@ -273,6 +332,127 @@ __global__ __launch_bounds__(TPB) void ln_bwd_kernel(int rows, int h, int rpb, c
             store8(pb + h + c * 8, adb[i]);
         }
     }
+}
+
+// Rows of at most 2048 columns: the workgroup's rows go to its four waves in
+// turn (rows r0 + w, r0 + w + 4, ...), one wave per row with the row sums by
+// wave reduction (no barrier per row) and, for up to 1024 columns, the
+// wave's next row in flight.  Each wave keeps its own parameter-gradient
+// sums; the four waves add them in wave order through LDS at the end, into
+// the same per-workgroup partials as ln_bwd_kernel.
+constexpr int kLnWaveMaxH = 2048;
+template <typename T, int NVW>
+__global__ __launch_bounds__(256) void ln_bwd_wave_kernel(int rows, int h, int rpb, const float *__restrict__ du,
+                                                          const T *__restrict__ resid, const T *__restrict__ x,
+                                                          const T *__restrict__ g, const float *__restrict__ mean,
+                                                          const float *__restrict__ rstd, T *__restrict__ dx,
+                                                          float *__restrict__ partials) {
+    __shared__ float sums[2 * kLnWaveMaxH];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nv = h >> 3;
+    const int r0 = blockIdx.x * rpb, r1 = min(rows, r0 + rpb);
+    const uint32_t row_f32 = (uint32_t)h * 4, row_t = (uint32_t)h * sizeof(T);
+    uint32_t o4[NVW], ot[NVW];
+    float gg[NVW][8], adg[NVW][8], adb[NVW][8];
+    {
+        const __amdgpu_buffer_rsrc_t pg = make_rsrc(g, row_t);
+#pragma unroll
+        for (int i = 0; i < NVW; ++i) {
+            const int c = lane + i * 64;
+            o4[i] = c < nv ? (uint32_t)c * 32 : kOOB;
+            ot[i] = c < nv ? (uint32_t)c * (8 * sizeof(T)) : kOOB;
+            Raw8<T> gr;
+            gr.load(pg, ot[i]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                gg[i][j] = gr[j];
+                adg[i][j] = adb[i][j] = 0.f;
+            }
+        }
+    }
+    // rows past the workgroup's range read zeros (descriptors of length zero)
+    auto load_row = [&](int row, LnRow<T> (&d)[NVW], float &mu, float &rs) __attribute__((always_inline)) {
+        const bool valid = row < r1;
+        const int rr = valid ? row : min(r0, rows - 1);  // a workgroup past the last row still reads in bounds
+        mu = mean[rr];
+        rs = rstd[rr];
+        const size_t base = (size_t)rr * h;
+        const __amdgpu_buffer_rsrc_t pdu = make_rsrc(du + base, valid ? row_f32 : 0u);
+        const __amdgpu_buffer_rsrc_t px = make_rsrc(x + base, valid ? row_t : 0u);
+        const __amdgpu_buffer_rsrc_t pr = make_rsrc(resid + base, valid ? row_t : 0u);
+#pragma unroll
+        for (int i = 0; i < NVW; ++i) {
+            d[i].du.load(pdu, o4[i]);
+            d[i].x.load(px, ot[i]);
+            d[i].res.load(pr, ot[i]);
+        }
+    };
+    auto process = [&](int row, const LnRow<T> (&cur)[NVW], float mu, float rs) __attribute__((always_inline)) {
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < NVW; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xh = (cur[i].x[j] - mu) * rs;
+                const float gd = cur[i].du[j] * gg[i][j];
+                s1 += gd;
+                s2 += gd * xh;
+                adg[i][j] += cur[i].du[j] * xh;
+                adb[i][j] += cur[i].du[j];
+            }
+        const float m1 = wave_sum(s1) / (float)h, m2 = wave_sum(s2) / (float)h;
+        const __amdgpu_buffer_rsrc_t pdx = make_rsrc(dx + (size_t)row * h, row_t);
+#pragma unroll
+        for (int i = 0; i < NVW; ++i) {
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xh = (cur[i].x[j] - mu) * rs;
+                o[j] = cur[i].res[j] + rs * (cur[i].du[j] * gg[i][j] - m1 - xh * m2);
+            }
+            store8_buf(pdx, ot[i], o, (T *)nullptr);
+        }
+    };
+    if constexpr (NVW <= 2) {
+        LnRow<T> ra[NVW], rb[NVW];
+        float mua, rsa, mub, rsb;
+        load_row(r0 + w, ra, mua, rsa);
+        for (int row = r0 + w; row < r1; row += 8) {
+            load_row(row + 4, rb, mub, rsb);
+            __builtin_amdgcn_sched_barrier(0);
+            process(row, ra, mua, rsa);
+            if (row + 4 >= r1) break;
+            load_row(row + 8, ra, mua, rsa);
+            __builtin_amdgcn_sched_barrier(0);
+            process(row + 4, rb, mub, rsb);
+        }
+    } else {
+        LnRow<T> ra[NVW];
+        for (int row = r0 + w; row < r1; row += 4) {
+            float mu, rs;
+            load_row(row, ra, mu, rs);
+            process(row, ra, mu, rs);
+        }
+    }
+    // the waves' sums added in wave order
+    for (int k = 0; k < 4; ++k) {
+        if (w == k) {
+#pragma unroll
+            for (int i = 0; i < NVW; ++i) {
+                const int c = lane + i * 64;
+                if (c < nv) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        sums[c * 8 + j] = k == 0 ? adg[i][j] : sums[c * 8 + j] + adg[i][j];
+                        sums[h + c * 8 + j] = k == 0 ? adb[i][j] : sums[h + c * 8 + j] + adb[i][j];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float *pb = partials + (size_t)blockIdx.x * 2 * h;
+    for (int c = threadIdx.x; c < 2 * h; c += 256) pb[c] = sums[c];
 }
 
 // out[c] (+)= sum over blocks of partials[blk][c], for c < n; partial rows are
@@ -428,9 +608,24 @@ static void launch_ln_fwd(int rows, int h, float eps, const void *x, const void 
                        (const T *)b, (T *)u, mean, rstd);
 }
 
+template <typename T, int NVW>
+static void launch_ln_fwd_wave(int rows, int h, float eps, const void *x, const void *g, const void *b, void *u,
+                               float *mean, float *rstd, hipStream_t st) {
+    hipLaunchKernelGGL((ln_fwd_wave_kernel<T, NVW>), dim3((rows + 3) / 4), dim3(256), 0, st, rows, h, eps,
+                       (const T *)x, (const T *)g, (const T *)b, (T *)u, mean, rstd);
+}
+
 template <typename T>
 static void dispatch_ln_fwd(int rows, int h, float eps, const void *x, const void *g, const void *b, void *u,
                             float *mean, float *rstd, hipStream_t st) {
+    if (h <= kLnWaveMaxH) {
+        switch (((h >> 3) + 63) / 64) {
+        case 1: launch_ln_fwd_wave<T, 1>(rows, h, eps, x, g, b, u, mean, rstd, st); return;
+        case 2: launch_ln_fwd_wave<T, 2>(rows, h, eps, x, g, b, u, mean, rstd, st); return;
+        case 3: launch_ln_fwd_wave<T, 3>(rows, h, eps, x, g, b, u, mean, rstd, st); return;
+        default: launch_ln_fwd_wave<T, 4>(rows, h, eps, x, g, b, u, mean, rstd, st); return;
+        }
+    }
     static_assert(kMaxVec == 8, "the cases below cover 1..kMaxVec vectors per thread");
     switch (((h >> 3) + kThreads - 1) / kThreads) {  // vectors per thread, 1..kMaxVec
     case 1: launch_ln_fwd<T, 1>(rows, h, eps, x, g, b, u, mean, rstd, st); break;
@@ -465,11 +660,27 @@ static void launch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du, c
                        (const T *)resid, (const T *)x, (const T *)g, mean, rstd, (T *)dx, partials);
 }
 
+template <typename T, int NVW>
+static void launch_ln_bwd_wave(int nblk, int rows, int h, int rpb, const float *du, const void *resid, const void *x,
+                               const void *g, const float *mean, const float *rstd, void *dx, float *partials,
+                               hipStream_t st) {
+    hipLaunchKernelGGL((ln_bwd_wave_kernel<T, NVW>), dim3(nblk), dim3(256), 0, st, rows, h, rpb, du, (const T *)resid,
+                       (const T *)x, (const T *)g, mean, rstd, (T *)dx, partials);
+}
+
 template <typename T>
 static void dispatch_ln_bwd(int nblk, int rows, int h, int rpb, const float *du, const void *resid, const void *x,
                             const void *g, const float *mean, const float *rstd, void *dx, float *partials,
                             hipStream_t st) {
     const int nv = h >> 3;
+    if (h <= kLnWaveMaxH) {
+        switch ((nv + 63) / 64) {
+        case 1: launch_ln_bwd_wave<T, 1>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); return;
+        case 2: launch_ln_bwd_wave<T, 2>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); return;
+        case 3: launch_ln_bwd_wave<T, 3>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); return;
+        default: launch_ln_bwd_wave<T, 4>(nblk, rows, h, rpb, du, resid, x, g, mean, rstd, dx, partials, st); return;
+        }
+    }
     // bf16 rows of 6145..12288 columns: 512 threads of 2 or 3 vectors each,
     // two waves per SIMD with the next row prefetched
     if constexpr (sizeof(T) == 2) {
