@@ -574,6 +574,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the per-slice and cube figures")
     ap.add_argument("--profile-only", action="store_true",
                     help="warm up and run the timed whole-partition steps only (for rocprofv3)")
+    ap.add_argument("--schedule", choices=("whole", "per-slice"), default="whole",
+                    help="with --profile-only: the call schedule of the profiled steps (one call per phase over all "
+                         "slices, or the pipeline-faithful one call per slice)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="with --profile-only: also run one plain streaming kernel over this many MiB "
                          "(read once, written once), the calibration of rocprofv3's HBM byte counters")
@@ -606,7 +609,7 @@ def main():
     g_fl, a_fl = step_flops(shape)
     total = g_fl + a_fl
 
-    step = make_step(layer, bufs, "whole")
+    step = make_step(layer, bufs, args.schedule if args.profile_only else "whole")
     per_step = []
     ms, wall_ms, _ = time_steps(torch, step, args.steps, args.warmup, trace=False, per_step=per_step)
     clk = None if args.profile_only else sustained_clock(torch, step)

@@ -22,6 +22,11 @@ def test_gemm_symbols_map_to_trace_names():
     p = "_ZN3tpk19gemm_bf16_pp_kernelINS_5DlCfgILi256ELi128ELi4ELi2ELi3ELi64ELi1EEELb0ELb1ENS_8EpiSplitELb1EEEvNS_8GemmArgsET2_i"
     assert profiling.trace_name(p) == "gemm_bf16_sk256x128_mk_split"
     assert profiling.trace_name("_ZN3tpk12_GLOBAL__N_113ln_bwd_kernelIDF16bEEviiiPKf") == "ln_bwd_kernel<bf16>"
+    # split reductions are told apart by their epilogue
+    r = "_ZN3tpk22splitk_reduce_t_kernelINS_6EpiQkvIDF16bEEEEvPKfiiiiT_"
+    assert profiling.trace_name(r) == "splitk_reduce_t_kernel<qkv>"
+    r = "_ZN3tpk20splitk_reduce_kernelINS_11EpiStoreF32IDF16bEEEEvPKfiiiT_"
+    assert profiling.trace_name(r) == "splitk_reduce_kernel<store_f32>"
 
 
 def test_traffic_is_dropped_when_sources_change(tmp_path):

@@ -87,6 +87,9 @@ def trace_name(symbol):
                 key = ("1" if mm.group(5) == "true" else "0", "1" if mm.group(6) == "true" else "0")
         if mm:
             return "gemm_bf16_%s_%s_%s" % (_tile_tag(pp, bm, bn, waves), _LAYOUT[key], _EPI.get(epi, epi))
+    mm = re.match(r"_ZN3tpk\d+(splitk_reduce\w*_kernel)INS_\d+([A-Za-z]\w*?)(?:I|E)", s)
+    if mm:  # a split reduction, named by the epilogue it applies
+        return "%s<%s>" % (mm.group(1), _EPI.get(mm.group(2), mm.group(2)))
     mm = re.match(r"_ZN3tpk(?:12_GLOBAL__N_1)?(\d+)", s)
     if mm:  # mangled name in the library's namespace: the kernel's own name
         n = int(mm.group(1))
