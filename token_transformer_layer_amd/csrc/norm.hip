@@ -554,7 +554,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t n8, int h, co
     }
 }
 
-int ln_bwd_blocks(int rows) { return rows < 256 ? rows : 256; }
+// Workgroups of the backward: 256 for long row ranges; a short one (a slice
+// of up to 255 rows) gives each workgroup two rows, which halves the
+// parameter-gradient partial sums (2 h floats a workgroup) against one row
+// a workgroup (the 175B per-slice schedule 0.6% faster; four rows a
+// workgroup 0.8% slower).
+int ln_bwd_blocks(int rows) { return rows < 256 ? (rows + 1) / 2 : 256; }
 // chunks of 32 rows, at most 256 (long token ranges keep short serial sums)
 int colsum_chunks(int rows) {
     int c = (rows + 31) / 32;
