@@ -841,6 +841,9 @@ using Pp256w8k32 = DlCfg<256, 256, 2, 4, 4, 32>;     // 128 KB
 // weight rows by the 128 token rows, three stages (two K-tiles in flight);
 // 8 waves measured 1-3% ahead of 4 (128x64 each) on the forward products
 using Sk256x128 = DlCfg<256, 128, 4, 2, 3, 64>;      // 144 KB; waves 4x2 (64x64 each)
+// 192x192 tiles of 4 waves (96x96 each), four stages of 32-deep K-tiles:
+// weight gradients whose 256x256 tiles leave most of a round idle
+using Pp192k32 = DlCfg<192, 192, 2, 2, 4, 32>;       // 96 KB, one workgroup per compute unit
 
 // Tile configurations, chosen per product shape from measurements on MI355X
 // (TFLOP/s of each candidate on the GPT-3 175B t=8 shard's products and on
@@ -849,7 +852,7 @@ using Sk256x128 = DlCfg<256, 128, 4, 2, 3, 64>;      // 144 KB; waves 4x2 (64x64
 // load path delivers, so larger tiles win wherever there are enough of them
 // to fill the 256 compute units; the plain (non-pipelined) 128x128 kernel
 // is the best fit for short reductions and narrow outputs.
-enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192, Pp256w8, Sk256x128 };
+enum class Tile { Dl128, Pp128, Pp256x128, Pp256, Pp256x192, Pp128x192, Pp256w8, Sk256x128, Pp192 };
 
 template <typename T, bool AK, bool BK_, class E>
 static hipError_t launch(const GemmArgs &g, const E &epi, Tile tile, hipStream_t st) {
@@ -864,6 +867,9 @@ static hipError_t launch(const GemmArgs &g, const E &epi, Tile tile, hipStream_t
         case Tile::Pp256x128: return launch_pp<Pp256x128, AK, BK_>(g, epi, st);
         case Tile::Pp128: return launch_pp<Dl128, AK, BK_>(g, epi, st);
         case Tile::Sk256x128: return launch_pp<Sk256x128, AK, BK_>(g, epi, st);
+        case Tile::Pp192:
+            if constexpr (!AK && !BK_) return launch_pp<Pp192k32, AK, BK_>(g, epi, st);
+            else return launch_pp<Pp128x192, AK, BK_>(g, epi, st);
         case Tile::Dl128: break;
         }
         return launch_dl<Dl128, AK, BK_>(g, epi, st);
