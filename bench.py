@@ -549,9 +549,14 @@ def terapipe_plan(layer, bufs, stages):
     from token_transformer_layer_amd import terapipe
     timer = terapipe.SliceTimer(layer, bufs)
     L = layer.shape.seq
-    fit = [(l, o) for l in (16, 64, 256, 512, 1024) for o in (128, 384, 768, 1024, 1536) if l + o <= L]
     check = [(32, 256), (128, 640), (512, 896), (96, 1536), (768, 1280), (192, 1152), (48, 1920)]
     check = [(l, o) for l, o in check if l + o <= L]
+    # the context overhead steps with the slice length where the attention
+    # kernels' work split changes (a 128-token slice carries less than its
+    # neighbours), so the fit samples nine lengths by eight offsets; the
+    # check points stay out of it
+    fit = [(l, o) for l in (16, 32, 64, 128, 256, 384, 512, 768, 1024)
+           for o in (128, 384, 512, 768, 1024, 1280, 1536, 1792) if l + o <= L and (l, o) not in check]
     out = terapipe.plan(timer, L, 16, stages, fit, check, reps=11)
     layer.new_step()
     return out
