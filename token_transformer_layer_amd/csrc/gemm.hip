@@ -177,7 +177,7 @@ static double product_bytes(int M, int N, int K, int es, Epi kind, const EpiArgs
 // Returns false (nothing launched) when the product does not qualify.
 static bool gemm_swapped(int M, int N, int K, const Mat &A, const Mat &B, Epi kind, const EpiArgs &e, const char *lay,
                          hipStream_t st, hipError_t &err) {
-    if (M > 128 || M % 8 != 0 || !A.kcontig || K < 1024) return false;
+    if (M > 128 || M % 8 != 0 || N % 8 != 0 || !A.kcontig || K < 1024) return false;
     const Tile tile = Tile::Sk256x128;
     const int tiles = (N + 255) / 256;
     int sp = std::max(1, 256 / tiles);
@@ -229,7 +229,9 @@ hipError_t gemm(DType dt, int M, int N, int K, Mat A, Mat B, Epi kind, const Epi
     g.a_bytes = K > 0 ? extent_bytes(M, K, A, es) : 0;
     g.b_bytes = K > 0 ? extent_bytes(N, K, B, es) : 0;
     const Tile tile = pick_tile(M, N, K, A.kcontig, B.kcontig);
-    const int nsplit = dt == DType::BF16 && e.split_ws ? pick_splits(M, N, g.K, tile, e.split_ws_floats) : 1;
+    // (the split reductions take 8 output columns per thread)
+    const int nsplit =
+        dt == DType::BF16 && e.split_ws && N % 8 == 0 ? pick_splits(M, N, g.K, tile, e.split_ws_floats) : 1;
     const char *lay = A.kcontig ? (B.kcontig ? "nt" : "nn") : "tn";
     if (nsplit > 1 && g_force_tile.load(std::memory_order_relaxed) < 0) {
         hipError_t err = hipSuccess;
