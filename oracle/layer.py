@@ -219,7 +219,8 @@ def attention_block(q, k, v, q_pos0, k_pos0):
     visible = pos_k[None, :] <= pos_q[:, None]
     scores = np.where(visible, scores, -np.inf)
     any_visible = visible.any(axis=-1)
-    row_max = np.where(any_visible, scores.max(axis=-1), 0.0)[..., None]
+    # (a block of no keys: the maximum over an empty row is -inf, masked out)
+    row_max = np.where(any_visible, scores.max(axis=-1, initial=-np.inf), 0.0)[..., None]
     e = np.where(visible, np.exp(scores - row_max), 0.0)
     denom = e.sum(axis=-1, keepdims=True)
     safe = np.where(denom > 0, denom, 1.0)

@@ -294,7 +294,7 @@ def ring_error(orc, seed=5):
     k = rng.normal(size=(b, n, lk_total, d))
     v = rng.normal(size=(b, n, lk_total, d))
     err = 0.0
-    blocks = [(0, 3), (3, 6), (6, 9), (9, lk_total)]
+    blocks = [(0, 3), (3, 3), (3, 6), (6, 9), (9, lk_total)]  # (3, 3): a block of no keys
     acc = None
     for k0, k1 in blocks:
         o, lse = orc.attention_block(q, k[:, :, k0:k1], v[:, :, k0:k1], q_pos0, k0)

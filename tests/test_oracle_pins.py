@@ -118,6 +118,30 @@ def test_attention_block_special_cases():
     assert np.allclose(l1[..., 0], (q[..., 0, :] * k[..., 0, :]).sum(-1) / 2.0, atol=1e-15)
 
 
+def test_attention_block_empty_blocks():
+    """A block of no keys leaves every query unseen (o = 0, lse = -inf) and
+    merges as the identity; a block of no queries has empty outputs; their
+    backward shares are zero or empty."""
+    rng = np.random.default_rng(12)
+    q = rng.normal(size=(1, 2, 3, 4))
+    k = rng.normal(size=(1, 2, 5, 4))
+    v = rng.normal(size=(1, 2, 5, 4))
+    none_k, none_v = k[:, :, :0], v[:, :, :0]
+    o, lse = oracle.attention_block(q, none_k, none_v, q_pos0=7, k_pos0=0)
+    assert o.shape == (1, 2, 3, 4) and lse.shape == (1, 2, 3)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    o2, l2 = oracle.attention_block(q, k, v, q_pos0=7, k_pos0=2)
+    mo, ml = oracle.merge_partials(o2, l2, o, lse)
+    assert np.array_equal(mo, o2) and np.array_equal(ml, l2)
+    oq, lq = oracle.attention_block(q[:, :, :0], k, v, q_pos0=7, k_pos0=2)
+    assert oq.shape == (1, 2, 0, 4) and lq.shape == (1, 2, 0)
+    do = rng.normal(size=q.shape)
+    dq, dk, dv = oracle.attention_block_backward(do, q, none_k, none_v, o2, l2, 7, 0)
+    assert np.all(dq == 0) and dk.shape == (1, 2, 0, 4) and dv.shape == (1, 2, 0, 4)
+    dq, dk, dv = oracle.attention_block_backward(do[:, :, :0], q[:, :, :0], k, v, o2[:, :, :0], l2[:, :, :0], 7, 2)
+    assert dq.shape == (1, 2, 0, 4) and np.all(dk == 0) and np.all(dv == 0)
+
+
 def test_attention_block_backward_matches_finite_differences():
     """Per-block backward with the merged forward result, summed over a ring
     of blocks, against finite differences of the brute-force forward."""
