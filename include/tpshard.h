@@ -342,7 +342,9 @@ typedef struct {
  * applied to v (normalised within the block); lse fp32 [batch, heads, nq]:
  * natural log of the sum of exp(score) over those keys.  A query that sees
  * none of the block's keys gets o = 0 and lse = -inf.  All pointers device,
- * 16-byte aligned, each buffer below 2 GiB; nq or nk may be 0. */
+ * 16-byte aligned, each buffer below 2 GiB; nq or nk may be 0, and a buffer
+ * sized by a count of 0 (q, o and lse by nq; k and v by nk) is not addressed
+ * and may be NULL (nk = 0: every query gets o = 0 and lse = -inf). */
 tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, const void *k,
                             const void *v, float *o, float *lse, void *stream);
 
@@ -351,7 +353,8 @@ tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, con
  * (nk, q_pos0 and k_pos0 are not used): with m = max(lse_a, lse_b) and
  * w = exp(lse - m) per side (0 for -inf), o = (w_a o_a + w_b o_b) /
  * (w_a + w_b) and lse = m + log(w_a + w_b); -inf and o = 0 if both sides
- * are empty.  o may be o_a or o_b and lse may be lse_a or lse_b (in place). */
+ * are empty.  o may be o_a or o_b and lse may be lse_a or lse_b (in place).
+ * With nq = 0 nothing is addressed and every pointer may be NULL. */
 tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, const float *lse_a,
                         const float *o_b, const float *lse_b, float *o, float *lse, void *stream);
 
@@ -370,7 +373,10 @@ tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, cons
  * blocks and dk, dv over the devices the block visits).  A query whose lse is
  * -inf (it sees no key) takes no gradient.  work: device memory of
  * tp_attn_block_bwd_work_bytes(shape) bytes (rowsum(dout * o)); every
- * pointer 16-byte aligned; same shape limits as tp_attn_block_fwd. */
+ * pointer 16-byte aligned; same shape limits as tp_attn_block_fwd.  A buffer
+ * sized by a count of 0 (q, o, lse, dout, dq and work by nq; k, v, dk and dv
+ * by nk) may be NULL; with nq = 0, dk and dv are zero (stored or added), with
+ * nk = 0 the dq share is. */
 size_t tp_attn_block_bwd_work_bytes(const tp_attn_block_shape *shape);
 tp_status tp_attn_block_bwd(const tp_attn_block_shape *shape, const void *q, const void *k,
                             const void *v, const float *o, const float *lse, const void *dout,

@@ -190,6 +190,13 @@ def test_block_attention_checks():
     assert _status(lambda: merge(good, o=None)) == abi.TP_EINVAL
     assert _status(lambda: merge(good, o=FAKE + 8)) == abi.TP_EALIGN
     assert _status(lambda: merge(abi.tp_attn_block_shape(1, 2, 32, 10, 0, 0, 0))) == abi.TP_EUNSUPPORTED
+    # buffers sized by a count of 0 are never addressed and may be NULL (no
+    # query: nothing to launch)
+    empty = abi.tp_attn_block_shape(1, 2, 128, 0, 0, 0, 0)
+    abi.tp_attn_block_fwd(empty, None, None, None, None, None, None)
+    abi.tp_attn_merge(empty, None, None, None, None, None, None, None)
+    no_keys = abi.tp_attn_block_shape(1, 2, 128, 10, 0, 0, 0)
+    assert _status(lambda: abi.tp_attn_block_fwd(no_keys, None, None, None, FAKE, FAKE, None)) == abi.TP_EINVAL
 
 
 def test_cube_op_checks():

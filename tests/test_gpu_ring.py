@@ -71,7 +71,8 @@ def _compare(o, lse, ro, rl, tol):
 
 
 # (d, nq, nk, q_pos0, k_pos0): blocks before the queries, on the diagonal,
-# straddling it, after every query, single rows, and ragged tile tails
+# straddling it, after every query, single rows, ragged tile tails, and
+# blocks of no keys or no queries (empty buffers passed as NULL)
 BLOCKS = [
     (128, 200, 150, 300, 0),
     (128, 200, 200, 300, 300),
@@ -81,6 +82,8 @@ BLOCKS = [
     (64, 257, 257, 0, 0),
     (64, 1, 129, 128, 0),
     (128, 129, 1, 5, 5),
+    (64, 50, 0, 100, 0),
+    (128, 0, 70, 0, 0),
 ]
 
 

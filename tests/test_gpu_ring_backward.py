@@ -35,6 +35,8 @@ def _stream():
 def _rel(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
     big = np.abs(ref).max()
     if big == 0:
         return float(np.abs(got).max())
@@ -74,8 +76,9 @@ def _inputs(b, n, d, nq, nk_total, seed):
 # (d, nq, nk, q_pos0, k_pos0, first key position of the merged key set):
 # the block is the last nk keys of a key set starting at `first`; blocks
 # before, on and across the diagonal, after every query, single rows and
-# columns, ragged tile tails; first = k_pos0 makes the block the only one,
-# so queries before it see no key (log-sum-exp -inf).
+# columns, ragged tile tails, blocks of no queries or no keys (empty buffers
+# passed as NULL); first = k_pos0 makes the block the only one, so queries
+# before it see no key (log-sum-exp -inf).
 CASES = [
     (128, 200, 150, 300, 100, 0),
     (128, 200, 200, 300, 300, 0),
@@ -87,6 +90,8 @@ CASES = [
     (128, 129, 1, 5, 5, 0),
     (128, 90, 50, 0, 20, 20),
     (64, 200, 64, 30, 100, 100),
+    (128, 0, 100, 50, 20, 0),
+    (64, 80, 0, 100, 30, 0),
 ]
 
 

@@ -128,6 +128,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
         if (!aligned16(ptr)) return fail(TP_EALIGN, "%s is not 16-byte aligned", name); \
     } while (0)
 
+// a buffer of n elements: checked only when n > 0 (an empty one is never
+// addressed and may be NULL)
+#define NEED_IF(n, ptr, name)          \
+    do {                               \
+        if ((n) > 0) NEED(ptr, name); \
+    } while (0)
+
 // scalar fp32 arrays (LayerNorm statistics): 4-byte alignment
 #define NEED4(ptr, name)                                                                 \
     do {                                                                                 \
@@ -600,13 +607,11 @@ tp_status tp_attn_block_fwd(const tp_attn_block_shape *shape, const void *q, con
                             float *lse, void *stream) {
     tp_status s = check_block(shape);
     if (s != TP_OK) return s;
-    NEED(q, "q");
-    NEED(k, "k");
-    NEED(v, "v");
-    NEED(o, "o");
-    NEED(lse, "lse");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return fail(TP_EALIGN, "q, k, v, o and lse must be 16-byte aligned");
+    NEED_IF(shape->nq, q, "q");
+    NEED_IF(shape->nk, k, "k");
+    NEED_IF(shape->nk, v, "v");
+    NEED_IF(shape->nq, o, "o");
+    NEED_IF(shape->nq, lse, "lse");
     AttnBlockArgs a;
     a.bh = shape->batch * shape->heads;
     a.nq = shape->nq;
@@ -623,13 +628,12 @@ tp_status tp_attn_merge(const tp_attn_block_shape *shape, const float *o_a, cons
                         const float *lse_b, float *o, float *lse, void *stream) {
     tp_status s = check_block(shape);
     if (s != TP_OK) return s;
-    NEED(o_a, "o_a");
-    NEED(lse_a, "lse_a");
-    NEED(o_b, "o_b");
-    NEED(lse_b, "lse_b");
-    NEED(o, "o");
-    NEED(lse, "lse");
-    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o)) return fail(TP_EALIGN, "o_a, o_b and o must be 16-byte aligned");
+    NEED_IF(shape->nq, o_a, "o_a");
+    NEED_IF(shape->nq, lse_a, "lse_a");
+    NEED_IF(shape->nq, o_b, "o_b");
+    NEED_IF(shape->nq, lse_b, "lse_b");
+    NEED_IF(shape->nq, o, "o");
+    NEED_IF(shape->nq, lse, "lse");
     const int64_t rows = (int64_t)shape->batch * shape->heads * shape->nq;
     return hip_status(attn_merge(rows, shape->head_dim, o_a, lse_a, o_b, lse_b, o, lse, (hipStream_t)stream),
                       "attention merge");
@@ -647,16 +651,16 @@ tp_status tp_attn_block_bwd(const tp_attn_block_shape *shape, const void *q, con
     tp_status s = check_block(shape);
     if (s != TP_OK) return s;
     if (accumulate != 0 && accumulate != 1) return fail(TP_EINVAL, "accumulate must be 0 or 1");
-    NEED(q, "q");
-    NEED(k, "k");
-    NEED(v, "v");
-    NEED(o, "o");
-    NEED(lse, "lse");
-    NEED(dout, "dout");
-    NEED(dq, "dq");
-    NEED(dk, "dk");
-    NEED(dv, "dv");
-    NEED(work, "work");
+    NEED_IF(shape->nq, q, "q");
+    NEED_IF(shape->nk, k, "k");
+    NEED_IF(shape->nk, v, "v");
+    NEED_IF(shape->nq, o, "o");
+    NEED_IF(shape->nq, lse, "lse");
+    NEED_IF(shape->nq, dout, "dout");
+    NEED_IF(shape->nq, dq, "dq");
+    NEED_IF(shape->nk, dk, "dk");
+    NEED_IF(shape->nk, dv, "dv");
+    NEED_IF(shape->nq, work, "work");
     AttnBlockBwdArgs a{};
     a.bh = shape->batch * shape->heads;
     a.nq = shape->nq;
